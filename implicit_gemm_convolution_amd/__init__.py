@@ -1,0 +1,24 @@
+"""MI355X-native tiled GEMM and implicit-GEMM convolution.
+
+The compute lives in ``libigc.so`` (hand-written HIP for gfx950, C ABI in
+``include/igc.h``); this package only builds it and marshals arguments to it.
+"""
+from .binding import (  # noqa: F401
+    EXPORTED,
+    IGC_EHIP,
+    IGC_EINVAL,
+    IGC_ENODEV,
+    IGC_EOVERFLOW,
+    IGC_EUNSUPPORTED,
+    IGC_OK,
+    LIB_PATH,
+    Epilogue,
+    IGCError,
+    conv2d_implicit_gemm,
+    device_check,
+    gemm_f16f32,
+    gemm_u8i8_zp,
+    last_error,
+    load,
+    status_string,
+)

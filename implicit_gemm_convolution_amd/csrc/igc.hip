@@ -1,0 +1,239 @@
+// igc.hip -- the C ABI of libigc.so (declared in include/igc.h): argument
+// validation, device check, kernel-variant choice and launch on the caller's
+// stream.  All arithmetic happens in the kernels of igc_kernels.hpp.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/igc.h"
+#include "igc_kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+// Per-device architecture cache: 0 unknown, 1 gfx950, -1 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device(int* dev_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(IGC_ENODEV, "no HIP device: %s", hipGetErrorString(e));
+  }
+  if (dev >= kMaxDevices) return fail(IGC_ENODEV, "device index %d out of range", dev);
+  int st = g_arch_ok[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(IGC_ENODEV, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    }
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_arch_ok[dev].store(st, std::memory_order_release);
+    if (st < 0) return fail(IGC_ENODEV, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  }
+  if (st < 0) return fail(IGC_ENODEV, "device %d is not gfx950", dev);
+  *dev_out = dev;
+  return IGC_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Tile variants.  The large tile keeps the most MFMA work per LDS byte; the
+// smaller ones exist so that small problems still spread over the 256 CUs
+// (the multi-kernel-per-shape dispatch of [GEMM-TVM] §4.3, done at run time).
+enum Variant { V_AUTO = -1, V_256x256 = 0, V_128x128 = 1, V_64x64 = 2, V_COUNT = 3 };
+
+int forced_variant() {
+  const char* s = std::getenv("IGC_FORCE_VARIANT");
+  if (!s || !*s) return V_AUTO;
+  int v = std::atoi(s);
+  return (v >= 0 && v < V_COUNT) ? v : V_AUTO;
+}
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+int choose_variant(int M, int N) {
+  int f = forced_variant();
+  if (f != V_AUTO) return f;
+  if (ceil_div(M, 256) * ceil_div(N, 256) >= 192) return V_256x256;
+  if (ceil_div(M, 128) * ceil_div(N, 128) >= 192) return V_128x128;
+  return V_64x64;
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, bool FAST>
+int launch_one(igc::Params p, hipStream_t stream) {
+  p.tiles_m = (int)ceil_div(p.M, BM);
+  p.tiles_n = (int)ceil_div(p.N, BN);
+  long long grid = (long long)p.tiles_m * p.tiles_n;
+  if (grid > 0x7fffffffLL) return fail(IGC_EUNSUPPORTED, "too many tiles (%lld)", grid);
+  hipLaunchKernelGGL((igc::gemm_kernel<KIND, BM, BN, WM, WN, FAST>), dim3((unsigned)grid),
+                     dim3(64 * WM * WN), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return IGC_OK;
+}
+
+template <int KIND, bool FAST>
+int launch_variant(int v, const igc::Params& p, hipStream_t stream) {
+  switch (v) {
+    case V_256x256:
+      if constexpr (FAST) return launch_one<KIND, 256, 256, 2, 2, FAST>(p, stream);
+      [[fallthrough]];
+    case V_128x128: return launch_one<KIND, 128, 128, 2, 2, FAST>(p, stream);
+    default: return launch_one<KIND, 64, 64, 2, 2, FAST>(p, stream);
+  }
+}
+
+template <int KIND>
+int launch(const igc::Params& p, bool fast, hipStream_t stream) {
+  int v = choose_variant(p.M, p.N);
+  // The element-wise (unaligned) loaders need more registers; they stop at 128x128.
+  if (!fast && v == V_256x256) v = V_128x128;
+  return fast ? launch_variant<KIND, true>(v, p, stream) : launch_variant<KIND, false>(v, p, stream);
+}
+
+igc::Params zero_params() {
+  igc::Params p;
+  std::memset(&p, 0, sizeof(p));
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* igc_status_string(int status) {
+  switch (status) {
+    case IGC_OK: return "IGC_OK";
+    case IGC_EINVAL: return "IGC_EINVAL: invalid argument";
+    case IGC_EUNSUPPORTED: return "IGC_EUNSUPPORTED: shape not supported";
+    case IGC_EOVERFLOW: return "IGC_EOVERFLOW: K too large for an exact int32 result";
+    case IGC_EHIP: return "IGC_EHIP: HIP runtime error";
+    case IGC_ENODEV: return "IGC_ENODEV: no gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+const char* igc_last_error(void) { return g_last_error; }
+
+int igc_device_check(void) {
+  int dev;
+  return check_device(&dev);
+}
+
+int gemm_f16f32(int M, int N, int K, const void* A, int lda, const void* B, int ldb, float* C,
+                int ldc, void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0 || N < 0 || K < 0) return fail(IGC_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
+  if (M == 0 || N == 0) return IGC_OK;
+  if (!C) return fail(IGC_EINVAL, "C is NULL");
+  if (ldc < N) return fail(IGC_EINVAL, "ldc=%d < N=%d", ldc, N);
+  if (K > 0) {
+    if (!A || !B) return fail(IGC_EINVAL, "A or B is NULL");
+    if (lda < K || ldb < K) return fail(IGC_EINVAL, "lda=%d / ldb=%d < K=%d", lda, ldb, K);
+  }
+  int dev;
+  if (int s = check_device(&dev)) return s;
+  igc::Params p = zero_params();
+  p.M = M; p.N = N; p.K = K;
+  p.A = static_cast<const uint8_t*>(A); p.lda = lda;
+  p.B = static_cast<const uint8_t*>(B); p.ldb = ldb;
+  p.Cf = C; p.ldcf = ldc;
+  // Buffer descriptors of the fast path cover one tile of rows and must stay below 2^31 bytes.
+  const bool fast = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 &&
+                    256LL * lda * 2 < (1LL << 31) && 256LL * ldb * 2 < (1LL << 31);
+  return launch<igc::KIND_F16_GEMM>(p, fast, static_cast<hipStream_t>(stream));
+}
+
+int gemm_u8i8_zp(int M, int N, int K, const uint8_t* A, int lda, int zA, const int8_t* B, int ldb,
+                 int zB, const igc_u8i8_epilogue* ep, void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0 || N < 0 || K < 0) return fail(IGC_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
+  if (zA < 0 || zA > 255) return fail(IGC_EINVAL, "zA=%d outside [0, 255]", zA);
+  if (zB < -128 || zB > 127) return fail(IGC_EINVAL, "zB=%d outside [-128, 127]", zB);
+  if (!ep) return fail(IGC_EINVAL, "epilogue descriptor is NULL");
+  if (!ep->C_i32 && !ep->D_f32 && !ep->Q_i8) return fail(IGC_EINVAL, "no output requested");
+  if (K > 33025) return fail(IGC_EOVERFLOW, "K=%d > 33025 can overflow int32", K);
+  if (M == 0 || N == 0) return IGC_OK;
+  if (ep->C_i32 && ep->ldc < N) return fail(IGC_EINVAL, "ldc=%d < N=%d", ep->ldc, N);
+  if (ep->D_f32 && ep->ldd < N) return fail(IGC_EINVAL, "ldd=%d < N=%d", ep->ldd, N);
+  if (ep->Q_i8) {
+    if (ep->ldq < N) return fail(IGC_EINVAL, "ldq=%d < N=%d", ep->ldq, N);
+    if (!ep->scale_n || !ep->bias_n) return fail(IGC_EINVAL, "Q_i8 needs scale_n and bias_n");
+  }
+  if (K > 0) {
+    if (!A || !B) return fail(IGC_EINVAL, "A or B is NULL");
+    if (lda < K || ldb < K) return fail(IGC_EINVAL, "lda=%d / ldb=%d < K=%d", lda, ldb, K);
+  }
+  int dev;
+  if (int s = check_device(&dev)) return s;
+  igc::Params p = zero_params();
+  p.M = M; p.N = N; p.K = K;
+  p.A = A; p.lda = lda;
+  p.B = reinterpret_cast<const uint8_t*>(B); p.ldb = ldb;
+  p.zAp = zA - 128; p.zB = zB;
+  p.Ci = ep->C_i32; p.ldci = ep->ldc;
+  p.D = ep->D_f32; p.ldd = ep->ldd; p.dq = ep->dq_scale;
+  p.Qo = ep->Q_i8; p.ldq = ep->ldq; p.scale = ep->scale_n; p.bias = ep->bias_n;
+  p.vec_c = aligned16(ep->C_i32) && ep->ldc % 4 == 0;
+  p.vec_d = aligned16(ep->D_f32) && ep->ldd % 4 == 0;
+  p.vec_q = (reinterpret_cast<uintptr_t>(ep->Q_i8) & 3u) == 0 && ep->ldq % 4 == 0;
+  const bool fast = aligned16(A) && aligned16(B) && lda % 16 == 0 && ldb % 16 == 0 &&
+                    K % 16 == 0 && 256LL * lda < (1LL << 31) && 256LL * ldb < (1LL << 31);
+  return launch<igc::KIND_U8I8_GEMM>(p, fast, static_cast<hipStream_t>(stream));
+}
+
+int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h,
+                         int stride_w, int pad_h, int pad_w, const void* x, const void* w, float* y,
+                         void* stream) {
+  g_last_error[0] = 0;
+  if (Nb <= 0 || H <= 0 || W <= 0 || C <= 0 || Kout <= 0 || R <= 0 || S <= 0)
+    return fail(IGC_EINVAL, "non-positive dimension");
+  if (stride_h <= 0 || stride_w <= 0 || pad_h < 0 || pad_w < 0)
+    return fail(IGC_EINVAL, "bad stride or padding");
+  if (!x || !w || !y) return fail(IGC_EINVAL, "x, w or y is NULL");
+  const long long P = ((long long)H + 2LL * pad_h - R) / stride_h + 1;
+  const long long Q = ((long long)W + 2LL * pad_w - S) / stride_w + 1;
+  if ((long long)H + 2LL * pad_h < R || (long long)W + 2LL * pad_w < S || P < 1 || Q < 1)
+    return fail(IGC_EINVAL, "filter larger than the padded input");
+  const long long M = (long long)Nb * P * Q;
+  const long long K = (long long)R * S * C;
+  const long long nx = (long long)Nb * H * W * C;
+  if (M > 0x7fffffffLL || K > 0x7fffffffLL || nx > 0x7fffffffLL ||
+      (long long)Kout * K > 0x7fffffffLL || M * Kout > (1LL << 62))
+    return fail(IGC_EUNSUPPORTED, "tensor index exceeds 32 bits");
+  int dev;
+  if (int s = check_device(&dev)) return s;
+  igc::Params p = zero_params();
+  p.M = (int)M; p.N = Kout; p.K = (int)K;
+  p.A = static_cast<const uint8_t*>(x); p.lda = 0;
+  p.B = static_cast<const uint8_t*>(w); p.ldb = K;
+  p.Nb = Nb; p.H = H; p.W = W; p.C = C; p.R = R; p.S = S;
+  p.sh = stride_h; p.sw = stride_w; p.ph = pad_h; p.pw = pad_w;
+  p.P = (int)P; p.Q = (int)Q;
+  p.Cf = y; p.ldcf = Kout;
+  p.vec_c = aligned16(y) && Kout % 4 == 0;
+  const bool fast = aligned16(x) && aligned16(w) && C % 8 == 0 && nx * 2 < (1LL << 31) &&
+                    256LL * K * 2 < (1LL << 31);
+  return launch<igc::KIND_F16_CONV>(p, fast, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

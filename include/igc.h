@@ -1,0 +1,160 @@
+/*
+ * igc.h -- C ABI of libigc.so: tiled dense GEMM (fp16 -> fp32 and u8 x i8 ->
+ * int32 with zero points and a fused quantization epilogue) and conv2d lowered
+ * to an implicit GEMM, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *  [GEMM-TVM]  CSDN article "TVM在CUDA GPU上跑GEMM的全套张量化实现：WMMA/DP4A/IMMA
+ *              + TensorIR调度 + INT8/FP16多精度支持".
+ *  [CONV-TC]   TVM tutorial (Chinese docs, segmentfault) on a conv2d schedule
+ *              with TensorCores.
+ *
+ * Conventions shared by every entry point
+ *  - All buffers are device memory owned by the caller (inputs, outputs and
+ *    per-channel vectors).  The library never allocates, frees or copies
+ *    device memory and keeps no state besides a per-device architecture cache.
+ *  - Argument validation is synchronous and happens before any HIP call; a
+ *    rejected call has no side effects.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without waiting.  The caller synchronizes.
+ *  - Outputs must not alias inputs.  Calls on different streams that write the
+ *    same output race.
+ *  - The functions are thread-safe.  igc_last_error() is per thread.
+ *  - Sizes are element counts; leading dimensions (ld*) are in elements.
+ *  - M == 0 or N == 0 is a valid empty problem: nothing is launched.
+ *    K == 0 is valid: every output is computed from an all-zero accumulator.
+ */
+#ifndef IGC_H
+#define IGC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define IGC_OK 0
+#define IGC_EINVAL (-1)       /* null pointer, negative size, ld too small, zero point out of range */
+#define IGC_EUNSUPPORTED (-2) /* a shape / stride combination no kernel variant handles             */
+#define IGC_EOVERFLOW (-3)    /* u8 x i8 with K > 33025: the int32 result could overflow              */
+#define IGC_EHIP (-4)         /* HIP runtime or launch error; detail in igc_last_error()              */
+#define IGC_ENODEV (-5)       /* the current HIP device is not a gfx950 GPU, or there is no device    */
+
+/*
+ * gemm_f16f32 -- C = A * B with fp16 operands and fp32 accumulation and output.
+ *
+ * Definition: [GEMM-TVM] §4.1 (C[i,j] = sum_k A[i,k] * B[k,j]); fp16 inputs
+ * with an fp32 accumulator as in the TensorCore introduction of [CONV-TC].
+ *
+ *   A  fp16 (binary16), M x K, row-major:     A[m*lda + k],  lda >= K
+ *   B  fp16, K x N, column-major (N rows of K): B[n*ldb + k], ldb >= K
+ *   C  fp32, M x N, row-major:                C[m*ldc + n],  ldc >= N
+ *
+ * Every product of two fp16 values is exact in fp32; the K-sum is accumulated
+ * in fp32 (summation order is unspecified).  Any alignment and any lda/ldb is
+ * accepted; 16-byte aligned A/B with lda, ldb and K multiples of 8 take the
+ * fast path.
+ * Errors: IGC_EINVAL (negative size, NULL pointer with a non-empty operand,
+ * lda < K, ldb < K, ldc < N), IGC_ENODEV, IGC_EHIP.
+ */
+int gemm_f16f32(int M, int N, int K,
+                const void* A, int lda,
+                const void* B, int ldb,
+                float* C, int ldc,
+                void* stream);
+
+/*
+ * Outputs of gemm_u8i8_zp.  Any non-empty subset may be requested in one call;
+ * a NULL pointer means "not requested".
+ *
+ *   C_i32, ldc      int32 M x N row-major: the exact zero-point-corrected
+ *                   product  C = sum_k (A[m,k] - zA) * (B[k,n] - zB).
+ *   D_f32, ldd      fp32 M x N row-major: dequantized  D = fl32(fl32(C) * dq_scale).
+ *                   dq_scale is one fp32 multiplier (pass fl32(sA * sB) for
+ *                   per-tensor scales sA, sB).
+ *   Q_i8, ldq       int8 M x N row-major: requantized per output channel n:
+ *                   t = fl32(fl32(C) * scale_n[n]); y = fl32(t + bias_n[n]);
+ *                   Q = clamp(round_half_even(y), -128, 127).
+ *                   scale_n and bias_n are fp32 device vectors of length N and
+ *                   are required when Q_i8 is requested.
+ *
+ * Int -> fp32 conversions round to nearest even; the two fp32 operations of
+ * the requantize step are separately rounded (no fused multiply-add).
+ */
+typedef struct igc_u8i8_epilogue {
+  int32_t* C_i32;
+  int ldc;
+  float* D_f32;
+  int ldd;
+  float dq_scale;
+  int8_t* Q_i8;
+  int ldq;
+  const float* scale_n;
+  const float* bias_n;
+} igc_u8i8_epilogue;
+
+/*
+ * gemm_u8i8_zp -- u8 x i8 GEMM with input zero points, int32 accumulation and
+ * a fused epilogue.
+ *
+ * Definition: [GEMM-TVM] §2.3: the quantized product is
+ * C = (A_q - zp_A) * (B_q - zp_B), followed by dequantize and add-bias in the
+ * same kernel ("4-term fusion").  The zero-point terms are applied in the
+ * epilogue through the four-term expansion
+ *   C = sum_k A*B - zA*colsum(B)[n] - zB*rowsum(A)[m] + K*zA*zB,
+ * which equals the definition exactly in int32.
+ *
+ *   A   uint8, M x K row-major: A[m*lda + k], lda >= K;   zA in [0, 255]
+ *   B   int8,  K x N column-major: B[n*ldb + k], ldb >= K; zB in [-128, 127]
+ *   ep  host pointer to the output description above (read during the call).
+ *
+ * Errors: IGC_EINVAL (negative size, NULL pointer with a non-empty operand,
+ * ld too small, zero point out of range, ep NULL or requesting no output,
+ * Q_i8 without scale_n/bias_n), IGC_EOVERFLOW (K > 33025, where
+ * 255*255*K can exceed the int32 range), IGC_ENODEV, IGC_EHIP.
+ */
+int gemm_u8i8_zp(int M, int N, int K,
+                 const uint8_t* A, int lda, int zA,
+                 const int8_t* B, int ldb, int zB,
+                 const igc_u8i8_epilogue* ep,
+                 void* stream);
+
+/*
+ * conv2d_implicit_gemm -- 2-D convolution (cross-correlation, no filter flip),
+ * fp16 in, fp32 accumulation and output, lowered to a GEMM whose A operand is
+ * the im2col matrix, formed on the fly and never materialized.
+ *
+ * Definition: [CONV-TC] "Preparation and algorithm": the input is read through
+ * a zero-padded view and
+ *   y[n,p,q,k] = sum_{r,s,c} xpad[n, p*stride_h + r, q*stride_w + s, c] * w[k,r,s,c]
+ * with xpad = x inside the input and 0 in the padding.  Dilation 1, groups 1.
+ *
+ *   x  fp16 NHWC [Nb][H][W][C]
+ *   w  fp16 KRSC [Kout][R][S][C]
+ *   y  fp32 NHWC [Nb][P][Q][Kout], P = (H + 2*pad_h - R)/stride_h + 1,
+ *      Q = (W + 2*pad_w - S)/stride_w + 1
+ *
+ * GEMM view: M = Nb*P*Q rows (n,p,q), N = Kout, K = R*S*C with
+ * k = (r*S + s)*C + c; the weight tensor is the column-major B operand.
+ * 16-byte aligned x/w with C a multiple of 8 take the fast path.
+ * Errors: IGC_EINVAL (non-positive dimension or stride, negative padding,
+ * NULL pointer, P or Q < 1), IGC_EUNSUPPORTED (an index of x, w or y that
+ * does not fit in 32 bits), IGC_ENODEV, IGC_EHIP.
+ */
+int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S,
+                         int stride_h, int stride_w, int pad_h, int pad_w,
+                         const void* x, const void* w, float* y,
+                         void* stream);
+
+/* Diagnostics. */
+const char* igc_status_string(int status); /* static string for a status code              */
+const char* igc_last_error(void);          /* detail of this thread's last failure, or ""  */
+int igc_device_check(void);                /* IGC_OK if the current device is gfx950       */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IGC_H */

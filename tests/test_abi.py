@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status codes
+before touching the HIP runtime."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "igc.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def igc():
+    import implicit_gemm_convolution_amd as m
+
+    if not os.path.exists(m.LIB_PATH):
+        from implicit_gemm_convolution_amd import build
+
+        build.build()
+    m.load()
+    return m
+
+
+def test_header_declares_the_three_entry_points():
+    fns = declared_functions()
+    for name in ("gemm_f16f32", "gemm_u8i8_zp", "conv2d_implicit_gemm"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(igc):
+    lib = ctypes.CDLL(igc.LIB_PATH)
+    fns = declared_functions()
+    assert set(fns) == set(igc.EXPORTED)
+    for name in fns:
+        assert hasattr(lib, name), name
+
+
+def test_one_hip_runtime_in_process(igc):
+    maps = open("/proc/self/maps").read()
+    paths = set(re.findall(r"\S*libamdhip64\S*", maps))
+    assert len(paths) == 1, paths
+
+
+def test_status_strings(igc):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert igc.status_string(st).startswith("IGC_")
+
+
+def test_gemm_f16_validation(igc):
+    E = igc.IGC_EINVAL
+    f = lambda *a: igc.gemm_f16f32(*a, check=False)  # noqa: E731
+    assert f(-1, 4, 4, 1, 4, 1, 4, 1, 4) == E
+    assert f(4, 4, 4, 0, 4, 1, 4, 1, 4) == E          # A NULL
+    assert f(4, 4, 4, 1, 4, 0, 4, 1, 4) == E          # B NULL
+    assert f(4, 4, 4, 1, 4, 1, 4, 0, 4) == E          # C NULL
+    assert f(4, 4, 8, 1, 4, 1, 8, 1, 4) == E          # lda < K
+    assert f(4, 4, 8, 1, 8, 1, 7, 1, 4) == E          # ldb < K
+    assert f(4, 5, 8, 1, 8, 1, 8, 1, 4) == E          # ldc < N
+    assert "ldc" in igc.last_error()
+    # empty problems succeed without any device work
+    assert f(0, 4, 4, 0, 4, 0, 4, 0, 4) == igc.IGC_OK
+    assert f(4, 0, 4, 0, 4, 0, 4, 0, 0) == igc.IGC_OK
+
+
+def test_gemm_u8i8_validation(igc):
+    E = igc.IGC_EINVAL
+
+    def f(M=4, N=4, K=16, A=1, lda=16, zA=128, B=1, ldb=16, zB=0, **kw):
+        kw.setdefault("C_i32", 1)
+        kw.setdefault("ldc", N)
+        return igc.gemm_u8i8_zp(M, N, K, A, lda, zA, B, ldb, zB, check=False, **kw)
+
+    assert f(zA=-1) == E
+    assert f(zA=256) == E
+    assert f(zB=128) == E
+    assert f(zB=-129) == E
+    assert f(C_i32=None) == E                          # no output requested
+    assert f(ldc=3) == E
+    assert f(C_i32=None, D_f32=1, ldd=2) == E
+    assert f(C_i32=None, Q_i8=1, ldq=4) == E           # Q without scale/bias
+    assert f(A=None) == E
+    assert f(lda=15) == E
+    assert f(K=33026, lda=33026, ldb=33026) == igc.IGC_EOVERFLOW
+    assert f(M=0) == igc.IGC_OK
+    st = igc.load().gemm_u8i8_zp(4, 4, 16, 1, 16, 128, 1, 16, 0, None, None)
+    assert st == E                                     # NULL epilogue descriptor
+
+
+def test_conv_validation(igc):
+    E = igc.IGC_EINVAL
+
+    def f(Nb=1, H=4, W=4, C=8, Kout=8, R=3, S=3, sh=1, sw=1, ph=1, pw=1, x=1, w=1, y=1):
+        return igc.conv2d_implicit_gemm(Nb, H, W, C, Kout, R, S, sh, sw, ph, pw, x, w, y, check=False)
+
+    assert f(Nb=0) == E
+    assert f(C=-1) == E
+    assert f(sh=0) == E
+    assert f(ph=-1) == E
+    assert f(x=None) == E
+    assert f(R=7, ph=1) == E                           # filter larger than the padded input
+    assert f(Nb=1 << 20, H=1 << 10, W=1 << 10, C=8) == igc.IGC_EUNSUPPORTED
+
+
+def test_valid_call_without_gpu_reports_nodev(igc):
+    try:
+        import torch
+
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    assert igc.gemm_f16f32(4, 4, 8, 16, 8, 16, 8, 16, 4, check=False) == igc.IGC_ENODEV
+    assert igc.device_check() == igc.IGC_ENODEV

@@ -1,0 +1,300 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer outputs (int32 C, requantized int8 Q) and the dequantized fp32 D are
+compared bit-exactly; fp32 outputs of the fp16 paths within the FP_TOL gate of
+gpu_util.fp_rel_err.  Integer-valued fp16 inputs make the fp16 paths exact too,
+which pins layouts, strides and data movement bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import FP_TOL, empty_dev, fp_rel_err, strided, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = ["0", "1", "2"]  # 256x256, 128x128, 64x64 tiles
+
+
+@pytest.fixture(scope="module")
+def igc():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import implicit_gemm_convolution_amd as m
+
+    assert m.device_check() == m.IGC_OK, m.last_error()
+    return m
+
+
+@pytest.fixture
+def variant(request, monkeypatch):
+    v = getattr(request, "param", None)
+    if v is None:
+        monkeypatch.delenv("IGC_FORCE_VARIANT", raising=False)
+    else:
+        monkeypatch.setenv("IGC_FORCE_VARIANT", v)
+    return v
+
+
+def run_f16(igc, A, Bt, lda=None, ldb=None, ldc=None, sentinel=np.nan):
+    import torch
+
+    M, K = A.shape
+    N = Bt.shape[0]
+    lda = lda or K
+    ldb = ldb or K
+    ldc = ldc or N
+    dA = to_dev(strided(A, lda)) if M else empty_dev((0,), torch.float16)
+    dB = to_dev(strided(Bt, ldb)) if N else empty_dev((0,), torch.float16)
+    dC = to_dev(np.full((M, ldc), sentinel, np.float32))
+    igc.gemm_f16f32(M, N, K, dA, lda, dB, ldb, dC, ldc)
+    C = to_host(dC)
+    if ldc > N:  # columns past N are never written
+        pad = C[:, N:]
+        assert np.all(np.isnan(pad)) if np.isnan(sentinel) else np.all(pad == sentinel)
+    return C[:, :N]
+
+
+# ----------------------------------------------------------------- fp16 GEMM
+F16_EXACT_SHAPES = [(64, 64, 64), (256, 256, 256), (300, 200, 264), (1, 1, 8), (33, 65, 136),
+                    (513, 257, 192), (128, 384, 8)]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("M,N,K", F16_EXACT_SHAPES)
+def test_f16_integer_valued_bit_exact(igc, oracle, variant, M, N, K):
+    rng = np.random.default_rng(M * 7919 + N * 31 + K)
+    A = synth.f16_small_ints(rng, (M, K))
+    Bt = synth.f16_small_ints(rng, (N, K))
+    C = run_f16(igc, A, Bt)
+    ref = oracle.gemm_f16(A, Bt)
+    assert np.array_equal(C.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 1024), (200, 300, 1000), (512, 128, 2048)])
+def test_f16_random_tolerance(igc, oracle, variant, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    A = synth.f16_normal(rng, (M, K))
+    Bt = synth.f16_normal(rng, (N, K))
+    C = run_f16(igc, A, Bt)
+    assert fp_rel_err(C, oracle.gemm_f16(A, Bt)) <= FP_TOL
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb,ldc", [
+    (70, 50, 7, 7, 7, 50),        # K not a multiple of 8: element-wise loaders
+    (65, 33, 13, 15, 21, 37),     # odd leading dimensions
+    (130, 260, 72, 80, 96, 261),  # aligned K, padded rows, odd ldc (scalar stores)
+    (256, 256, 128, 136, 128, 260),
+])
+def test_f16_strides_and_unaligned(igc, oracle, M, N, K, lda, ldb, ldc):
+    rng = np.random.default_rng(lda * ldb + ldc)
+    A = synth.f16_small_ints(rng, (M, K))
+    Bt = synth.f16_small_ints(rng, (N, K))
+    C = run_f16(igc, A, Bt, lda, ldb, ldc)
+    assert np.array_equal(C.astype(np.float64), oracle.gemm_f16(A, Bt))
+
+
+def test_f16_misaligned_pointer(igc, oracle):
+    import torch
+
+    rng = np.random.default_rng(5)
+    M, N, K = 40, 24, 64
+    A = synth.f16_small_ints(rng, (M, K))
+    Bt = synth.f16_small_ints(rng, (N, K))
+    flatA = np.concatenate([np.zeros(1, np.float16), A.ravel()])  # +2 bytes
+    dA = to_dev(flatA)
+    dB = to_dev(Bt)
+    dC = empty_dev((M, N), torch.float32)
+    igc.gemm_f16f32(M, N, K, dA.data_ptr() + 2, K, dB, K, dC, N)
+    assert np.array_equal(to_host(dC).astype(np.float64), oracle.gemm_f16(A, Bt))
+
+
+def test_f16_k_zero_and_empty(igc):
+    import torch
+
+    dC = to_dev(np.full((5, 7), np.nan, np.float32))
+    igc.gemm_f16f32(5, 7, 0, 0, 0, 0, 0, dC, 7)
+    assert np.all(to_host(dC) == 0)
+    assert igc.gemm_f16f32(0, 7, 16, 0, 16, 0, 16, 0, 7) == igc.IGC_OK
+    assert igc.gemm_f16f32(7, 0, 16, 0, 16, 0, 16, 0, 0) == igc.IGC_OK
+    del torch
+
+
+# ----------------------------------------------------------------- u8 x i8
+def run_u8i8(igc, A, zA, Bt, zB, outputs=("C", "D", "Q"), scale=None, bias=None, dq=0.0,
+             lda=None, ldb=None):
+    import torch
+
+    M, K = A.shape
+    N = Bt.shape[0]
+    lda = lda or K
+    ldb = ldb or K
+    dA = to_dev(strided(A, lda))
+    dB = to_dev(strided(Bt, ldb))
+    out = {}
+    kw = dict(dq_scale=dq)
+    if "C" in outputs:
+        out["C"] = empty_dev((M, N), torch.int32)
+        kw.update(C_i32=out["C"], ldc=N)
+    if "D" in outputs:
+        out["D"] = empty_dev((M, N), torch.float32)
+        kw.update(D_f32=out["D"], ldd=N)
+    if "Q" in outputs:
+        out["Q"] = empty_dev((M, N), torch.int8)
+        dS = to_dev(scale.astype(np.float32))
+        dBi = to_dev(bias.astype(np.float32))
+        out["_keep"] = (dS, dBi)
+        kw.update(Q_i8=out["Q"], ldq=N, scale_n=dS, bias_n=dBi)
+    igc.gemm_u8i8_zp(M, N, K, dA, lda, zA, dB, ldb, zB, **kw)
+    return {k: to_host(v) for k, v in out.items() if not k.startswith("_")}
+
+
+def check_u8i8(oracle, got, A, zA, Bt, zB, scale=None, bias=None, sA=0.02, sB=0.01):
+    C = oracle.gemm_u8i8_naive(A, zA, Bt, zB)
+    if "C" in got:
+        assert np.array_equal(got["C"].astype(np.int64), C)
+    if "D" in got:
+        assert np.array_equal(got["D"], oracle.dequant(C, sA, sB))
+    if "Q" in got:
+        assert np.array_equal(got["Q"], oracle.requant(C, scale, bias))
+
+
+def q_params(rng, N, K):
+    # a scale near 1/sigma(acc) so most requantized outputs are not saturated
+    sigma = 74.0 * 74.0 * np.sqrt(K)  # std of one product of centred operands, times sqrt(K)
+    scale = (rng.uniform(0.5, 2.0, N) * 40.0 / sigma).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    return scale, bias
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("M,N,K", [(64, 64, 128), (300, 200, 272), (256, 256, 1024), (17, 260, 16),
+                                   (520, 72, 400)])
+@pytest.mark.parametrize("zA,zB", [(128, 3), (128, 0), (0, 0), (37, -5), (255, 127)])
+def test_u8i8_bit_exact(igc, oracle, variant, M, N, K, zA, zB):
+    rng = np.random.default_rng(M * 131 + N * 17 + K + zA * 3 + zB)
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = synth.i8_uniform(rng, (N, K), lo=-128, hi=127)
+    scale, bias = q_params(rng, N, K)
+    s = oracle.dequant_scale(0.02, 0.01)
+    got = run_u8i8(igc, A, zA, Bt, zB, scale=scale, bias=bias, dq=float(s))
+    check_u8i8(oracle, got, A, zA, Bt, zB, scale, bias)
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb", [(50, 40, 13, 13, 13), (33, 17, 100, 103, 101),
+                                           (64, 64, 48, 64, 48)])
+def test_u8i8_unaligned_and_tails(igc, oracle, M, N, K, lda, ldb):
+    rng = np.random.default_rng(K * lda + ldb)
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = synth.i8_uniform(rng, (N, K), lo=-128, hi=127)
+    scale, bias = q_params(rng, N, K)
+    for zA, zB in [(128, 3), (7, -100)]:
+        got = run_u8i8(igc, A, zA, Bt, zB, scale=scale, bias=bias,
+                       dq=float(oracle.dequant_scale(0.02, 0.01)), lda=lda, ldb=ldb)
+        check_u8i8(oracle, got, A, zA, Bt, zB, scale, bias)
+
+
+@pytest.mark.parametrize("outputs", [("C",), ("D",), ("Q",), ("C", "Q"), ("D", "Q")])
+def test_u8i8_output_subsets(igc, oracle, outputs):
+    rng = np.random.default_rng(len(outputs) * 10 + ord(outputs[0][0]))
+    M, N, K = 96, 80, 256
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = synth.i8_uniform(rng, (N, K))
+    scale, bias = q_params(rng, N, K)
+    got = run_u8i8(igc, A, 128, Bt, 3, outputs=outputs, scale=scale, bias=bias,
+                   dq=float(oracle.dequant_scale(0.02, 0.01)))
+    assert set(got) == set(outputs)
+    check_u8i8(oracle, got, A, 128, Bt, 3, scale, bias)
+
+
+@pytest.mark.parametrize("K", [33024, 33025])
+def test_u8i8_extreme_values_at_overflow_bound(igc, oracle, K):
+    # |C| = 255 * 255 * K reaches 2,147,450,625 at K = 33025 (just below 2^31).
+    M, N = 64, 64
+    A = np.full((M, K), 255, np.uint8)
+    Bt = np.full((N, K), -128, np.int8)
+    got = run_u8i8(igc, A, 0, Bt, 127, outputs=("C",))
+    assert np.all(got["C"].astype(np.int64) == 255 * (-255) * K)
+    A2 = np.zeros((M, K), np.uint8)
+    got = run_u8i8(igc, A2, 255, Bt, 127, outputs=("C",))
+    assert np.all(got["C"].astype(np.int64) == (-255) * (-255) * K)
+
+
+def test_u8i8_deterministic(igc):
+    rng = np.random.default_rng(3)
+    A = synth.u8_uniform(rng, (512, 512))
+    Bt = synth.i8_uniform(rng, (512, 512))
+    r1 = run_u8i8(igc, A, 128, Bt, 3, outputs=("C",))
+    r2 = run_u8i8(igc, A, 128, Bt, 3, outputs=("C",))
+    assert np.array_equal(r1["C"], r2["C"])
+
+
+# ----------------------------------------------------------------- conv
+def run_conv(igc, x, w, stride, pad):
+    import torch
+
+    Nb, H, W, C = x.shape
+    Kout, R, S, _ = w.shape
+    P = (H + 2 * pad[0] - R) // stride[0] + 1
+    Q = (W + 2 * pad[1] - S) // stride[1] + 1
+    dx = to_dev(x)
+    dw = to_dev(w)
+    dy = empty_dev((Nb, P, Q, Kout), torch.float32)
+    igc.conv2d_implicit_gemm(Nb, H, W, C, Kout, R, S, stride[0], stride[1], pad[0], pad[1], dx, dw, dy)
+    return to_host(dy)
+
+
+CONV_CASES = [
+    # Nb, H, W, C, Kout, R, S, stride, pad
+    (1, 14, 14, 256, 512, 3, 3, (1, 1), (1, 1)),   # one image of the 256-batch workload
+    (2, 9, 11, 64, 96, 3, 3, (1, 1), (1, 1)),
+    (3, 8, 8, 16, 24, 1, 1, (1, 1), (0, 0)),
+    (2, 13, 10, 32, 40, 5, 5, (2, 2), (2, 2)),
+    (1, 7, 9, 3, 13, 3, 3, (1, 2), (1, 0)),       # C % 8 != 0, odd Kout
+    (2, 6, 6, 24, 20, 3, 2, (2, 1), (0, 1)),
+    (1, 30, 30, 8, 300, 3, 3, (1, 1), (1, 1)),    # M = 900 rows, N ragged
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("case", CONV_CASES)
+def test_conv_integer_valued_bit_exact(igc, oracle, variant, case):
+    Nb, H, W, C, Kout, R, S, st, pd = case
+    # |x|, |w| <= 4: every partial sum is an integer below 16*R*S*C < 2^24, so exact.
+    rng = np.random.default_rng(sum(case[:7]))
+    x = synth.f16_small_ints(rng, (Nb, H, W, C), -4, 4)
+    w = synth.f16_small_ints(rng, (Kout, R, S, C), -4, 4)
+    y = run_conv(igc, x, w, st, pd)
+    assert np.array_equal(y.astype(np.float64), oracle.conv2d_direct(x, w, st, pd))
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("case", CONV_CASES)
+def test_conv_random_tolerance(igc, oracle, variant, case):
+    Nb, H, W, C, Kout, R, S, st, pd = case
+    rng = np.random.default_rng(3 * sum(case[:7]))
+    x = synth.f16_normal(rng, (Nb, H, W, C))
+    w = synth.f16_normal(rng, (Kout, R, S, C), std=0.05)
+    y = run_conv(igc, x, w, st, pd)
+    assert fp_rel_err(y, oracle.conv2d_direct(x, w, st, pd)) <= FP_TOL
+
+
+def test_conv_impulse(igc):
+    Nb, H, W, C, Kout = 1, 6, 7, 16, 8
+    rng = np.random.default_rng(17)
+    w = synth.f16_normal(rng, (Kout, 3, 3, C))
+    x = np.zeros((Nb, H, W, C), np.float16)
+    h0, w0, c0 = 0, 4, 5
+    x[0, h0, w0, c0] = 1.0
+    y = run_conv(igc, x, w, (1, 1), (1, 1))
+    want = np.zeros_like(y)
+    for r in range(3):
+        for s in range(3):
+            p, q = h0 + 1 - r, w0 + 1 - s
+            if 0 <= p < H and 0 <= q < W:
+                want[0, p, q, :] = w[:, r, s, c0].astype(np.float32)
+    assert np.array_equal(y, want)
