@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the GEMM / implicit-GEMM convolution path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+One step is one call of the workload's entry point over its synthetic inputs,
+which are resident in HBM before the timed region starts.  W untimed steps,
+then exactly K steps between two synchronizations; rank 0 prints one JSON
+line.  The headline workload is the 4096^3 fp16 GEMM (TFLOPS); the other four
+workloads are measured in the same run the same way and reported under
+"workloads" (the u8 x i8 GEMMs in TOPS).
+
+`roofline` describes the workload's kernel: algorithmic operations per launch
+(2*M*N*K) divided by its mean launch duration, taken from HIP events recorded
+around every launch of the timed region on the stream the kernel runs on,
+against the MI355X dense MFMA peak of its dtype.  `traffic` (HBM bytes per
+launch) comes from the committed rocprofv3 counter summary in profiles/ when
+that summary was taken on the current kernel sources, else null.
+
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload
+(whole output rows, or whole output pixels for the convolution) on the host's
+cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+METRIC = "GEMM/conv TFLOPS (fp16) & TOPS (int8) on 1 MI355X; % of dense MFMA peak"
+# MI355X dense MFMA peaks: 256 CUs x 2.4 GHz x (4096 fp16 FLOP | 8192 int8 OP) per clock per CU.
+PEAK_F16_TFLOPS = 2516.6
+PEAK_I8_TOPS = 5033.2
+HBM_GBPS = 8000.0
+SRC_FILES = ("implicit_gemm_convolution_amd/csrc/igc.hip",
+             "implicit_gemm_convolution_amd/csrc/igc_kernels.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in SRC_FILES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl) -> int:
+    """Bytes the workload must move at least once: inputs read once, outputs written once."""
+    d = wl.dims
+    M, N, K = d["M"], d["N"], d["K"]
+    if wl.kind == "gemm_f16":
+        return 2 * (M * K + N * K) + 4 * M * N
+    if wl.kind == "conv_f16":
+        return wl.arrays["x"].nbytes + wl.arrays["w"].nbytes + 4 * M * N
+    out = 0
+    for o in wl.params["outputs"]:
+        out += {"C_i32": 4, "D_f32": 4, "Q_i8": 1}[o] * M * N
+    return M * K + N * K + out + (8 * N if "Q_i8" in wl.params["outputs"] else 0)
+
+
+class Runner:
+    """Device-resident inputs/outputs of one workload and a closure launching it."""
+
+    def __init__(self, wl, igc, torch):
+        self.wl = wl
+        dev = torch.device("cuda:0")
+        d = wl.dims
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+        self.keep = []
+        if wl.kind == "gemm_f16":
+            A, B = t(wl.arrays["A"]), t(wl.arrays["Bt"])
+            C = torch.empty((d["M"], d["N"]), dtype=torch.float32, device=dev)
+            self.keep = [A, B, C]
+            M, N, K = d["M"], d["N"], d["K"]
+            self.call = lambda: igc.gemm_f16f32(M, N, K, A, K, B, K, C, N)
+            self.dtype, self.peak, self.unit = "f16", PEAK_F16_TFLOPS, "TFLOPS"
+        elif wl.kind == "gemm_u8i8":
+            pr = wl.params
+            A, B = t(wl.arrays["A"]), t(wl.arrays["Bt"])
+            M, N, K = d["M"], d["N"], d["K"]
+            kw = {}
+            if "C_i32" in pr["outputs"]:
+                C = torch.empty((M, N), dtype=torch.int32, device=dev)
+                kw.update(C_i32=C, ldc=N)
+            if "D_f32" in pr["outputs"]:
+                D = torch.empty((M, N), dtype=torch.float32, device=dev)
+                s = float(np.float32(np.float32(pr["sA"]) * np.float32(pr["sB"])))
+                kw.update(D_f32=D, ldd=N, dq_scale=s)
+            if "Q_i8" in pr["outputs"]:
+                Q = torch.empty((M, N), dtype=torch.int8, device=dev)
+                S, Bi = t(wl.arrays["scale"]), t(wl.arrays["bias"])
+                kw.update(Q_i8=Q, ldq=N, scale_n=S, bias_n=Bi)
+            self.keep = [A, B] + [v for v in kw.values() if hasattr(v, "data_ptr")]
+            zA, zB = pr["zA"], pr["zB"]
+            self.call = lambda: igc.gemm_u8i8_zp(M, N, K, A, K, zA, B, K, zB, **kw)
+            self.dtype, self.peak, self.unit = "i8", PEAK_I8_TOPS, "TOPS"
+        else:
+            x, w = t(wl.arrays["x"]), t(wl.arrays["w"])
+            P = (d["H"] + 2 * d["pad_h"] - d["R"]) // d["stride_h"] + 1
+            Q = (d["W"] + 2 * d["pad_w"] - d["S"]) // d["stride_w"] + 1
+            y = torch.empty((d["Nb"], P, Q, d["Kout"]), dtype=torch.float32, device=dev)
+            self.keep = [x, w, y]
+            args = (d["Nb"], d["H"], d["W"], d["C"], d["Kout"], d["R"], d["S"], d["stride_h"],
+                    d["stride_w"], d["pad_h"], d["pad_w"])
+            self.call = lambda: igc.conv2d_implicit_gemm(*args, x, w, y)
+            self.dtype, self.peak, self.unit = "f16", PEAK_F16_TFLOPS, "TFLOPS"
+
+    def measure(self, torch, steps: int, warmup: int) -> dict:
+        for _ in range(warmup):
+            self.call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t_all0 = torch.cuda.Event(enable_timing=True)
+        t_all1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_all0.record()
+        for s, e in ev:
+            s.record()
+            self.call()
+            e.record()
+        t_all1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per = np.array([s.elapsed_time(e) for s, e in ev]) * 1e-3  # seconds per launch
+        total = t_all0.elapsed_time(t_all1) * 1e-3
+        ops = self.wl.ops()
+        step_s = total / steps
+        launch_s = float(np.mean(per))
+        return dict(
+            steps=steps, warmup=warmup, ms_per_step=step_s * 1e3, wall_s=wall,
+            value=ops / step_s / 1e12, unit=self.unit, dtype=self.dtype,
+            launch_us_mean=launch_s * 1e6, launch_us_median=float(np.median(per)) * 1e6,
+            launch_us_min=float(np.min(per)) * 1e6, launch_us_max=float(np.max(per)) * 1e6,
+            achieved=ops / launch_s / 1e12, peak=self.peak,
+            frac_of_peak=ops / launch_s / 1e12 / self.peak,
+            alg_gbps=algorithmic_bytes(self.wl) / launch_s / 1e9,
+        )
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """Time the oracle on whole output rows (pixels) of the workload for about budget_s."""
+    import oracle
+
+    oracle.lib()
+    d = wl.dims
+    cores = oracle.num_threads()
+
+    def run(nrows):
+        rows = np.arange(nrows)
+        t0 = time.perf_counter()
+        if wl.kind == "gemm_f16":
+            oracle.gemm_f16(wl.arrays["A"][rows], wl.arrays["Bt"])
+        elif wl.kind == "gemm_u8i8":
+            pr = wl.params
+            C = oracle.gemm_u8i8_naive(wl.arrays["A"][rows], pr["zA"], wl.arrays["Bt"], pr["zB"])
+            if "D_f32" in pr["outputs"]:
+                oracle.dequant(C, pr["sA"], pr["sB"])
+            if "Q_i8" in pr["outputs"]:
+                oracle.requant(C, wl.arrays["scale"], wl.arrays["bias"])
+        else:
+            oracle.conv2d_direct_at(wl.arrays["x"], wl.arrays["w"], rows,
+                                    (d["stride_h"], d["stride_w"]), (d["pad_h"], d["pad_w"]))
+        return time.perf_counter() - t0
+
+    n = 8
+    t = run(n)
+    while t < 0.5 and n < d["M"]:
+        n = min(d["M"], n * 4)
+        t = run(n)
+    n = int(min(d["M"], max(n, n * budget_s / max(t, 1e-9))))
+    t = run(n)
+    ops = 2.0 * n * d["N"] * d["K"]
+    unit = "TOPS" if wl.kind == "gemm_u8i8" else "TFLOPS"
+    what = "output pixels" if wl.kind == "conv_f16" else "output rows"
+    return dict(value=ops / t / 1e12, unit=unit, cores=cores, kind="oracle",
+                sample=f"first {n} of {d['M']} {what} of {wl.name} (all {d['N']} columns, "
+                       f"K={d['K']}), {t:.1f} s on {cores} threads",
+                seconds=t)
+
+
+def traffic_for(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it matches these sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if tr.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    w = tr.get("workloads", {}).get(workload)
+    if not w:
+        return None
+    return w.get("hbm_bytes_per_launch")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", choices=synth.WORKLOADS)
+    ap.add_argument("--only", action="store_true", help="measure the headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB MiB (counter calibration) and exit")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 1
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                          "launches": 5}))
+        return 0
+
+    import implicit_gemm_convolution_amd as igc
+
+    st = igc.device_check()
+    if st != igc.IGC_OK:
+        print(f"device check failed: {igc.last_error()}", file=sys.stderr)
+        return 1
+
+    names = [args.workload] + ([] if args.only else [w for w in synth.WORKLOADS if w != args.workload])
+    results = {}
+    head_wl = None
+    for name in names:
+        wl = synth.workload(name)
+        r = Runner(wl, igc, torch)
+        res = r.measure(torch, args.steps, args.warmup)
+        res["config"] = synth.DESCRIPTIONS[name]
+        results[name] = res
+        if name == args.workload:
+            head_wl = wl
+        del r
+        torch.cuda.empty_cache()
+        print(f"# {name}: {res['value']:.1f} {res['unit']} ({100 * res['frac_of_peak']:.1f}% of peak), "
+              f"{res['launch_us_mean']:.1f} us/launch", file=sys.stderr, flush=True)
+
+    head = results[args.workload]
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(head_wl, args.cpu_budget)
+        cpu.pop("seconds", None)
+
+    d = head_wl.dims
+    line = {
+        "metric": METRIC,
+        "value": round(head["value"], 2),
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic (seeded numpy inputs with the workload's shapes and distributions)",
+        "config": {"workload": f"{args.workload}: {synth.DESCRIPTIONS[args.workload]}",
+                   "M": d["M"], "N": d["N"], "K": d["K"], "ops_per_step": head_wl.ops()},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(head["achieved"], 2),
+            "peak": head["peak"],
+            "unit": "TFLOP/s" if head["dtype"] == "f16" else "TOP/s",
+            "frac": round(head["frac_of_peak"], 4),
+            "traffic": traffic_for(args.workload),
+            "launch_us_mean": round(head["launch_us_mean"], 2),
+            "kernel_source_hash": kernel_source_hash(),
+        },
+        "cpu_baseline": cpu,
+        "workloads": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                      for k, v in results.items()},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
