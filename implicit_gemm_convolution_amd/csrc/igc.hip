@@ -59,7 +59,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Tile variants.  The large tile keeps the most MFMA work per LDS byte; the
 // smaller ones exist so that small problems still spread over the 256 CUs
 // (the multi-kernel-per-shape dispatch of [GEMM-TVM] §4.3, done at run time).
-enum Variant { V_AUTO = -1, V_256x256 = 0, V_128x128 = 1, V_64x64 = 2, V_COUNT = 3 };
+enum Variant { V_AUTO = -1, V_256x256 = 0, V_128x128 = 1, V_64x64 = 2, V_256x128 = 3, V_COUNT = 4 };
 
 int forced_variant() {
   const char* s = std::getenv("IGC_FORCE_VARIANT");
@@ -78,36 +78,40 @@ int choose_variant(int M, int N) {
   return V_64x64;
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, bool FAST>
+template <int KIND, int BM, int BN, int WM, int WN, bool FAST, bool SUMS>
 int launch_one(igc::Params p, hipStream_t stream) {
   p.tiles_m = (int)ceil_div(p.M, BM);
   p.tiles_n = (int)ceil_div(p.N, BN);
   long long grid = (long long)p.tiles_m * p.tiles_n;
   if (grid > 0x7fffffffLL) return fail(IGC_EUNSUPPORTED, "too many tiles (%lld)", grid);
-  hipLaunchKernelGGL((igc::gemm_kernel<KIND, BM, BN, WM, WN, FAST>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((igc::gemm_kernel<KIND, BM, BN, WM, WN, FAST, SUMS>), dim3((unsigned)grid),
                      dim3(64 * WM * WN), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return IGC_OK;
 }
 
-template <int KIND, bool FAST>
+template <int KIND, bool FAST, bool SUMS>
 int launch_variant(int v, const igc::Params& p, hipStream_t stream) {
   switch (v) {
     case V_256x256:
-      if constexpr (FAST) return launch_one<KIND, 256, 256, 2, 2, FAST>(p, stream);
+      if constexpr (FAST) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, stream);
       [[fallthrough]];
-    case V_128x128: return launch_one<KIND, 128, 128, 2, 2, FAST>(p, stream);
-    default: return launch_one<KIND, 64, 64, 2, 2, FAST>(p, stream);
+    case V_256x128:
+      if constexpr (FAST) return launch_one<KIND, 256, 128, 2, 2, FAST, SUMS>(p, stream);
+      [[fallthrough]];
+    case V_128x128: return launch_one<KIND, 128, 128, 2, 2, FAST, SUMS>(p, stream);
+    default: return launch_one<KIND, 64, 64, 2, 2, FAST, SUMS>(p, stream);
   }
 }
 
-template <int KIND>
+template <int KIND, bool SUMS>
 int launch(const igc::Params& p, bool fast, hipStream_t stream) {
   int v = choose_variant(p.M, p.N);
   // The element-wise (unaligned) loaders need more registers; they stop at 128x128.
-  if (!fast && v == V_256x256) v = V_128x128;
-  return fast ? launch_variant<KIND, true>(v, p, stream) : launch_variant<KIND, false>(v, p, stream);
+  if (!fast && (v == V_256x256 || v == V_256x128)) v = V_128x128;
+  return fast ? launch_variant<KIND, true, SUMS>(v, p, stream)
+              : launch_variant<KIND, false, SUMS>(v, p, stream);
 }
 
 igc::Params zero_params() {
@@ -160,7 +164,7 @@ int gemm_f16f32(int M, int N, int K, const void* A, int lda, const void* B, int 
   // Buffer descriptors of the fast path cover one tile of rows and must stay below 2^31 bytes.
   const bool fast = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 &&
                     256LL * lda * 2 < (1LL << 31) && 256LL * ldb * 2 < (1LL << 31);
-  return launch<igc::KIND_F16_GEMM>(p, fast, static_cast<hipStream_t>(stream));
+  return launch<igc::KIND_F16_GEMM, false>(p, fast, static_cast<hipStream_t>(stream));
 }
 
 int gemm_u8i8_zp(int M, int N, int K, const uint8_t* A, int lda, int zA, const int8_t* B, int ldb,
@@ -198,7 +202,10 @@ int gemm_u8i8_zp(int M, int N, int K, const uint8_t* A, int lda, int zA, const i
   p.vec_q = (reinterpret_cast<uintptr_t>(ep->Q_i8) & 3u) == 0 && ep->ldq % 4 == 0;
   const bool fast = aligned16(A) && aligned16(B) && lda % 16 == 0 && ldb % 16 == 0 &&
                     K % 16 == 0 && 256LL * lda < (1LL << 31) && 256LL * ldb < (1LL << 31);
-  return launch<igc::KIND_U8I8_GEMM>(p, fast, static_cast<hipStream_t>(stream));
+  // The zero-point sums are compiled only into the kernels that need them.
+  if (p.zAp != 0 || p.zB != 0)
+    return launch<igc::KIND_U8I8_GEMM, true>(p, fast, static_cast<hipStream_t>(stream));
+  return launch<igc::KIND_U8I8_GEMM, false>(p, fast, static_cast<hipStream_t>(stream));
 }
 
 int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h,
@@ -233,7 +240,7 @@ int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, in
   p.vec_c = aligned16(y) && Kout % 4 == 0;
   const bool fast = aligned16(x) && aligned16(w) && C % 8 == 0 && nx * 2 < (1LL << 31) &&
                     256LL * K * 2 < (1LL << 31);
-  return launch<igc::KIND_F16_CONV>(p, fast, static_cast<hipStream_t>(stream));
+  return launch<igc::KIND_F16_CONV, false>(p, fast, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

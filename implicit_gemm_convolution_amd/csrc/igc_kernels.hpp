@@ -11,26 +11,29 @@
 //  [TIR-COMPILER] article on the MLIR-based "TensorIR-Compiler".
 //
 // Design (gfx950, wave64):
-//  * Each workgroup owns one BM x BN tile of C and walks K in tiles of 128
-//    bytes per row (64 fp16 or 128 int8 elements): the block / warp / fragment
+//  * Each workgroup owns one BM x BN tile of C and walks K in tiles of 64
+//    bytes per row (32 fp16 or 64 int8 elements): the block / warp / fragment
 //    hierarchy of [GEMM-TVM] §4.2 and [CONV-TC] "Scheduling the computation",
 //    re-derived for 64-wide waves and 32x32 MFMA tiles.
-//  * Both operands are K-contiguous (A row-major, B column-major), so every
-//    tile row is one 128-byte run: eight 16-byte vector loads, coalesced
-//    ([CONV-TC] vectorizes the shared-memory fill the same way).
-//  * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at chunk
-//    slot c ^ (r & 7).  A fragment read (32 rows, one chunk column) then hits
-//    eight distinct slots per eight lanes: no bank conflicts.  This replaces
-//    the padding offsets of [GEMM-TVM] §3.2 and storage_align of
-//    [TIR-PRACTICE] §2.2 with the swizzle named in [TIR-COMPILER] §2.2.
-//  * Two LDS stages: the global loads for tile k+1 are issued before the
-//    MFMAs of tile k and written to the other stage afterwards; one barrier
-//    per K tile (software pipelining, [TIR-COMPILER] §2.2 and §4.4).
+//  * Both operands are K-contiguous (A row-major, B column-major), so a tile
+//    row is one 64-byte run, fetched as four 16-byte pieces.
+//  * Operand tiles go from HBM straight into LDS with buffer loads that write
+//    LDS (no register staging), into NSTAGE rotating LDS stages: the loads for
+//    K tile kt+NSTAGE-1 are issued while tile kt is computed, so each load has
+//    about NSTAGE-2 tile times to land (software pipelining, [TIR-COMPILER]
+//    §2.2 and §4.4).  Out-of-range buffer offsets write zeros: ragged tiles,
+//    K tails and the convolution's zero padding need no branches.
+//  * LDS rows are 64 bytes; the 16-byte chunk c of row r sits in slot
+//    c ^ ((r >> 2) & 3), so fragment reads are free of bank conflicts on the
+//    64-bank LDS (see swz()).  This replaces the padding offsets of
+//    [GEMM-TVM] §3.2 and storage_align of [TIR-PRACTICE] §2.2 with the
+//    swizzle named in [TIR-COMPILER] §2.2.
 //  * MFMA: v_mfma_f32_32x32x16_f16 and v_mfma_i32_32x32x32_i8.  Each lane
 //    feeds 16 bytes of one row of A and 16 bytes of one column of B per
 //    instruction (lane l: row/column l % 32, K half l / 32).  A and B use the
 //    same (lane, element) -> k assignment, so the K order inside one MFMA
-//    never matters.
+//    never matters.  Fragments are read one k-step ahead; the second k-step's
+//    MFMAs of a tile run after the barrier, hiding the next tile's reads.
 //  * u8 activations on the signed i8 MFMA: A' = A - 128 = A xor 0x80 per byte,
 //    applied to the fragment after it is read from LDS; the epilogue then uses
 //    zA' = zA - 128 in the four-term identity of [GEMM-TVM] §2.3.
@@ -39,6 +42,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
 #include <type_traits>
 
 namespace igc {
@@ -50,8 +54,9 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 enum Kind : int { KIND_F16_GEMM = 0, KIND_F16_CONV = 1, KIND_U8I8_GEMM = 2 };
 
-constexpr int ROW_BYTES = 128;  // bytes of K per tile row
-constexpr int CHUNK_BYTES = 16; // one vector load
+constexpr int KT_BYTES = 64;     // bytes of K per tile row
+constexpr int CHUNK_BYTES = 16;  // one vector load
+constexpr int NSTAGE = 5;        // LDS stages of the K pipeline
 
 struct Params {
   // GEMM view: M x N output, K reduction.
@@ -103,8 +108,12 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
   tn = in_group / gsize;
 }
 
+// LDS has 64 banks of 4 bytes and serves a 16-byte-per-lane access 16 lanes
+// at a time.  Four 64-byte rows span the banks once; XOR-ing the chunk with
+// (r >> 2) & 3 gives the 16 rows read by 16 consecutive lanes (one chunk
+// column) 16 distinct (row % 4, slot) bank groups.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * ROW_BYTES + ((chunk ^ (row & 7)) << 4);
+  return row * KT_BYTES + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
 __device__ __forceinline__ uint4 lds_read16(const uint8_t* base, int off) {
@@ -116,13 +125,7 @@ __device__ __forceinline__ void lds_write16(uint8_t* base, int off, uint4 v) {
 }
 
 // ---------------------------------------------------------------------------
-// Operand loaders.  Thread t owns chunk column (t % 8) of rows
-// t/8 + (NT/8)*j, j = 0..NCH-1 of its tile.  Padding (rows past M/N, k past K,
-// and the zero padding of the convolution) reads as zero bytes.
-//
-// The fast path uses raw buffer loads: the buffer descriptor bounds the tile's
-// rows, and an offset of OOB (past every descriptor's extent) makes the
-// hardware return zeros, so the loads carry no branches.
+// Buffer descriptors and direct-to-LDS loads.
 // ---------------------------------------------------------------------------
 constexpr uint32_t OOB = 0x80000000u;  // descriptors are limited to < 2^31 bytes
 
@@ -132,53 +135,79 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
+// One wave-wide 16-byte-per-lane load written to LDS: lane l's 16 bytes land
+// at lds + 16*l (lds is uniform across the wave).  An offset past the
+// descriptor's extent writes zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
 }
 
+// Operand tiles of ROWS rows x 64 bytes.  The wave-instruction q fills rows
+// 16q .. 16q+15 (1 KB of LDS); lane l covers row 16q + l/4 and fetches the
+// global chunk that belongs in its LDS slot l % 4, i.e. chunk
+// (l % 4) ^ ((l / 16) % 4).  Instruction q = i*NWAVES + wave, i < NQ.
+template <int NT, int ROWS>
+struct TileShape {
+  static constexpr int NWAVES = NT / 64;
+  static constexpr int NQ = ROWS / 16 / NWAVES;  // instructions per wave per tile
+  static_assert(ROWS % (16 * NWAVES) == 0, "tile rows must split over the waves");
+  __device__ static __forceinline__ int lane_row() {
+    return (threadIdx.x >> 6) * 16 + ((threadIdx.x & 63) >> 2);  // + i * 16 * NWAVES
+  }
+  __device__ static __forceinline__ int lane_chunk() {
+    const int l = threadIdx.x & 63;
+    return (l & 3) ^ ((l >> 4) & 3);
+  }
+  __device__ static __forceinline__ uint8_t* dst(uint8_t* tile, int i) {
+    return tile + (i * NWAVES + (int)(threadIdx.x >> 6)) * 1024;
+  }
+};
+
 // Plain row-major operand (A of a GEMM, or B / the conv weight).
-template <int NT, int NCH, int EB, bool FAST>
+//  FAST: 16-byte aligned rows, K a multiple of the chunk: direct-to-LDS loads.
+//  else: element-wise loads through registers, written with the same layout.
+template <int NT, int ROWS, int EB, bool FAST>
 struct RowLoader {
+  typedef TileShape<NT, ROWS> Sh;
   const uint8_t* base;  // row 0 of this tile
   long long ld_bytes;
   int rows_valid;       // rows of this tile that exist
   int K;
-  int chunk;            // this thread's chunk column
-  int row0;             // this thread's first row
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t row_off[NCH];
+  uint32_t lane_off;    // byte offset of this lane's first row and chunk
+  uint32_t row_step;    // bytes between this lane's rows (uniform)
 
-  __device__ __forceinline__ void init(const uint8_t* ptr, long long ld, int r0, int nrows, int k,
-                                       int tile_rows) {
+  __device__ __forceinline__ void init(const uint8_t* ptr, long long ld, int r0, int nrows, int k) {
     ld_bytes = ld * EB;
     base = ptr + (long long)r0 * ld_bytes;
     rows_valid = nrows - r0;
     K = k;
-    chunk = threadIdx.x & 7;
-    row0 = threadIdx.x >> 3;
     if (FAST) {
-      const long long extent = (long long)min(rows_valid, tile_rows) * ld_bytes;
+      const long long extent = (long long)min(rows_valid, ROWS) * ld_bytes;
       rsrc = make_rsrc(base, (uint32_t)extent);
-#pragma unroll
-      for (int j = 0; j < NCH; ++j)
-        row_off[j] = (uint32_t)((row0 + j * (NT / 8)) * ld_bytes) + (uint32_t)(chunk * CHUNK_BYTES);
+      lane_off = (uint32_t)(Sh::lane_row() * ld_bytes) + (uint32_t)(Sh::lane_chunk() * CHUNK_BYTES);
+      row_step = (uint32_t)(16 * Sh::NWAVES * ld_bytes);
     }
   }
 
-  __device__ __forceinline__ void load(uint4 (&r)[NCH], int kt) const {
-    constexpr int EPC = CHUNK_BYTES / EB;
-    const int k0 = kt * (ROW_BYTES / EB) + chunk * EPC;
+  // Fill `tile` (ROWS x 64 bytes, swizzled) with K tile kt.  Rows past the
+  // operand and k past K read as zero bytes.
+  __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
     if (FAST) {
-      // K % EPC == 0 here, so a chunk is either wholly inside K or wholly past it.
-      const bool kin = k0 < K;
-      const uint32_t koff = (uint32_t)(kt * ROW_BYTES);
+      const bool kin = kt * KT_BYTES + Sh::lane_chunk() * CHUNK_BYTES < K * EB;
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) r[j] = buf_load16(rsrc, kin ? row_off[j] + koff : OOB);
+      for (int i = 0; i < Sh::NQ; ++i)
+        dma16(rsrc, Sh::dst(tile, i),
+              kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
     } else {
+      constexpr int EPC = CHUNK_BYTES / EB;
+      // thread t: row t/4 + (NT/4)*j, logical chunk t%4
+      const int c = threadIdx.x & 3;
+      const int k0 = kt * (KT_BYTES / EB) + c * EPC;
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int row = row0 + j * (NT / 8);
+      for (int j = 0; j < ROWS * 4 / NT; ++j) {
+        const int row = (threadIdx.x >> 2) + j * (NT / 4);
         const uint8_t* rp = base + (long long)row * ld_bytes;
         uint8_t bytes[16];
 #pragma unroll
@@ -190,7 +219,7 @@ struct RowLoader {
         }
         uint4 v;
         __builtin_memcpy(&v, bytes, 16);
-        r[j] = v;
+        lds_write16(tile, swz(row, c), v);
       }
     }
   }
@@ -200,84 +229,101 @@ struct RowLoader {
 // k = (r*S + s)*C + c holds x[n, p*sh + r - ph, q*sw + s - pw, c], or 0 where
 // that position lies in the zero padding ([CONV-TC] "Preparation and
 // algorithm": Apad is inlined, the padding predicate is evaluated inside the
-// shared-memory fill).  (n, p, q) is decoded once per row at kernel start;
-// (r, s, c) once per K tile.
-template <int NT, int NCH, bool FAST>
+// shared-memory fill).  (n, p, q) is decoded once per row at kernel start.
+// FAST (C % 8 == 0): the 8 channels of a chunk share one tap (r, s); each lane
+// tracks the (r, s, c) of its chunk and advances it by 32 channels per K tile.
+template <int NT, int ROWS, bool FAST>
 struct Im2colLoader {
+  typedef TileShape<NT, ROWS> Sh;
+  static constexpr int NR = FAST ? Sh::NQ : ROWS * 4 / NT;  // rows per lane
   const uint8_t* x;
-  int img[NCH];  // n*H*W (pixel index of the image), or -1 for rows past M
-  int hb[NCH];   // p*sh - ph
-  int wb[NCH];   // q*sw - pw
+  int pix[NR];  // pixel index in x of (n, p*sh - ph, q*sw - pw), i.e. of tap (0, 0)
+  int hw[NR];   // (p*sh - ph) << 16 | (q*sw - pw) & 0xffff; INT32_MIN for rows past M
   int H, W, C, S, K;
-  int chunk;
   __amdgpu_buffer_rsrc_t rsrc;
+  // tap of this lane's chunk for the next K tile to be loaded (FAST)
+  mutable int cur_r, cur_s, cur_c;
+
+  __device__ __forceinline__ int row_h(int j) const { return hw[j] >> 16; }
+  __device__ __forceinline__ int row_w(int j) const { return (int)(int16_t)(hw[j] & 0xffff); }
 
   __device__ __forceinline__ void init(const Params& p, int m0) {
     x = p.A;
     H = p.H; W = p.W; C = p.C; S = p.S; K = p.K;
-    chunk = threadIdx.x & 7;
     if (FAST) rsrc = make_rsrc(x, (uint32_t)((long long)p.Nb * H * W * C * 2));
     const int PQ = p.P * p.Q;
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int m = m0 + (threadIdx.x >> 3) + j * (NT / 8);
+    for (int j = 0; j < NR; ++j) {
+      const int r = FAST ? Sh::lane_row() + j * 16 * Sh::NWAVES : (int)(threadIdx.x >> 2) + j * (NT / 4);
+      const int m = m0 + r;
       if (m < p.M) {
         const int n = m / PQ;
         const int pq = m - n * PQ;
         const int pp = pq / p.Q;
         const int qq = pq - pp * p.Q;
-        img[j] = n * H * W;
-        hb[j] = pp * p.sh - p.ph;
-        wb[j] = qq * p.sw - p.pw;
+        const int h0 = pp * p.sh - p.ph;
+        const int w0 = qq * p.sw - p.pw;
+        pix[j] = n * H * W + h0 * W + w0;
+        hw[j] = (int)(((uint32_t)h0 << 16) | ((uint32_t)w0 & 0xffffu));
       } else {
-        img[j] = -1;
-        hb[j] = 0;
-        wb[j] = 0;
+        pix[j] = 0;
+        hw[j] = INT32_MIN;
       }
     }
+    // tap of k = chunk*8 (K tile 0)
+    const int k0 = FAST ? Sh::lane_chunk() * 8 : 0;
+    const int rs = k0 / C;
+    cur_c = k0 - rs * C;
+    cur_r = rs / S;
+    cur_s = rs - cur_r * S;
   }
 
   __device__ __forceinline__ uint16_t elem(int j, int k) const {
-    if (img[j] < 0 || k >= K) return 0;
+    if (hw[j] == INT32_MIN || k >= K) return 0;
     const int rs = k / C;
     const int c = k - rs * C;
     const int r = rs / S;
     const int s = rs - r * S;
-    const int h = hb[j] + r;
-    const int w = wb[j] + s;
+    const int h = row_h(j) + r;
+    const int w = row_w(j) + s;
     if ((unsigned)h >= (unsigned)H || (unsigned)w >= (unsigned)W) return 0;
-    return reinterpret_cast<const uint16_t*>(x)[(long long)(img[j] + h * W + w) * C + c];
+    return reinterpret_cast<const uint16_t*>(x)[(long long)(pix[j] + r * W + s) * C + c];
   }
 
-  __device__ __forceinline__ void load(uint4 (&r)[NCH], int kt) const {
-    const int k0 = kt * 64 + chunk * 8;  // 64 fp16 per K tile, 8 per chunk
+  // FAST: K tiles must be requested in order 0, 1, 2, ... (the tap advances).
+  __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
     if (FAST) {
-      // C % 8 == 0: the 8 channels of a chunk share one (r, s).
-      int rr = 0, ss = 0, cc = 0;
-      const bool kin = k0 < K;
-      if (kin) {
-        const int rs = k0 / C;
-        cc = k0 - rs * C;
-        rr = rs / S;
-        ss = rs - rr * S;
-      }
+      const bool kin = kt * 32 + Sh::lane_chunk() * 8 < K;
+      const int tap = cur_r * W + cur_s;
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int h = hb[j] + rr;
-        const int w = wb[j] + ss;
-        const bool ok = kin && img[j] >= 0 && (unsigned)h < (unsigned)H && (unsigned)w < (unsigned)W;
-        const uint32_t off = ((uint32_t)(img[j] + h * W + w) * (uint32_t)C + (uint32_t)cc) * 2u;
-        r[j] = buf_load16(rsrc, ok ? off : OOB);
+      for (int j = 0; j < Sh::NQ; ++j) {
+        const int h = row_h(j) + cur_r;  // rows past M have h < -16000: never in range
+        const int w = row_w(j) + cur_s;
+        const bool ok = kin && (unsigned)h < (unsigned)H && (unsigned)w < (unsigned)W;
+        const uint32_t off = ((uint32_t)(pix[j] + tap) * (uint32_t)C + (uint32_t)cur_c) * 2u;
+        dma16(rsrc, Sh::dst(tile, j), ok ? off : OOB);
+      }
+      // advance this lane's tap by the 32 channels of one K tile
+      cur_c += 32;
+      while (cur_c >= C) {
+        cur_c -= C;
+        if (++cur_s == S) {
+          cur_s = 0;
+          ++cur_r;
+        }
       }
     } else {
+      const int c = threadIdx.x & 3;
+      const int k0 = kt * 32 + c * 8;
 #pragma unroll
-      for (int j = 0; j < NCH; ++j) {
+      for (int j = 0; j < NR; ++j) {
+        const int row = (threadIdx.x >> 2) + j * (NT / 4);
         uint16_t e[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) e[i] = elem(j, k0 + i);
         uint4 v;
         __builtin_memcpy(&v, e, 16);
-        r[j] = v;
+        lds_write16(tile, swz(row, c), v);
       }
     }
   }
@@ -316,26 +362,56 @@ __device__ __forceinline__ int sum_bytes(uint4 v, int acc) {
   return acc;
 }
 
+// s_waitcnt until at most N vector-memory operations of this wave are
+// outstanding and all of its LDS operations are done.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
 // ---------------------------------------------------------------------------
 // The kernel.
+//  SUMS (u8 x i8 only): accumulate rowsum(A') / colsum(B) for the zero-point
+//  correction; not compiled when zA == 128 and zB == 0.
 // ---------------------------------------------------------------------------
-template <int KIND, int BM, int BN, int WM, int WN, bool FAST>
+template <int KIND, int BM, int BN, int WM, int WN, bool FAST, bool SUMS = false>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int EB = (KIND == KIND_U8I8_GEMM) ? 1 : 2;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int A_CH = BM * 8 / NT, B_CH = BN * 8 / NT;
-  constexpr int STAGE = (BM + BN) * ROW_BYTES;
+  constexpr int STAGE = (BM + BN) * KT_BYTES;
   constexpr bool INT8 = KIND == KIND_U8I8_GEMM;
+  constexpr int NL = TileShape<NT, BM>::NQ + TileShape<NT, BN>::NQ;  // loads per tile per lane
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile rows must split evenly");
+  static_assert(FM <= 4 && BM >= BN, "epilogue staging reuses stage arrays 0..3");
+  static_assert((NSTAGE - 2) * NL < 64, "vmcnt range");
+  static_assert(NSTAGE == 5, "the stage arrays below are written out for five stages");
   typedef typename Mfma<KIND>::acc_t acc_t;
 
-  constexpr int PITCH = BN + 8;  // dwords per row of the epilogue staging buffer
-  constexpr int SMEM = (2 * STAGE > TM * PITCH * 4) ? 2 * STAGE : TM * PITCH * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
-  __shared__ int sums[INT8 ? (BM + BN) : 1];
+  // One LDS array per stage: the compiler then knows which stage each
+  // direct-to-LDS load writes and waits for exactly that one.
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st4[STAGE];
+  auto stage = [&](auto U) -> uint8_t* {
+    constexpr int u = decltype(U)::value % NSTAGE;
+    if constexpr (u == 0) return st0;
+    if constexpr (u == 1) return st1;
+    if constexpr (u == 2) return st2;
+    if constexpr (u == 3) return st3;
+    return st4;
+  };
+  auto stage_rt = [&](int u) -> uint8_t* {  // u uniform and known after unrolling
+    return u == 0 ? st0 : u == 1 ? st1 : u == 2 ? st2 : st3;
+  };
+  // The zero-point sums are published after the main loop in the last stage
+  // array, which the epilogue staging (at most four arrays) leaves free.
+  static_assert(FM < NSTAGE && (BM + BN) * 4 <= STAGE, "sums fit in the last stage");
+  int* const sums = reinterpret_cast<int*>(st4);
 
   int tm, tn;
   tile_coords<8>(p, tm, tn);
@@ -345,16 +421,16 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   const int wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  typedef typename std::conditional<KIND == KIND_F16_CONV, Im2colLoader<NT, A_CH, FAST>,
-                                    RowLoader<NT, A_CH, EB, FAST>>::type ALoader;
+  typedef typename std::conditional<KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
+                                    RowLoader<NT, BM, EB, FAST>>::type ALoader;
   ALoader la;
   if constexpr (KIND == KIND_F16_CONV) {
     la.init(p, m0);
   } else {
-    la.init(p.A, p.lda, m0, p.M, p.K, BM);
+    la.init(p.A, p.lda, m0, p.M, p.K);
   }
-  RowLoader<NT, B_CH, EB, FAST> lb;
-  lb.init(p.B, p.ldb, n0, p.N, p.K, BN);
+  RowLoader<NT, BN, EB, FAST> lb;
+  lb.init(p.B, p.ldb, n0, p.N, p.K);
 
   acc_t acc[FM][FN];
 #pragma unroll
@@ -364,96 +440,131 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-  // Per-lane partial sums of A' rows / B columns (u8 x i8 only).
+  // Per-lane partial sums of A' rows / B columns (u8 x i8 with zero points).
   int rsum[FM], csum[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) rsum[i] = 0;
 #pragma unroll
   for (int j = 0; j < FN; ++j) csum[j] = 0;
-  const bool want_rsum = INT8 && p.zB != 0 && wn == 0;
-  const bool want_csum = INT8 && p.zAp != 0 && wm == 0;
+  const bool want_rsum = SUMS && p.zB != 0 && wn == 0;
+  const bool want_csum = SUMS && p.zAp != 0 && wm == 0;
 
-  const int nk = (p.K + (ROW_BYTES / EB) - 1) / (ROW_BYTES / EB);
-  uint4 ra[A_CH], rb[B_CH];
+  const int nk = (p.K * EB + KT_BYTES - 1) / KT_BYTES;
 
-  const int st_row = tid >> 3, st_chunk = tid & 7;
-  auto store_stage = [&](int s) {
-    uint8_t* As = smem + s * STAGE;
-    uint8_t* Bs = As + BM * ROW_BYTES;
-#pragma unroll
-    for (int j = 0; j < A_CH; ++j) lds_write16(As, swz(st_row + j * (NT / 8), st_chunk), ra[j]);
-#pragma unroll
-    for (int j = 0; j < B_CH; ++j) lds_write16(Bs, swz(st_row + j * (NT / 8), st_chunk), rb[j]);
+  auto load_tile = [&](uint8_t* st, int kt) {
+    la.load(st, kt);
+    lb.load(st + BM * KT_BYTES, kt);
   };
 
-  if (nk > 0) {
-    la.load(ra, 0);
-    lb.load(rb, 0);
-    store_stage(0);
-  }
-  __syncthreads();
-
+  // Fragments, double-buffered in registers: lane l reads row l % 32 of its
+  // 32-row block, 16-byte chunk 2*ks + l/32 (k-step ks covers 32 bytes of K).
   const int frow = lane & 31;
   const int fhalf = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      la.load(ra, kt + 1);
-      lb.load(rb, kt + 1);
-    }
-    const uint8_t* As = smem + cur * STAGE;
-    const uint8_t* Bs = As + BM * ROW_BYTES;
+  uint4 fa[2][FM], fb[2][FN];
+  auto read_frags = [&](const uint8_t* st, int ks, uint4 (&a)[FM], uint4 (&b)[FN]) {
+    const uint8_t* Bs = st + BM * KT_BYTES;
 #pragma unroll
-    for (int ks = 0; ks < ROW_BYTES / 32; ++ks) {
-      uint4 af[FM], bf[FN];
+    for (int i = 0; i < FM; ++i) a[i] = lds_read16(st, swz(wm * TM + i * 32 + frow, ks * 2 + fhalf));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b[j] = lds_read16(Bs, swz(wn * TN + j * 32 + frow, ks * 2 + fhalf));
+  };
+  auto mfmas = [&](uint4 (&a)[FM], const uint4 (&b)[FN]) {
+    if constexpr (INT8) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        af[i] = lds_read16(As, swz(wm * TM + i * 32 + frow, ks * 2 + fhalf));
-        if constexpr (INT8) {
-          af[i].x ^= 0x80808080u; af[i].y ^= 0x80808080u;
-          af[i].z ^= 0x80808080u; af[i].w ^= 0x80808080u;
-        }
+        a[i].x ^= 0x80808080u; a[i].y ^= 0x80808080u;
+        a[i].z ^= 0x80808080u; a[i].w ^= 0x80808080u;
       }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bf[j] = lds_read16(Bs, swz(wn * TN + j * 32 + frow, ks * 2 + fhalf));
-      if constexpr (INT8) {
-        if (want_rsum) {
-#pragma unroll
-          for (int i = 0; i < FM; ++i) rsum[i] = sum_bytes(af[i], rsum[i]);
-        }
-        if (want_csum) {
-#pragma unroll
-          for (int j = 0; j < FN; ++j) csum[j] = sum_bytes(bf[j], csum[j]);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) Mfma<KIND>::run(acc[i][j], af[i], bf[j]);
     }
-    if (kt + 1 < nk) store_stage(cur ^ 1);
-    __syncthreads();
+    if constexpr (SUMS) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) rsum[i] = sum_bytes(a[i], rsum[i]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) csum[j] = sum_bytes(b[j], csum[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) Mfma<KIND>::run(acc[i][j], a[i], b[j]);
+  };
+  constexpr int NMF = FM * FN;  // MFMAs per k-step
+  constexpr int NRD = FM + FN;  // fragment reads per k-step
+
+  // Prologue: K tiles 0 .. NSTAGE-2 in flight; wait for tile 0.
+  load_tile(st0, 0);
+  load_tile(st1, 1);
+  load_tile(st2, 2);
+  load_tile(st3, 3);
+  wait_vmcnt_lgkm0<(NSTAGE - 2) * NL>();
+  __builtin_amdgcn_s_barrier();
+  read_frags(st0, 0, fa[0], fb[0]);
+
+  // K tile kt lives in stage kt % NSTAGE.  Region 1: issue the loads of tile
+  // kt+NSTAGE-1 into the stage freed by tile kt-1, read the k-step 1
+  // fragments, run the k-step 0 MFMAs.  Then wait until this lane's loads of
+  // tile kt+1 have landed and every LDS read of this wave is done, and
+  // barrier (after it, tile kt+1 is complete in LDS and nobody reads tile kt
+  // any more).  Region 2: read the next tile's k-step 0 fragments under the
+  // k-step 1 MFMAs.  The instruction scheduler is asked to interleave memory
+  // instructions between the MFMAs, so the in-order wave never stalls behind
+  // a burst of them.
+  auto tile = [&](int kt, auto U) {
+    constexpr int u = decltype(U)::value;
+    load_tile(stage(std::integral_constant<int, u + NSTAGE - 1>()), kt + NSTAGE - 1);
+    read_frags(stage(U), 1, fa[1], fb[1]);
+    mfmas(fa[0], fb[0]);
+#pragma unroll
+    for (int m = 0; m < NMF; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (m < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      if ((m & 1) == 1 && (m >> 1) < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // load
+    }
+    wait_vmcnt_lgkm0<(NSTAGE - 2) * NL>();
+    __builtin_amdgcn_s_barrier();
+    read_frags(stage(std::integral_constant<int, u + 1>()), 0, fa[0], fb[0]);
+    mfmas(fa[1], fb[1]);
+#pragma unroll
+    for (int m = 0; m < NMF; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (m < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  for (int kt = 0; kt < nk; kt += NSTAGE) {
+    tile(kt, std::integral_constant<int, 0>());
+    if (kt + 1 < nk) tile(kt + 1, std::integral_constant<int, 1>());
+    if (kt + 2 < nk) tile(kt + 2, std::integral_constant<int, 2>());
+    if (kt + 3 < nk) tile(kt + 3, std::integral_constant<int, 3>());
+    if (kt + 4 < nk) tile(kt + 4, std::integral_constant<int, 4>());
   }
+  // Loads past the last tile may still be writing (zeros): drain them before
+  // the epilogue reuses the stage arrays.
+  wait_vmcnt_lgkm0<0>();
+  __builtin_amdgcn_s_barrier();
 
   // ------------------------------------------------------------------ epilogue
-  // The accumulators are staged through LDS one wave-row at a time (row-major,
-  // PITCH dwords per row), then every thread takes 4 consecutive columns of a
-  // row: the int8 corrections and quantization run element-wise on them and
-  // the results leave in 16-byte (fp32/int32) or 4-byte (int8) stores.
+  // The accumulators are staged through LDS one wave-row at a time (TM rows;
+  // rows 32i..32i+31 in stage array i, BN*4 bytes per row, 16-byte chunk q
+  // in slot q ^ (8 * ((row >> 2) & 1)) so that the two row groups written by
+  // one staging store land in different bank halves).  Then every thread
+  // takes 4 consecutive columns of a row: the int8 corrections and
+  // quantization run element-wise on them, and results leave in 16-byte
+  // (fp32/int32) or 4-byte (int8) stores.
   //
   // Accumulator layout of a 32x32 MFMA tile: lane l holds column l % 32 and,
   // in register e, row 8*(e/4) + 4*(l/32) + e%4.
   const int ccol = lane & 31;
   const int rbase = 4 * (lane >> 5);
-  int32_t* stage = reinterpret_cast<int32_t*>(smem);
+  auto stage_off = [](int rl, int c) {  // rl: row within a 32-row array; c: column
+    return rl * (BN * 4) + (((c >> 2) ^ (8 * ((rl >> 2) & 1))) << 4) + (c & 3) * 4;
+  };
 
   uint32_t kzz = 0;
-  if constexpr (INT8) {
+  if constexpr (SUMS) {
     // Complete the row / column sums (the two K halves live in lanes l, l^32)
     // and publish them through LDS.
     if (want_rsum) {
       // K-tail padding reads as byte 0, i.e. A' = -128: add those terms back.
-      const int pad_fix = 128 * (nk * ROW_BYTES - p.K);
+      const int pad_fix = 128 * (nk * KT_BYTES - p.K);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int t = rsum[i] + __shfl_xor(rsum[i], 32) + pad_fix;
@@ -467,20 +578,22 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
         if (lane < 32) sums[BM + wn * TN + j * 32 + lane] = t;
       }
     }
-    kzz = (uint32_t)p.K * (uint32_t)p.zAp * (uint32_t)p.zB;
   }
+  if constexpr (INT8) kzz = (uint32_t)p.K * (uint32_t)p.zAp * (uint32_t)p.zB;
 
-  constexpr int GPR = BN / 4;           // 4-column groups per row
-  constexpr int RPP = NT / GPR;         // rows per pass of the whole workgroup
-  static_assert(NT % GPR == 0, "a pass must cover whole rows");
+  constexpr int GPR = BN / 4;    // 4-column groups per row
+  constexpr int RPP = NT / GPR;  // rows per pass of the whole workgroup
+  static_assert(NT % GPR == 0 && 32 % RPP == 0, "a pass must cover whole rows of one array");
   const int lcol = (tid % GPR) * 4;
   const int col = n0 + lcol;
+  const int rr0 = tid / GPR;
 
 #pragma unroll
   for (int h = 0; h < WM; ++h) {
     if (wm == h) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
+        uint8_t* arr = stage_rt(i);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -488,16 +601,20 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
             // copy the element out first: bit-casting a vector-element lvalue
             // directly reads element 0 with this compiler
             const auto val = acc[i][j][e];
-            stage[(i * 32 + 8 * (e >> 2) + rbase + (e & 3)) * PITCH + wn * TN + j * 32 + ccol] =
-                __builtin_bit_cast(int32_t, val);
+            const int off = stage_off(8 * (e >> 2) + rbase + (e & 3), wn * TN + j * 32 + ccol);
+            *reinterpret_cast<int32_t*>(arr + off) = __builtin_bit_cast(int32_t, val);
           }
+      }
     }
     __syncthreads();
-    for (int rr = tid / GPR; rr < TM; rr += RPP) {
+#pragma unroll
+    for (int pass = 0; pass < TM / RPP; ++pass) {
+      const int rr = rr0 + pass * RPP;         // row within the wave-row
+      const uint8_t* arr = stage_rt((pass * RPP) / 32);
       const int lrow = h * TM + rr;
       const int row = m0 + lrow;
       if (row < p.M && col < p.N) {
-        const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * PITCH + lcol);
+        const uint4 v = *reinterpret_cast<const uint4*>(arr + stage_off(rr & 31, lcol));
         const bool full = col + 3 < p.N;
         if constexpr (!INT8) {
           float* dst = p.Cf + (long long)row * p.ldcf + col;
@@ -512,13 +629,15 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
         } else {
           // C = acc' - zA'*colsum(B) - zB*rowsum(A') + K*zA'*zB in wrapping
           // 32-bit arithmetic; the true value fits in int32 (K <= 33025).
-          const uint32_t rcorr = p.zB != 0 ? (uint32_t)p.zB * (uint32_t)sums[lrow] : 0u;
+          uint32_t rcorr = 0;
+          if constexpr (SUMS) rcorr = p.zB != 0 ? (uint32_t)p.zB * (uint32_t)sums[lrow] : 0u;
           const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
           int32_t c[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const uint32_t ccorr =
-                p.zAp != 0 ? (uint32_t)p.zAp * (uint32_t)sums[BM + min(lcol + q, BN - 1)] : 0u;
+            uint32_t ccorr = 0;
+            if constexpr (SUMS)
+              ccorr = p.zAp != 0 ? (uint32_t)p.zAp * (uint32_t)sums[BM + min(lcol + q, BN - 1)] : 0u;
             c[q] = (int32_t)(vv[q] - ccorr - rcorr + kzz);
           }
           if (p.Ci) {
