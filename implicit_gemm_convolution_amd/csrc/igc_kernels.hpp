@@ -11,28 +11,30 @@
 //  [TIR-COMPILER] article on the MLIR-based "TensorIR-Compiler".
 //
 // Design (gfx950, wave64):
-//  * Each workgroup owns one BM x BN tile of C and walks K in tiles of 64
-//    bytes per row (32 fp16 or 64 int8 elements): the block / warp / fragment
+//  * Each workgroup owns one BM x BN tile of C and walks K in tiles of 128
+//    bytes per row (64 fp16 or 128 int8 elements): the block / warp / fragment
 //    hierarchy of [GEMM-TVM] §4.2 and [CONV-TC] "Scheduling the computation",
 //    re-derived for 64-wide waves and 32x32 MFMA tiles.
 //  * Both operands are K-contiguous (A row-major, B column-major), so a tile
-//    row is one 64-byte run, fetched as four 16-byte pieces.
-//  * Operand tiles go from HBM straight into LDS with buffer loads that write
-//    LDS (no register staging), into NSTAGE rotating LDS stages: the loads for
-//    K tile kt+NSTAGE-1 are issued while tile kt is computed, so each load has
-//    about NSTAGE-2 tile times to land (software pipelining, [TIR-COMPILER]
-//    §2.2 and §4.4).  Out-of-range buffer offsets write zeros: ragged tiles,
-//    K tails and the convolution's zero padding need no branches.
-//  * LDS rows are 64 bytes; the 16-byte chunk c of row r sits in slot
-//    c ^ ((r >> 2) & 3), so fragment reads are free of bank conflicts on the
-//    64-bank LDS (see swz()).  This replaces the padding offsets of
-//    [GEMM-TVM] §3.2 and storage_align of [TIR-PRACTICE] §2.2 with the
-//    swizzle named in [TIR-COMPILER] §2.2.
+//    row is one 128-byte run: every load request is a whole cache line.
+//  * The K loop is software-pipelined two tiles deep ([TIR-COMPILER] §2.2 and
+//    §4.4): the A tile goes from HBM straight into one of three LDS stages with
+//    buffer loads that write LDS; the B tile goes through one of two register
+//    staging sets into one of two LDS stages.  Loads for tile kt+2 are issued
+//    while tile kt is computed (three A stages and two B stages fill the
+//    160 KiB LDS at 256x256).  Out-of-range buffer offsets read as zeros:
+//    ragged tiles, K tails and the convolution's zero padding need no
+//    branches.
+//  * LDS rows are 128 bytes; the 16-byte chunk c of row r sits in slot
+//    c ^ ((r >> 1) & 7), so fragment reads and tile writes are free of bank
+//    conflicts on the 64-bank LDS (see swz()).  This replaces the padding
+//    offsets of [GEMM-TVM] §3.2 and storage_align of [TIR-PRACTICE] §2.2 with
+//    the swizzle named in [TIR-COMPILER] §2.2.
 //  * MFMA: v_mfma_f32_32x32x16_f16 and v_mfma_i32_32x32x32_i8.  Each lane
 //    feeds 16 bytes of one row of A and 16 bytes of one column of B per
 //    instruction (lane l: row/column l % 32, K half l / 32).  A and B use the
 //    same (lane, element) -> k assignment, so the K order inside one MFMA
-//    never matters.  Fragments are read one k-step ahead; the second k-step's
+//    never matters.  Fragments are read one k-step ahead; the last k-step's
 //    MFMAs of a tile run after the barrier, hiding the next tile's reads.
 //  * u8 activations on the signed i8 MFMA: A' = A - 128 = A xor 0x80 per byte,
 //    applied to the fragment after it is read from LDS; the epilogue then uses
@@ -54,9 +56,11 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 enum Kind : int { KIND_F16_GEMM = 0, KIND_F16_CONV = 1, KIND_U8I8_GEMM = 2 };
 
-constexpr int KT_BYTES = 64;     // bytes of K per tile row
+constexpr int KT_BYTES = 128;    // bytes of K per tile row
 constexpr int CHUNK_BYTES = 16;  // one vector load
-constexpr int NSTAGE = 5;        // LDS stages of the K pipeline
+constexpr int CPR = KT_BYTES / CHUNK_BYTES;  // chunks per tile row
+constexpr int NSA = 3;           // LDS stages of A
+constexpr int NSB = 2;           // LDS stages (and register staging sets) of B
 
 struct Params {
   // GEMM view: M x N output, K reduction.
@@ -109,11 +113,12 @@ __device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
 }
 
 // LDS has 64 banks of 4 bytes and serves a 16-byte-per-lane access 16 lanes
-// at a time.  Four 64-byte rows span the banks once; XOR-ing the chunk with
-// (r >> 2) & 3 gives the 16 rows read by 16 consecutive lanes (one chunk
-// column) 16 distinct (row % 4, slot) bank groups.
+// at a time.  A 128-byte row covers half the banks, so rows r and r+1 use
+// different halves, and the chunk XOR (r >> 1) & 7 spreads the 8 rows of each
+// parity over the 8 chunk slots: 16 consecutive rows reading one chunk
+// column, and 2 rows written by 16 consecutive lanes, are conflict-free.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * KT_BYTES + ((chunk ^ ((row >> 2) & 3)) << 4);
+  return row * KT_BYTES + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 __device__ __forceinline__ uint4 lds_read16(const uint8_t* base, int off) {
@@ -143,33 +148,34 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, ui
       r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
 }
 
-// Operand tiles of ROWS rows x 64 bytes.  The wave-instruction q fills rows
-// 16q .. 16q+15 (1 KB of LDS); lane l covers row 16q + l/4 and fetches the
-// global chunk that belongs in its LDS slot l % 4, i.e. chunk
-// (l % 4) ^ ((l / 16) % 4).  Instruction q = i*NWAVES + wave, i < NQ.
+// Direct-to-LDS tiles of ROWS rows x 128 bytes.  Wave-instruction q fills
+// rows 8q .. 8q+7 (1 KB of LDS); lane l covers row 8q + l/8 and fetches the
+// global chunk that belongs in its LDS slot l % 8, i.e. chunk
+// (l % 8) ^ ((4q + l/16) % 8).  Instruction q = i*NWAVES + wave, i < NQ; with
+// an even wave count q % 2 = wave % 2, so each lane's chunk is fixed.
 template <int NT, int ROWS>
-struct TileShape {
+struct DmaShape {
   static constexpr int NWAVES = NT / 64;
-  static constexpr int NQ = ROWS / 16 / NWAVES;  // instructions per wave per tile
-  static_assert(ROWS % (16 * NWAVES) == 0, "tile rows must split over the waves");
-  __device__ static __forceinline__ int lane_row() {
-    return (threadIdx.x >> 6) * 16 + ((threadIdx.x & 63) >> 2);  // + i * 16 * NWAVES
+  static constexpr int NQ = ROWS / 8 / NWAVES;  // instructions per wave per tile
+  static_assert(ROWS % (8 * NWAVES) == 0 && NWAVES % 2 == 0, "tile rows must split over the waves");
+  __device__ static __forceinline__ int lane_row() {  // + i * 8 * NWAVES
+    return (threadIdx.x >> 6) * 8 + ((threadIdx.x & 63) >> 3);
   }
   __device__ static __forceinline__ int lane_chunk() {
     const int l = threadIdx.x & 63;
-    return (l & 3) ^ ((l >> 4) & 3);
+    return (l & 7) ^ ((4 * ((threadIdx.x >> 6) & 1) + (l >> 4)) & 7);
   }
   __device__ static __forceinline__ uint8_t* dst(uint8_t* tile, int i) {
     return tile + (i * NWAVES + (int)(threadIdx.x >> 6)) * 1024;
   }
 };
 
-// Plain row-major operand (A of a GEMM, or B / the conv weight).
+// A operand of a GEMM (row-major, rows of K).
 //  FAST: 16-byte aligned rows, K a multiple of the chunk: direct-to-LDS loads.
-//  else: element-wise loads through registers, written with the same layout.
+//  else: element-wise loads, written to LDS with the same layout.
 template <int NT, int ROWS, int EB, bool FAST>
-struct RowLoader {
-  typedef TileShape<NT, ROWS> Sh;
+struct RowDmaLoader {
+  typedef DmaShape<NT, ROWS> Sh;
   const uint8_t* base;  // row 0 of this tile
   long long ld_bytes;
   int rows_valid;       // rows of this tile that exist
@@ -187,27 +193,25 @@ struct RowLoader {
       const long long extent = (long long)min(rows_valid, ROWS) * ld_bytes;
       rsrc = make_rsrc(base, (uint32_t)extent);
       lane_off = (uint32_t)(Sh::lane_row() * ld_bytes) + (uint32_t)(Sh::lane_chunk() * CHUNK_BYTES);
-      row_step = (uint32_t)(16 * Sh::NWAVES * ld_bytes);
+      row_step = (uint32_t)(8 * Sh::NWAVES * ld_bytes);
     }
   }
 
-  // Fill `tile` (ROWS x 64 bytes, swizzled) with K tile kt.  Rows past the
+  // Fill `tile` (ROWS x 128 bytes, swizzled) with K tile kt; rows past the
   // operand and k past K read as zero bytes.
   __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
     if (FAST) {
       const bool kin = kt * KT_BYTES + Sh::lane_chunk() * CHUNK_BYTES < K * EB;
 #pragma unroll
       for (int i = 0; i < Sh::NQ; ++i)
-        dma16(rsrc, Sh::dst(tile, i),
-              kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
+        dma16(rsrc, Sh::dst(tile, i), kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
     } else {
       constexpr int EPC = CHUNK_BYTES / EB;
-      // thread t: row t/4 + (NT/4)*j, logical chunk t%4
-      const int c = threadIdx.x & 3;
+      const int c = threadIdx.x & 7;  // thread t: chunk t%8 of rows t/8 + (NT/8)*j
       const int k0 = kt * (KT_BYTES / EB) + c * EPC;
 #pragma unroll
-      for (int j = 0; j < ROWS * 4 / NT; ++j) {
-        const int row = (threadIdx.x >> 2) + j * (NT / 4);
+      for (int j = 0; j < ROWS * CPR / NT; ++j) {
+        const int row = (threadIdx.x >> 3) + j * (NT / 8);
         const uint8_t* rp = base + (long long)row * ld_bytes;
         uint8_t bytes[16];
 #pragma unroll
@@ -225,17 +229,84 @@ struct RowLoader {
   }
 };
 
-// Implicit im2col view of an NHWC fp16 input: row m = (n, p, q), column
-// k = (r*S + s)*C + c holds x[n, p*sh + r - ph, q*sw + s - pw, c], or 0 where
-// that position lies in the zero padding ([CONV-TC] "Preparation and
-// algorithm": Apad is inlined, the padding predicate is evaluated inside the
-// shared-memory fill).  (n, p, q) is decoded once per row at kernel start.
-// FAST (C % 8 == 0): the 8 channels of a chunk share one tap (r, s); each lane
-// tracks the (r, s, c) of its chunk and advances it by 32 channels per K tile.
+// B operand (column-major B, i.e. rows of K; also the conv weight), staged
+// through registers: thread t holds chunk t%8 of rows t/8 + (NT/8)*j, so each
+// group of 8 lanes fetches one whole 128-byte line.
+template <int NT, int ROWS, int EB, bool FAST>
+struct RowRegLoader {
+  static constexpr int NCH = ROWS * CPR / NT;  // chunks per thread
+  const uint8_t* base;
+  long long ld_bytes;
+  int rows_valid;
+  int K;
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t lane_off;  // byte offset of this thread's first row and chunk
+  uint32_t row_step;  // bytes between its rows (uniform)
+
+  __device__ __forceinline__ void init(const uint8_t* ptr, long long ld, int r0, int nrows, int k) {
+    ld_bytes = ld * EB;
+    base = ptr + (long long)r0 * ld_bytes;
+    rows_valid = nrows - r0;
+    K = k;
+    if (FAST) {
+      const long long extent = (long long)min(rows_valid, ROWS) * ld_bytes;
+      rsrc = make_rsrc(base, (uint32_t)extent);
+      lane_off = (uint32_t)((threadIdx.x >> 3) * ld_bytes) + (uint32_t)((threadIdx.x & 7) * CHUNK_BYTES);
+      row_step = (uint32_t)((NT / 8) * ld_bytes);
+    }
+  }
+
+  __device__ __forceinline__ void load(uint4 (&r)[NCH], int kt) const {
+    constexpr int EPC = CHUNK_BYTES / EB;
+    const int c = threadIdx.x & 7;
+    if (FAST) {
+      const bool kin = kt * KT_BYTES + c * CHUNK_BYTES < K * EB;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        auto v = __builtin_amdgcn_raw_buffer_load_b128(
+            rsrc, (int)(kin ? lane_off + (uint32_t)(j * row_step + kt * KT_BYTES) : OOB), 0, 0);
+        r[j] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+      const int k0 = kt * (KT_BYTES / EB) + c * EPC;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        const int row = (threadIdx.x >> 3) + j * (NT / 8);
+        const uint8_t* rp = base + (long long)row * ld_bytes;
+        uint8_t bytes[16];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          const int k = k0 + e;
+          const bool ok = row < rows_valid && k < K;
+#pragma unroll
+          for (int b = 0; b < EB; ++b) bytes[e * EB + b] = ok ? rp[(long long)k * EB + b] : (uint8_t)0;
+        }
+        uint4 v;
+        __builtin_memcpy(&v, bytes, 16);
+        r[j] = v;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* tile, const uint4 (&r)[NCH]) const {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+      lds_write16(tile, swz((threadIdx.x >> 3) + j * (NT / 8), threadIdx.x & 7), r[j]);
+  }
+};
+
+// Implicit im2col view of an NHWC fp16 input (the conv's A operand): row
+// m = (n, p, q), column k = (r*S + s)*C + c holds
+// x[n, p*sh + r - ph, q*sw + s - pw, c], or 0 where that position lies in the
+// zero padding ([CONV-TC] "Preparation and algorithm": Apad is inlined, the
+// padding predicate is evaluated inside the shared-memory fill).  (n, p, q)
+// is decoded once per row at kernel start.  FAST (C % 8 == 0): the 8 channels
+// of a chunk share one tap (r, s); each lane tracks the (r, s, c) of its chunk
+// and advances it by the 64 channels of one K tile.
 template <int NT, int ROWS, bool FAST>
 struct Im2colLoader {
-  typedef TileShape<NT, ROWS> Sh;
-  static constexpr int NR = FAST ? Sh::NQ : ROWS * 4 / NT;  // rows per lane
+  typedef DmaShape<NT, ROWS> Sh;
+  static constexpr int NR = FAST ? Sh::NQ : ROWS * CPR / NT;  // rows per lane
   const uint8_t* x;
   int pix[NR];  // pixel index in x of (n, p*sh - ph, q*sw - pw), i.e. of tap (0, 0)
   int hw[NR];   // (p*sh - ph) << 16 | (q*sw - pw) & 0xffff; INT32_MIN for rows past M
@@ -254,7 +325,7 @@ struct Im2colLoader {
     const int PQ = p.P * p.Q;
 #pragma unroll
     for (int j = 0; j < NR; ++j) {
-      const int r = FAST ? Sh::lane_row() + j * 16 * Sh::NWAVES : (int)(threadIdx.x >> 2) + j * (NT / 4);
+      const int r = FAST ? Sh::lane_row() + j * 8 * Sh::NWAVES : (int)(threadIdx.x >> 3) + j * (NT / 8);
       const int m = m0 + r;
       if (m < p.M) {
         const int n = m / PQ;
@@ -293,7 +364,7 @@ struct Im2colLoader {
   // FAST: K tiles must be requested in order 0, 1, 2, ... (the tap advances).
   __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
     if (FAST) {
-      const bool kin = kt * 32 + Sh::lane_chunk() * 8 < K;
+      const bool kin = kt * 64 + Sh::lane_chunk() * 8 < K;
       const int tap = cur_r * W + cur_s;
 #pragma unroll
       for (int j = 0; j < Sh::NQ; ++j) {
@@ -303,8 +374,8 @@ struct Im2colLoader {
         const uint32_t off = ((uint32_t)(pix[j] + tap) * (uint32_t)C + (uint32_t)cur_c) * 2u;
         dma16(rsrc, Sh::dst(tile, j), ok ? off : OOB);
       }
-      // advance this lane's tap by the 32 channels of one K tile
-      cur_c += 32;
+      // advance this lane's tap by the 64 channels of one K tile
+      cur_c += 64;
       while (cur_c >= C) {
         cur_c -= C;
         if (++cur_s == S) {
@@ -313,11 +384,11 @@ struct Im2colLoader {
         }
       }
     } else {
-      const int c = threadIdx.x & 3;
-      const int k0 = kt * 32 + c * 8;
+      const int c = threadIdx.x & 7;
+      const int k0 = kt * 64 + c * 8;
 #pragma unroll
       for (int j = 0; j < NR; ++j) {
-        const int row = (threadIdx.x >> 2) + j * (NT / 4);
+        const int row = (threadIdx.x >> 3) + j * (NT / 8);
         uint16_t e[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) e[i] = elem(j, k0 + i);
@@ -381,37 +452,38 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int EB = (KIND == KIND_U8I8_GEMM) ? 1 : 2;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int STAGE = (BM + BN) * KT_BYTES;
+  constexpr int SA = BM * KT_BYTES, SB = BN * KT_BYTES;  // stage sizes
   constexpr bool INT8 = KIND == KIND_U8I8_GEMM;
-  constexpr int NL = TileShape<NT, BM>::NQ + TileShape<NT, BN>::NQ;  // loads per tile per lane
+  typedef RowRegLoader<NT, BN, EB, FAST> BLoader;
+  constexpr int NCH_B = BLoader::NCH;
+  // vector-memory instructions per K tile per lane (the A loads count only
+  // on the direct-to-LDS path; element-wise loads are waited for by the
+  // compiler before they are used)
+  constexpr int NLA = FAST ? DmaShape<NT, BM>::NQ : 0;
+  constexpr int NVM = NLA + (FAST ? NCH_B : 0);
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(FM <= 4 && BM >= BN, "epilogue staging reuses stage arrays 0..3");
-  static_assert((NSTAGE - 2) * NL < 64, "vmcnt range");
-  static_assert(NSTAGE == 5, "the stage arrays below are written out for five stages");
+  static_assert(FM <= NSA + 1 && BM >= BN, "epilogue staging reuses the stage arrays");
+  static_assert(NVM < 64, "vmcnt range");
   typedef typename Mfma<KIND>::acc_t acc_t;
 
   // One LDS array per stage: the compiler then knows which stage each
   // direct-to-LDS load writes and waits for exactly that one.
-  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t st3[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t st4[STAGE];
-  auto stage = [&](auto U) -> uint8_t* {
-    constexpr int u = decltype(U)::value % NSTAGE;
-    if constexpr (u == 0) return st0;
-    if constexpr (u == 1) return st1;
-    if constexpr (u == 2) return st2;
-    if constexpr (u == 3) return st3;
-    return st4;
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[SA];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[SA];
+  __shared__ __attribute__((aligned(16))) uint8_t sa2[SA];
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[SB];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[SB];
+  auto stA = [&](auto U) -> uint8_t* {
+    constexpr int u = decltype(U)::value % NSA;
+    if constexpr (u == 0) return sa0;
+    if constexpr (u == 1) return sa1;
+    return sa2;
   };
-  auto stage_rt = [&](int u) -> uint8_t* {  // u uniform and known after unrolling
-    return u == 0 ? st0 : u == 1 ? st1 : u == 2 ? st2 : st3;
+  auto stB = [&](auto U) -> uint8_t* {
+    constexpr int u = decltype(U)::value % NSB;
+    if constexpr (u == 0) return sb0;
+    return sb1;
   };
-  // The zero-point sums are published after the main loop in the last stage
-  // array, which the epilogue staging (at most four arrays) leaves free.
-  static_assert(FM < NSTAGE && (BM + BN) * 4 <= STAGE, "sums fit in the last stage");
-  int* const sums = reinterpret_cast<int*>(st4);
 
   int tm, tn;
   tile_coords<8>(p, tm, tn);
@@ -422,14 +494,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   const int wm = wave / WN, wn = wave % WN;
 
   typedef typename std::conditional<KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
-                                    RowLoader<NT, BM, EB, FAST>>::type ALoader;
+                                    RowDmaLoader<NT, BM, EB, FAST>>::type ALoader;
   ALoader la;
   if constexpr (KIND == KIND_F16_CONV) {
     la.init(p, m0);
   } else {
     la.init(p.A, p.lda, m0, p.M, p.K);
   }
-  RowLoader<NT, BN, EB, FAST> lb;
+  BLoader lb;
   lb.init(p.B, p.ldb, n0, p.N, p.K);
 
   acc_t acc[FM][FN];
@@ -451,20 +523,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 
   const int nk = (p.K * EB + KT_BYTES - 1) / KT_BYTES;
 
-  auto load_tile = [&](uint8_t* st, int kt) {
-    la.load(st, kt);
-    lb.load(st + BM * KT_BYTES, kt);
-  };
-
   // Fragments, double-buffered in registers: lane l reads row l % 32 of its
   // 32-row block, 16-byte chunk 2*ks + l/32 (k-step ks covers 32 bytes of K).
   const int frow = lane & 31;
   const int fhalf = lane >> 5;
   uint4 fa[2][FM], fb[2][FN];
-  auto read_frags = [&](const uint8_t* st, int ks, uint4 (&a)[FM], uint4 (&b)[FN]) {
-    const uint8_t* Bs = st + BM * KT_BYTES;
+  auto read_frags = [&](const uint8_t* As, const uint8_t* Bs, int ks, uint4 (&a)[FM], uint4 (&b)[FN]) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) a[i] = lds_read16(st, swz(wm * TM + i * 32 + frow, ks * 2 + fhalf));
+    for (int i = 0; i < FM; ++i) a[i] = lds_read16(As, swz(wm * TM + i * 32 + frow, ks * 2 + fhalf));
 #pragma unroll
     for (int j = 0; j < FN; ++j) b[j] = lds_read16(Bs, swz(wn * TN + j * 32 + frow, ks * 2 + fhalf));
   };
@@ -489,52 +555,82 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   };
   constexpr int NMF = FM * FN;  // MFMAs per k-step
   constexpr int NRD = FM + FN;  // fragment reads per k-step
+  constexpr int KSTEPS = KT_BYTES / 32;
 
-  // Prologue: K tiles 0 .. NSTAGE-2 in flight; wait for tile 0.
-  load_tile(st0, 0);
-  load_tile(st1, 1);
-  load_tile(st2, 2);
-  load_tile(st3, 3);
-  wait_vmcnt_lgkm0<(NSTAGE - 2) * NL>();
+  uint4 rb[NSB][NCH_B];  // B staging sets
+
+  // Prologue: tiles 0 and 1 in flight; tile 0 in LDS.
+  la.load(sa0, 0);
+  lb.load(rb[0], 0);
+  la.load(sa1, 1);
+  lb.load(rb[1], 1);
+  lb.store(sb0, rb[0]);
+  wait_vmcnt_lgkm0<NVM>();
   __builtin_amdgcn_s_barrier();
-  read_frags(st0, 0, fa[0], fb[0]);
+  read_frags(sa0, sb0, 0, fa[0], fb[0]);
 
-  // K tile kt lives in stage kt % NSTAGE.  Region 1: issue the loads of tile
-  // kt+NSTAGE-1 into the stage freed by tile kt-1, read the k-step 1
-  // fragments, run the k-step 0 MFMAs.  Then wait until this lane's loads of
-  // tile kt+1 have landed and every LDS read of this wave is done, and
-  // barrier (after it, tile kt+1 is complete in LDS and nobody reads tile kt
-  // any more).  Region 2: read the next tile's k-step 0 fragments under the
-  // k-step 1 MFMAs.  The instruction scheduler is asked to interleave memory
+  // K tile kt: A in stage kt % 3, B in stage kt % 2.
+  // Region 1: A of tile kt+2 -> stage (kt+2) % 3 (freed by tile kt-1), B of
+  // tile kt+2 -> staging set kt % 2, k-steps 0..KSTEPS-2 of tile kt, and the
+  // staging set of tile kt+1 -> B stage (kt+1) % 2.  Then wait until every
+  // load issued before this iteration has landed (A of tile kt+1 included)
+  // and every LDS access of this wave is done, and barrier.
+  // Region 2: the last k-step's MFMAs run over the reads of the next tile's
+  // first fragments.  The instruction scheduler is asked to spread the memory
   // instructions between the MFMAs, so the in-order wave never stalls behind
   // a burst of them.
   auto tile = [&](int kt, auto U) {
     constexpr int u = decltype(U)::value;
-    load_tile(stage(std::integral_constant<int, u + NSTAGE - 1>()), kt + NSTAGE - 1);
-    read_frags(stage(U), 1, fa[1], fb[1]);
-    mfmas(fa[0], fb[0]);
+    uint8_t* As = stA(U);
+    uint8_t* Bs = stB(U);
+    la.load(stA(std::integral_constant<int, u + 2>()), kt + 2);
+    lb.load(rb[u % NSB], kt + 2);
+    int buf = 0;
 #pragma unroll
-    for (int m = 0; m < NMF; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      if (m < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-      if ((m & 1) == 1 && (m >> 1) < NL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // load
+    for (int ks = 0; ks < KSTEPS - 1; ++ks) {
+      read_frags(As, Bs, ks + 1, fa[buf ^ 1], fb[buf ^ 1]);
+      mfmas(fa[buf], fb[buf]);
+      buf ^= 1;
     }
-    wait_vmcnt_lgkm0<(NSTAGE - 2) * NL>();
-    __builtin_amdgcn_s_barrier();
-    read_frags(stage(std::integral_constant<int, u + 1>()), 0, fa[0], fb[0]);
-    mfmas(fa[1], fb[1]);
+    lb.store(stB(std::integral_constant<int, u + 1>()), rb[(u + 1) % NSB]);
+    {
+      int rd = 0, vm = 0, wr = 0;
 #pragma unroll
-    for (int m = 0; m < NMF; ++m) {
+      for (int m = 0; m < (KSTEPS - 1) * NMF; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if ((m & 1) == 0 && rd < (KSTEPS - 1) * NRD) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          ++rd;
+        }
+        if (m % 3 == 0 && vm < NLA + NCH_B) {
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+          ++vm;
+        }
+        if (m % 3 == 1 && m >= NMF && wr < NCH_B) {
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+          ++wr;
+        }
+      }
+    }
+    wait_vmcnt_lgkm0<NVM>();
+    __builtin_amdgcn_s_barrier();
+    read_frags(stA(std::integral_constant<int, u + 1>()), stB(std::integral_constant<int, u + 1>()), 0,
+               fa[buf ^ 1], fb[buf ^ 1]);
+    mfmas(fa[buf], fb[buf]);
+#pragma unroll
+    for (int q = 0; q < NMF; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (m < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  for (int kt = 0; kt < nk; kt += NSTAGE) {
+  static_assert(KSTEPS % 2 == 0, "the fragment double buffer returns to set 0 after a tile");
+  for (int kt = 0; kt < nk; kt += 6) {
     tile(kt, std::integral_constant<int, 0>());
     if (kt + 1 < nk) tile(kt + 1, std::integral_constant<int, 1>());
     if (kt + 2 < nk) tile(kt + 2, std::integral_constant<int, 2>());
     if (kt + 3 < nk) tile(kt + 3, std::integral_constant<int, 3>());
     if (kt + 4 < nk) tile(kt + 4, std::integral_constant<int, 4>());
+    if (kt + 5 < nk) tile(kt + 5, std::integral_constant<int, 5>());
   }
   // Loads past the last tile may still be writing (zeros): drain them before
   // the epilogue reuses the stage arrays.
@@ -554,6 +650,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // in register e, row 8*(e/4) + 4*(l/32) + e%4.
   const int ccol = lane & 31;
   const int rbase = 4 * (lane >> 5);
+  // Staging arrays for 32-row blocks: the three A stages and the first B
+  // stage (each holds 32 x BN x 4 bytes since BN <= BM); the zero-point sums
+  // go to the second B stage.
+  auto stage_rt = [&](int u) -> uint8_t* {  // u is a constant after unrolling
+    return u == 0 ? sa0 : u == 1 ? sa1 : u == 2 ? sa2 : sb0;
+  };
+  static_assert(32 * BN * 4 <= SB && (BM + BN) * 4 <= SB, "staging and sums fit in the B stages");
+  int* const sums = reinterpret_cast<int*>(sb1);
   auto stage_off = [](int rl, int c) {  // rl: row within a 32-row array; c: column
     return rl * (BN * 4) + (((c >> 2) ^ (8 * ((rl >> 2) & 1))) << 4) + (c & 3) * 4;
   };
