@@ -44,7 +44,7 @@ PEAK_I8_TOPS = 5033.2
 HBM_GBPS = 8000.0
 SRC_FILES = ("implicit_gemm_convolution_amd/csrc/igc.hip",
              "implicit_gemm_convolution_amd/csrc/igc_kernels.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
 def kernel_source_hash() -> str:
@@ -192,18 +192,23 @@ def cpu_baseline(wl, budget_s: float) -> dict:
 
 
 def traffic_for(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it matches these sources."""
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources (else None)."""
     try:
         with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-    except (OSError, ValueError):
+            text = f.read()
+    except OSError:
         return None
-    if tr.get("kernel_source_hash") != kernel_source_hash():
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("kernel_source_hash:"):
+            vals["hash"] = line.split(":", 1)[1].strip()
+        elif line.startswith("hbm_bytes_per_launch "):
+            key, v = line[len("hbm_bytes_per_launch "):].split(":", 1)
+            vals[key.strip()] = int(v)
+    if vals.get("hash") != kernel_source_hash():
         return None
-    w = tr.get("workloads", {}).get(workload)
-    if not w:
-        return None
-    return w.get("hbm_bytes_per_launch")
+    return vals.get(workload)
 
 
 def main(argv=None) -> int:
