@@ -129,6 +129,16 @@ __device__ __forceinline__ void lds_write16(uint8_t* base, int off, uint4 v) {
   *reinterpret_cast<uint4*>(base + off) = v;
 }
 
+// Output stores bypass the caches' retention (non-temporal): the results are
+// not read again by the kernel, and streaming them measured ~20% faster.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16_nt(void* dst, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(dst));
+}
+__device__ __forceinline__ void store4_nt(void* dst, uint32_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(dst));
+}
+
 // ---------------------------------------------------------------------------
 // Buffer descriptors and direct-to-LDS loads.
 // ---------------------------------------------------------------------------
@@ -153,6 +163,9 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, ui
 // global chunk that belongs in its LDS slot l % 8, i.e. chunk
 // (l % 8) ^ ((4q + l/16) % 8).  Instruction q = i*NWAVES + wave, i < NQ; with
 // an even wave count q % 2 = wave % 2, so each lane's chunk is fixed.
+// Index of the calling wave in its workgroup, as a scalar (wave-uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 template <int NT, int ROWS>
 struct DmaShape {
   static constexpr int NWAVES = NT / 64;
@@ -166,7 +179,7 @@ struct DmaShape {
     return (l & 7) ^ ((4 * ((threadIdx.x >> 6) & 1) + (l >> 4)) & 7);
   }
   __device__ static __forceinline__ uint8_t* dst(uint8_t* tile, int i) {
-    return tile + (i * NWAVES + (int)(threadIdx.x >> 6)) * 1024;
+    return tile + (i * NWAVES + wave_id()) * 1024;
   }
 };
 
@@ -490,7 +503,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int wm = wave / WN, wn = wave % WN;
 
   typedef typename std::conditional<KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
@@ -723,7 +736,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
         if constexpr (!INT8) {
           float* dst = p.Cf + (long long)row * p.ldcf + col;
           if (full && p.vec_c) {
-            *reinterpret_cast<uint4*>(dst) = v;
+            store16_nt(dst, v);
           } else {
             const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -747,7 +760,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           if (p.Ci) {
             int32_t* dst = p.Ci + (long long)row * p.ldci + col;
             if (full && p.vec_c) {
-              *reinterpret_cast<int4*>(dst) = make_int4(c[0], c[1], c[2], c[3]);
+              store16_nt(dst, make_uint4((uint32_t)c[0], (uint32_t)c[1], (uint32_t)c[2], (uint32_t)c[3]));
             } else {
 #pragma unroll
               for (int q = 0; q < 4; ++q)
@@ -763,7 +776,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) d[q] = cf[q] * p.dq;
             if (full && p.vec_d) {
-              *reinterpret_cast<float4*>(dst) = make_float4(d[0], d[1], d[2], d[3]);
+              store16_nt(dst, make_uint4(__builtin_bit_cast(uint32_t, d[0]), __builtin_bit_cast(uint32_t, d[1]),
+                                         __builtin_bit_cast(uint32_t, d[2]), __builtin_bit_cast(uint32_t, d[3])));
             } else {
 #pragma unroll
               for (int q = 0; q < 4; ++q)
@@ -785,7 +799,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
               packed |= (uint32_t)(uint8_t)qv[q] << (8 * q);
             }
             if (full && p.vec_q) {
-              *reinterpret_cast<uint32_t*>(dst) = packed;
+              store4_nt(dst, packed);
             } else {
 #pragma unroll
               for (int q = 0; q < 4; ++q)
