@@ -1,0 +1,75 @@
+"""Checks on the gfx950 assembly of the library's own kernels (CPU only):
+every kernel computes on the matrix cores with the instruction of its dtype,
+the large-tile kernels use no scratch memory, fit the 160 KiB LDS, load
+operands straight into LDS and stream their outputs."""
+from __future__ import annotations
+
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    from implicit_gemm_convolution_amd import build
+
+    out = tmp_path_factory.mktemp("asm")
+    path = build.assembly(str(out))
+    text = open(path).read()
+    kernels = {}
+    for name in re.findall(r"^\s+\.amdhsa_kernel (\S+)", text, re.M):
+        start = re.search(r"^" + re.escape(name) + r":", text, re.M)
+        assert start, name
+        body = text[start.end():].split("s_endpgm", 1)[0]
+        meta = text.split(".amdhsa_kernel " + name, 1)[1].split(".end_amdhsa_kernel", 1)[0]
+        demangled = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip()
+        kernels[demangled] = (body, meta)
+    assert kernels
+    return kernels
+
+
+def _params(demangled):
+    m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (true|false), (true|false)>", demangled)
+    assert m, demangled
+    kind, bm, bn, wm, wn = (int(m.group(i)) for i in range(1, 6))
+    return kind, bm, bn, m.group(6) == "true"
+
+
+def test_every_kernel_uses_mfma_of_its_dtype(asm):
+    for name, (body, _) in asm.items():
+        kind, bm, bn, fast = _params(name)
+        want = "v_mfma_i32_32x32x32_i8" if kind == 2 else "v_mfma_f32_32x32x16_f16"
+        assert want in body, name
+        other = "v_mfma_f32_32x32x16_f16" if kind == 2 else "v_mfma_i32_32x32x32_i8"
+        assert other not in body, name
+
+
+def test_no_scratch_and_lds_within_limit(asm):
+    for name, (_, meta) in asm.items():
+        kind, bm, bn, fast = _params(name)
+        lds = int(re.search(r"\.amdhsa_group_segment_fixed_size (\d+)", meta).group(1))
+        assert lds <= 160 * 1024, name
+        scratch = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", meta).group(1))
+        if bm == 256 and bn == 256:
+            assert scratch == 0, (name, scratch)
+
+
+def test_fast_kernels_load_straight_into_lds_and_stream_outputs(asm):
+    for name, (body, _) in asm.items():
+        kind, bm, bn, fast = _params(name)
+        if not fast:
+            continue
+        assert re.search(r"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], 0 offen lds", body), name
+        assert re.search(r"global_store_dword(x4)? .* nt", body), name
+
+
+def test_no_packed_fp32_and_no_fma_in_epilogue_math(asm):
+    for name, (body, _) in asm.items():
+        assert "v_pk_add_f32" not in body and "v_pk_mul_f32" not in body and "v_pk_fma_f32" not in body
+        kind, *_ = _params(name)
+        if kind == 2:  # requantize: two separately rounded operations
+            assert "v_fma_f32" not in body and "v_fmac_f32" not in body and "v_fmamk_f32" not in body, name
