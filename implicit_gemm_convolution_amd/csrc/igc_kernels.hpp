@@ -18,10 +18,10 @@
 //  * Both operands are K-contiguous (A row-major, B column-major), so a tile
 //    row is one 128-byte run: every load request is a whole cache line.
 //  * The K loop is software-pipelined two tiles deep ([TIR-COMPILER] §2.2 and
-//    §4.4): the A tile goes from HBM straight into one of three LDS stages with
-//    buffer loads that write LDS; the B tile goes through one of two register
-//    staging sets into one of two LDS stages.  Loads for tile kt+2 are issued
-//    while tile kt is computed (three A stages and two B stages fill the
+//    §4.4): one operand goes from HBM straight into one of three LDS stages
+//    with buffer loads that write LDS; the other goes through one of two
+//    register staging sets into one of two LDS stages.  Loads for tile kt+2
+//    are issued while tile kt is computed (three plus two stages fill the
 //    160 KiB LDS at 256x256).  Out-of-range buffer offsets read as zeros:
 //    ragged tiles, K tails and the convolution's zero padding need no
 //    branches.
@@ -37,8 +37,9 @@
 //    never matters.  Fragments are read one k-step ahead; the last k-step's
 //    MFMAs of a tile run after the barrier, hiding the next tile's reads.
 //  * u8 activations on the signed i8 MFMA: A' = A - 128 = A xor 0x80 per byte,
-//    applied to the fragment after it is read from LDS; the epilogue then uses
-//    zA' = zA - 128 in the four-term identity of [GEMM-TVM] §2.3.
+//    applied on the way into LDS (the u8 A takes the register path); the
+//    epilogue then uses zA' = zA - 128 in the four-term identity of
+//    [GEMM-TVM] §2.3.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,8 +60,6 @@ enum Kind : int { KIND_F16_GEMM = 0, KIND_F16_CONV = 1, KIND_U8I8_GEMM = 2 };
 constexpr int KT_BYTES = 128;    // bytes of K per tile row
 constexpr int CHUNK_BYTES = 16;  // one vector load
 constexpr int CPR = KT_BYTES / CHUNK_BYTES;  // chunks per tile row
-constexpr int NSA = 3;           // LDS stages of A
-constexpr int NSB = 2;           // LDS stages (and register staging sets) of B
 
 struct Params {
   // GEMM view: M x N output, K reduction.
@@ -183,7 +182,8 @@ struct DmaShape {
   }
 };
 
-// A operand of a GEMM (row-major, rows of K).
+// Operand loaded straight into LDS (A of the fp16 GEMM; the i8 B of the
+// u8 x i8 GEMM): rows of K.
 //  FAST: 16-byte aligned rows, K a multiple of the chunk: direct-to-LDS loads.
 //  else: element-wise loads, written to LDS with the same layout.
 template <int NT, int ROWS, int EB, bool FAST>
@@ -242,10 +242,10 @@ struct RowDmaLoader {
   }
 };
 
-// B operand (column-major B, i.e. rows of K; also the conv weight), staged
-// through registers: thread t holds chunk t%8 of rows t/8 + (NT/8)*j, so each
-// group of 8 lanes fetches one whole 128-byte line.
-template <int NT, int ROWS, int EB, bool FAST>
+// Operand staged through registers (B of the fp16 GEMM and the conv weight;
+// the u8 A of the u8 x i8 GEMM): thread t holds chunk t%8 of rows
+// t/8 + (NT/8)*j, so each group of 8 lanes fetches one whole 128-byte line.
+template <int NT, int ROWS, int EB, bool FAST, bool XOR80 = false>
 struct RowRegLoader {
   static constexpr int NCH = ROWS * CPR / NT;  // chunks per thread
   const uint8_t* base;
@@ -301,10 +301,17 @@ struct RowRegLoader {
     }
   }
 
+  // XOR80: u8 -> s8 operand, A' = A - 128 = A xor 0x80 per byte, applied on
+  // the way into LDS (padding bytes 0 become A' = 0).
   __device__ __forceinline__ void store(uint8_t* tile, const uint4 (&r)[NCH]) const {
 #pragma unroll
-    for (int j = 0; j < NCH; ++j)
-      lds_write16(tile, swz((threadIdx.x >> 3) + j * (NT / 8), threadIdx.x & 7), r[j]);
+    for (int j = 0; j < NCH; ++j) {
+      uint4 v = r[j];
+      if constexpr (XOR80) {
+        v.x ^= 0x80808080u; v.y ^= 0x80808080u; v.z ^= 0x80808080u; v.w ^= 0x80808080u;
+      }
+      lds_write16(tile, swz((threadIdx.x >> 3) + j * (NT / 8), threadIdx.x & 7), v);
+    }
   }
 };
 
@@ -467,35 +474,54 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int SA = BM * KT_BYTES, SB = BN * KT_BYTES;  // stage sizes
   constexpr bool INT8 = KIND == KIND_U8I8_GEMM;
-  typedef RowRegLoader<NT, BN, EB, FAST> BLoader;
-  constexpr int NCH_B = BLoader::NCH;
-  // vector-memory instructions per K tile per lane (the A loads count only
-  // on the direct-to-LDS path; element-wise loads are waited for by the
-  // compiler before they are used)
-  constexpr int NLA = FAST ? DmaShape<NT, BM>::NQ : 0;
-  constexpr int NVM = NLA + (FAST ? NCH_B : 0);
+  // Operand roles: one operand streams straight into a 3-stage LDS ring (X),
+  // the other goes through 2 register staging sets into a 2-stage ring (Y).
+  // The u8 A of the integer GEMM takes the register path so that its
+  // u8 -> s8 conversion happens once, on the way into LDS, rather than on
+  // every fragment read.
+  constexpr bool A_IN_X = !INT8;
+  constexpr int SX = A_IN_X ? SA : SB, SY = A_IN_X ? SB : SA;
+  typedef typename std::conditional<
+      KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
+      typename std::conditional<A_IN_X, RowDmaLoader<NT, BM, EB, FAST>,
+                                RowRegLoader<NT, BM, EB, FAST, true>>::type>::type ALoader;
+  typedef typename std::conditional<A_IN_X, RowRegLoader<NT, BN, EB, FAST>,
+                                    RowDmaLoader<NT, BN, EB, FAST>>::type BLoader;
+  typedef typename std::conditional<A_IN_X, BLoader, ALoader>::type YLoader;  // register path
+  constexpr int NCH_Y = YLoader::NCH;
+  // vector-memory instructions per K tile per lane (the X loads count only on
+  // the direct-to-LDS path; element-wise loads are waited for by the compiler
+  // before they are used)
+  constexpr int NLX = FAST ? DmaShape<NT, A_IN_X ? BM : BN>::NQ : 0;
+  constexpr int NVM = NLX + (FAST ? NCH_Y : 0);
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(FM <= NSA + 1 && BM >= BN, "epilogue staging reuses the stage arrays");
+  static_assert(FM <= 4 && BM >= BN, "epilogue staging reuses the stage arrays");
   static_assert(NVM < 64, "vmcnt range");
   typedef typename Mfma<KIND>::acc_t acc_t;
 
   // One LDS array per stage: the compiler then knows which stage each
   // direct-to-LDS load writes and waits for exactly that one.
-  __shared__ __attribute__((aligned(16))) uint8_t sa0[SA];
-  __shared__ __attribute__((aligned(16))) uint8_t sa1[SA];
-  __shared__ __attribute__((aligned(16))) uint8_t sa2[SA];
-  __shared__ __attribute__((aligned(16))) uint8_t sb0[SB];
-  __shared__ __attribute__((aligned(16))) uint8_t sb1[SB];
+  __shared__ __attribute__((aligned(16))) uint8_t sx0[SX];
+  __shared__ __attribute__((aligned(16))) uint8_t sx1[SX];
+  __shared__ __attribute__((aligned(16))) uint8_t sx2[SX];
+  __shared__ __attribute__((aligned(16))) uint8_t sy0[SY];
+  __shared__ __attribute__((aligned(16))) uint8_t sy1[SY];
+  auto stX = [&](auto U) -> uint8_t* {
+    constexpr int u = decltype(U)::value % 3;
+    if constexpr (u == 0) return sx0;
+    if constexpr (u == 1) return sx1;
+    return sx2;
+  };
+  auto stY = [&](auto U) -> uint8_t* {
+    constexpr int u = decltype(U)::value % 2;
+    if constexpr (u == 0) return sy0;
+    return sy1;
+  };
   auto stA = [&](auto U) -> uint8_t* {
-    constexpr int u = decltype(U)::value % NSA;
-    if constexpr (u == 0) return sa0;
-    if constexpr (u == 1) return sa1;
-    return sa2;
+    if constexpr (A_IN_X) return stX(U); else return stY(U);
   };
   auto stB = [&](auto U) -> uint8_t* {
-    constexpr int u = decltype(U)::value % NSB;
-    if constexpr (u == 0) return sb0;
-    return sb1;
+    if constexpr (A_IN_X) return stY(U); else return stX(U);
   };
 
   int tm, tn;
@@ -506,8 +532,6 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   const int wave = wave_id();
   const int wm = wave / WN, wn = wave % WN;
 
-  typedef typename std::conditional<KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
-                                    RowDmaLoader<NT, BM, EB, FAST>>::type ALoader;
   ALoader la;
   if constexpr (KIND == KIND_F16_CONV) {
     la.init(p, m0);
@@ -547,14 +571,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) b[j] = lds_read16(Bs, swz(wn * TN + j * 32 + frow, ks * 2 + fhalf));
   };
-  auto mfmas = [&](uint4 (&a)[FM], const uint4 (&b)[FN]) {
-    if constexpr (INT8) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        a[i].x ^= 0x80808080u; a[i].y ^= 0x80808080u;
-        a[i].z ^= 0x80808080u; a[i].w ^= 0x80808080u;
-      }
-    }
+  auto mfmas = [&](const uint4 (&a)[FM], const uint4 (&b)[FN]) {
     if constexpr (SUMS) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) rsum[i] = sum_bytes(a[i], rsum[i]);
@@ -570,34 +587,44 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int NRD = FM + FN;  // fragment reads per k-step
   constexpr int KSTEPS = KT_BYTES / 32;
 
-  uint4 rb[NSB][NCH_B];  // B staging sets
+  // The two operand paths: X straight into LDS, Y through registers.
+  auto x_load = [&](uint8_t* st, int kt) {
+    if constexpr (A_IN_X) la.load(st, kt); else lb.load(st, kt);
+  };
+  auto y_load = [&](uint4 (&r)[NCH_Y], int kt) {
+    if constexpr (A_IN_X) lb.load(r, kt); else la.load(r, kt);
+  };
+  auto y_store = [&](uint8_t* st, const uint4 (&r)[NCH_Y]) {
+    if constexpr (A_IN_X) lb.store(st, r); else la.store(st, r);
+  };
+  uint4 ry[2][NCH_Y];  // register staging sets
 
   // Prologue: tiles 0 and 1 in flight; tile 0 in LDS.
-  la.load(sa0, 0);
-  lb.load(rb[0], 0);
-  la.load(sa1, 1);
-  lb.load(rb[1], 1);
-  lb.store(sb0, rb[0]);
+  x_load(sx0, 0);
+  y_load(ry[0], 0);
+  x_load(sx1, 1);
+  y_load(ry[1], 1);
+  y_store(sy0, ry[0]);
   wait_vmcnt_lgkm0<NVM>();
   __builtin_amdgcn_s_barrier();
-  read_frags(sa0, sb0, 0, fa[0], fb[0]);
+  read_frags(stA(std::integral_constant<int, 0>()), stB(std::integral_constant<int, 0>()), 0, fa[0], fb[0]);
 
-  // K tile kt: A in stage kt % 3, B in stage kt % 2.
-  // Region 1: A of tile kt+2 -> stage (kt+2) % 3 (freed by tile kt-1), B of
-  // tile kt+2 -> staging set kt % 2, k-steps 0..KSTEPS-2 of tile kt, and the
-  // staging set of tile kt+1 -> B stage (kt+1) % 2.  Then wait until every
-  // load issued before this iteration has landed (A of tile kt+1 included)
-  // and every LDS access of this wave is done, and barrier.
-  // Region 2: the last k-step's MFMAs run over the reads of the next tile's
-  // first fragments.  The instruction scheduler is asked to spread the memory
+  // K tile kt: X operand in stage kt % 3 (the stage of tile kt+2 is the one
+  // tile kt-1 used), Y operand in stage kt % 2, Y of tile kt+2 in staging set
+  // kt % 2.  Region 1: loads of tile kt+2, k-steps 0..KSTEPS-2 of tile kt,
+  // staging set of tile kt+1 -> Y stage (kt+1) % 2.  Then wait until every
+  // load issued before this iteration has landed (X of tile kt+1 included)
+  // and every LDS access of this wave is done, and barrier.  Region 2: the
+  // last k-step's MFMAs run over the reads of the next tile's first
+  // fragments.  The instruction scheduler is asked to spread the memory
   // instructions between the MFMAs, so the in-order wave never stalls behind
   // a burst of them.
   auto tile = [&](int kt, auto U) {
     constexpr int u = decltype(U)::value;
-    uint8_t* As = stA(U);
-    uint8_t* Bs = stB(U);
-    la.load(stA(std::integral_constant<int, u + 2>()), kt + 2);
-    lb.load(rb[u % NSB], kt + 2);
+    const uint8_t* As = stA(U);
+    const uint8_t* Bs = stB(U);
+    x_load(stX(std::integral_constant<int, u + 2>()), kt + 2);
+    y_load(ry[u % 2], kt + 2);
     int buf = 0;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS - 1; ++ks) {
@@ -605,7 +632,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       mfmas(fa[buf], fb[buf]);
       buf ^= 1;
     }
-    lb.store(stB(std::integral_constant<int, u + 1>()), rb[(u + 1) % NSB]);
+    y_store(stY(std::integral_constant<int, u + 1>()), ry[(u + 1) % 2]);
     {
       int rd = 0, vm = 0, wr = 0;
 #pragma unroll
@@ -615,11 +642,11 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
           ++rd;
         }
-        if (m % 3 == 0 && vm < NLA + NCH_B) {
+        if (m % 3 == 0 && vm < NLX + NCH_Y) {
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
           ++vm;
         }
-        if (m % 3 == 1 && m >= NMF && wr < NCH_B) {
+        if (m % 3 == 1 && m >= NMF && wr < NCH_Y) {
           __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
           ++wr;
         }
@@ -663,14 +690,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // in register e, row 8*(e/4) + 4*(l/32) + e%4.
   const int ccol = lane & 31;
   const int rbase = 4 * (lane >> 5);
-  // Staging arrays for 32-row blocks: the three A stages and the first B
+  // Staging arrays for 32-row blocks: the three X stages and the first Y
   // stage (each holds 32 x BN x 4 bytes since BN <= BM); the zero-point sums
-  // go to the second B stage.
+  // go to the second Y stage.
   auto stage_rt = [&](int u) -> uint8_t* {  // u is a constant after unrolling
-    return u == 0 ? sa0 : u == 1 ? sa1 : u == 2 ? sa2 : sb0;
+    return u == 0 ? sx0 : u == 1 ? sx1 : u == 2 ? sx2 : sy0;
   };
-  static_assert(32 * BN * 4 <= SB && (BM + BN) * 4 <= SB, "staging and sums fit in the B stages");
-  int* const sums = reinterpret_cast<int*>(sb1);
+  static_assert(32 * BN * 4 <= SB && (BM + BN) * 4 <= SB, "staging and sums fit in the stages");
+  int* const sums = reinterpret_cast<int*>(sy1);
   auto stage_off = [](int rl, int c) {  // rl: row within a 32-row array; c: column
     return rl * (BN * 4) + (((c >> 2) ^ (8 * ((rl >> 2) & 1))) << 4) + (c & 3) * 4;
   };
@@ -680,7 +707,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     // Complete the row / column sums (the two K halves live in lanes l, l^32)
     // and publish them through LDS.
     if (want_rsum) {
-      // K-tail padding reads as byte 0, i.e. A' = -128: add those terms back.
+      // K-tail padding loads as byte 0 and is stored as A' = -128: add those
+      // terms back.
       const int pad_fix = 128 * (nk * KT_BYTES - p.K);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
