@@ -14,32 +14,36 @@
 //  * Each workgroup owns one BM x BN tile of C and walks K in tiles of 128
 //    bytes per row (64 fp16 or 128 int8 elements): the block / warp / fragment
 //    hierarchy of [GEMM-TVM] §4.2 and [CONV-TC] "Scheduling the computation",
-//    re-derived for 64-wide waves and 32x32 MFMA tiles.
+//    re-derived for 64-wide waves and 16x16 MFMA blocks.
 //  * Both operands are K-contiguous (A row-major, B column-major), so a tile
 //    row is one 128-byte run: every load request is a whole cache line.
-//  * The K loop is software-pipelined two tiles deep ([TIR-COMPILER] §2.2 and
-//    §4.4): one operand goes from HBM straight into one of three LDS stages
-//    with buffer loads that write LDS; the other goes through one of two
-//    register staging sets into one of two LDS stages.  Loads for tile kt+2
-//    are issued while tile kt is computed (three plus two stages fill the
-//    160 KiB LDS at 256x256).  Out-of-range buffer offsets read as zeros:
-//    ragged tiles, K tails and the convolution's zero padding need no
-//    branches.
+//  * Both operands go from HBM straight into LDS with buffer loads that write
+//    LDS (no register staging).  The K loop is software-pipelined
+//    ([TIR-COMPILER] §2.2 and §4.4): A has three LDS stages and its tile kt+2
+//    is loaded during the first k-step of tile kt; B has two and its tile
+//    kt+2 is loaded during the last k-step, right after the barrier that frees
+//    tile kt's stage (3 x 32 + 2 x 32 KiB fill the 160 KiB LDS at 256x256).
+//    The loads are spread one per MFMA row over the k-steps in program order,
+//    so the address unit's queues never fill and stall the wave.  Out-of-range
+//    buffer offsets read as zeros: ragged tiles, K tails and the
+//    convolution's zero padding need no branches.
 //  * LDS rows are 128 bytes; the 16-byte chunk c of row r sits in slot
 //    c ^ ((r >> 1) & 7), so fragment reads and tile writes are free of bank
 //    conflicts on the 64-bank LDS (see swz()).  This replaces the padding
 //    offsets of [GEMM-TVM] §3.2 and storage_align of [TIR-PRACTICE] §2.2 with
 //    the swizzle named in [TIR-COMPILER] §2.2.
-//  * MFMA: v_mfma_f32_32x32x16_f16 and v_mfma_i32_32x32x32_i8.  Each lane
+//  * MFMA: v_mfma_f32_16x16x32_f16 and v_mfma_i32_16x16x64_i8.  Each lane
 //    feeds 16 bytes of one row of A and 16 bytes of one column of B per
-//    instruction (lane l: row/column l % 32, K half l / 32).  A and B use the
-//    same (lane, element) -> k assignment, so the K order inside one MFMA
-//    never matters.  Fragments are read one k-step ahead; the last k-step's
-//    MFMAs of a tile run after the barrier, hiding the next tile's reads.
-//  * u8 activations on the signed i8 MFMA: A' = A - 128 = A xor 0x80 per byte,
-//    applied on the way into LDS (the u8 A takes the register path); the
-//    epilogue then uses zA' = zA - 128 in the four-term identity of
-//    [GEMM-TVM] §2.3.
+//    instruction (lane l: row/column l % 16, 16-byte chunk l / 16 of the
+//    64-byte k-step).  A and B use the same (lane, element) -> k assignment,
+//    so the K order inside one MFMA never matters.  On MI355X the 16x16 forms
+//    hold a higher clock under the power limit than the 32x32 forms with the
+//    same work per cycle.  Fragments are read one k-step ahead; the last
+//    k-step's MFMAs of a tile run after the barrier, hiding the next tile's
+//    reads.
+//  * u8 activations on the signed i8 MFMA: A' = A - 128 = A xor 0x80 per
+//    byte, applied to each A fragment just before use; the epilogue then uses
+//    zA' = zA - 128 in the four-term identity of [GEMM-TVM] §2.3.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -54,6 +58,11 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#ifndef IGC_MFMA_DIM
+#define IGC_MFMA_DIM 16
+#endif
 
 enum Kind : int { KIND_F16_GEMM = 0, KIND_F16_CONV = 1, KIND_U8I8_GEMM = 2 };
 
@@ -143,18 +152,38 @@ __device__ __forceinline__ void store4_nt(void* dst, uint32_t v) {
 // ---------------------------------------------------------------------------
 constexpr uint32_t OOB = 0x80000000u;  // descriptors are limited to < 2^31 bytes
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+// A buffer descriptor, both as the compiler's resource type (for the
+// compiler-visible loads) and as the four raw words (for the inline-assembly
+// direct-to-LDS loads).
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t r;
+  i32x4 d;
+};
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   // word 3 = 0x00020000: raw (untyped) 32-bit-dword buffer on gfx9-family GPUs.
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
+  Rsrc x;
+  x.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  x.d = i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+  return x;
 }
-
-// One wave-wide 16-byte-per-lane load written to LDS: lane l's 16 bytes land
-// at lds + 16*l (lds is uniform across the wave).  An offset past the
-// descriptor's extent writes zeros.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
+// The direct-to-LDS load is issued from inline assembly: the compiler then
+// neither reorders it (program order is the schedule) nor inserts its own,
+// conservative vmcnt waits before later LDS reads (it cannot tell the stage
+// arrays apart across the loop's back edge).  Every wait for these loads is
+// explicit in the kernel.  One wait state separates the M0 write from the
+// load.  IGC_DMA_ASM=0 selects the compiler builtin instead.
+#ifndef IGC_DMA_ASM
+#define IGC_DMA_ASM 1
+#endif
+__device__ __forceinline__ void dma16(const Rsrc& r, uint8_t* lds, uint32_t off) {
+  if constexpr (IGC_DMA_ASM) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(r.d), "{m0}"(m0) : "memory");
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r.r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
+  }
 }
 
 // Direct-to-LDS tiles of ROWS rows x 128 bytes.  Wave-instruction q fills
@@ -193,7 +222,7 @@ struct RowDmaLoader {
   long long ld_bytes;
   int rows_valid;       // rows of this tile that exist
   int K;
-  __amdgpu_buffer_rsrc_t rsrc;
+  Rsrc rsrc;
   uint32_t lane_off;    // byte offset of this lane's first row and chunk
   uint32_t row_step;    // bytes between this lane's rows (uniform)
 
@@ -210,14 +239,20 @@ struct RowDmaLoader {
     }
   }
 
-  // Fill `tile` (ROWS x 128 bytes, swizzled) with K tile kt; rows past the
-  // operand and k past K read as zero bytes.
+  // Loading K tile kt into `tile` (ROWS x 128 bytes, swizzled) takes NPART
+  // calls part(tile, kt, i), i = 0..NPART-1, then advance(); rows past the
+  // operand and k past K read as zero bytes.  FAST: part i is one
+  // direct-to-LDS load of 8 rows per wave; else part 0 does it all.
+  static constexpr int NPART = FAST ? Sh::NQ : 1;
+  __device__ __forceinline__ void advance() const {}
   __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
+#pragma unroll
+    for (int i = 0; i < NPART; ++i) part(tile, kt, i);
+  }
+  __device__ __forceinline__ void part(uint8_t* tile, int kt, int i) const {
     if (FAST) {
       const bool kin = kt * KT_BYTES + Sh::lane_chunk() * CHUNK_BYTES < K * EB;
-#pragma unroll
-      for (int i = 0; i < Sh::NQ; ++i)
-        dma16(rsrc, Sh::dst(tile, i), kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
+      dma16(rsrc, Sh::dst(tile, i), kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
     } else {
       constexpr int EPC = CHUNK_BYTES / EB;
       const int c = threadIdx.x & 7;  // thread t: chunk t%8 of rows t/8 + (NT/8)*j
@@ -242,79 +277,6 @@ struct RowDmaLoader {
   }
 };
 
-// Operand staged through registers (B of the fp16 GEMM and the conv weight;
-// the u8 A of the u8 x i8 GEMM): thread t holds chunk t%8 of rows
-// t/8 + (NT/8)*j, so each group of 8 lanes fetches one whole 128-byte line.
-template <int NT, int ROWS, int EB, bool FAST, bool XOR80 = false>
-struct RowRegLoader {
-  static constexpr int NCH = ROWS * CPR / NT;  // chunks per thread
-  const uint8_t* base;
-  long long ld_bytes;
-  int rows_valid;
-  int K;
-  __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t lane_off;  // byte offset of this thread's first row and chunk
-  uint32_t row_step;  // bytes between its rows (uniform)
-
-  __device__ __forceinline__ void init(const uint8_t* ptr, long long ld, int r0, int nrows, int k) {
-    ld_bytes = ld * EB;
-    base = ptr + (long long)r0 * ld_bytes;
-    rows_valid = nrows - r0;
-    K = k;
-    if (FAST) {
-      const long long extent = (long long)min(rows_valid, ROWS) * ld_bytes;
-      rsrc = make_rsrc(base, (uint32_t)extent);
-      lane_off = (uint32_t)((threadIdx.x >> 3) * ld_bytes) + (uint32_t)((threadIdx.x & 7) * CHUNK_BYTES);
-      row_step = (uint32_t)((NT / 8) * ld_bytes);
-    }
-  }
-
-  __device__ __forceinline__ void load(uint4 (&r)[NCH], int kt) const {
-    constexpr int EPC = CHUNK_BYTES / EB;
-    const int c = threadIdx.x & 7;
-    if (FAST) {
-      const bool kin = kt * KT_BYTES + c * CHUNK_BYTES < K * EB;
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        auto v = __builtin_amdgcn_raw_buffer_load_b128(
-            rsrc, (int)(kin ? lane_off + (uint32_t)(j * row_step + kt * KT_BYTES) : OOB), 0, 0);
-        r[j] = make_uint4(v[0], v[1], v[2], v[3]);
-      }
-    } else {
-      const int k0 = kt * (KT_BYTES / EB) + c * EPC;
-#pragma unroll
-      for (int j = 0; j < NCH; ++j) {
-        const int row = (threadIdx.x >> 3) + j * (NT / 8);
-        const uint8_t* rp = base + (long long)row * ld_bytes;
-        uint8_t bytes[16];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const int k = k0 + e;
-          const bool ok = row < rows_valid && k < K;
-#pragma unroll
-          for (int b = 0; b < EB; ++b) bytes[e * EB + b] = ok ? rp[(long long)k * EB + b] : (uint8_t)0;
-        }
-        uint4 v;
-        __builtin_memcpy(&v, bytes, 16);
-        r[j] = v;
-      }
-    }
-  }
-
-  // XOR80: u8 -> s8 operand, A' = A - 128 = A xor 0x80 per byte, applied on
-  // the way into LDS (padding bytes 0 become A' = 0).
-  __device__ __forceinline__ void store(uint8_t* tile, const uint4 (&r)[NCH]) const {
-#pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      uint4 v = r[j];
-      if constexpr (XOR80) {
-        v.x ^= 0x80808080u; v.y ^= 0x80808080u; v.z ^= 0x80808080u; v.w ^= 0x80808080u;
-      }
-      lds_write16(tile, swz((threadIdx.x >> 3) + j * (NT / 8), threadIdx.x & 7), v);
-    }
-  }
-};
-
 // Implicit im2col view of an NHWC fp16 input (the conv's A operand): row
 // m = (n, p, q), column k = (r*S + s)*C + c holds
 // x[n, p*sh + r - ph, q*sw + s - pw, c], or 0 where that position lies in the
@@ -331,7 +293,7 @@ struct Im2colLoader {
   int pix[NR];  // pixel index in x of (n, p*sh - ph, q*sw - pw), i.e. of tap (0, 0)
   int hw[NR];   // (p*sh - ph) << 16 | (q*sw - pw) & 0xffff; INT32_MIN for rows past M
   int H, W, C, S, K;
-  __amdgpu_buffer_rsrc_t rsrc;
+  Rsrc rsrc;
   // tap of this lane's chunk for the next K tile to be loaded (FAST)
   mutable int cur_r, cur_s, cur_c;
 
@@ -381,20 +343,18 @@ struct Im2colLoader {
     return reinterpret_cast<const uint16_t*>(x)[(long long)(pix[j] + r * W + s) * C + c];
   }
 
-  // FAST: K tiles must be requested in order 0, 1, 2, ... (the tap advances).
+  // Loading K tile kt takes NPART calls part(tile, kt, j) and then
+  // advance().  FAST: K tiles must be loaded in order 0, 1, 2, ... (advance()
+  // moves this lane's tap on by the 64 channels of one K tile); part j is one
+  // direct-to-LDS load of 8 rows per wave.  Else part 0 does it all.
+  static constexpr int NPART = FAST ? Sh::NQ : 1;
   __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
-    if (FAST) {
-      const bool kin = kt * 64 + Sh::lane_chunk() * 8 < K;
-      const int tap = cur_r * W + cur_s;
 #pragma unroll
-      for (int j = 0; j < Sh::NQ; ++j) {
-        const int h = row_h(j) + cur_r;  // rows past M have h < -16000: never in range
-        const int w = row_w(j) + cur_s;
-        const bool ok = kin && (unsigned)h < (unsigned)H && (unsigned)w < (unsigned)W;
-        const uint32_t off = ((uint32_t)(pix[j] + tap) * (uint32_t)C + (uint32_t)cur_c) * 2u;
-        dma16(rsrc, Sh::dst(tile, j), ok ? off : OOB);
-      }
-      // advance this lane's tap by the 64 channels of one K tile
+    for (int j = 0; j < NPART; ++j) part(tile, kt, j);
+    advance();
+  }
+  __device__ __forceinline__ void advance() const {
+    if (FAST) {
       cur_c += 64;
       while (cur_c >= C) {
         cur_c -= C;
@@ -403,6 +363,17 @@ struct Im2colLoader {
           ++cur_r;
         }
       }
+    }
+  }
+  __device__ __forceinline__ void part(uint8_t* tile, int kt, int j) const {
+    if (FAST) {
+      const bool kin = kt * 64 + Sh::lane_chunk() * 8 < K;
+      const int tap = cur_r * W + cur_s;
+      const int h = row_h(j) + cur_r;  // rows past M have h < -16000: never in range
+      const int w = row_w(j) + cur_s;
+      const bool ok = kin && (unsigned)h < (unsigned)H && (unsigned)w < (unsigned)W;
+      const uint32_t off = ((uint32_t)(pix[j] + tap) * (uint32_t)C + (uint32_t)cur_c) * 2u;
+      dma16(rsrc, Sh::dst(tile, j), ok ? off : OOB);
     } else {
       const int c = threadIdx.x & 7;
       const int k0 = kt * 64 + c * 8;
@@ -423,11 +394,11 @@ struct Im2colLoader {
 // ---------------------------------------------------------------------------
 // MFMA wrappers.  One call = one 32 x 32 output tile, 32 bytes of K per row.
 // ---------------------------------------------------------------------------
-template <int KIND>
+template <int KIND, int MB>
 struct Mfma;
 
 template <>
-struct Mfma<KIND_F16_GEMM> {
+struct Mfma<KIND_F16_GEMM, 32> {
   typedef f32x16 acc_t;
   __device__ __forceinline__ static void run(acc_t& c, uint4 a, uint4 b) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
@@ -435,12 +406,28 @@ struct Mfma<KIND_F16_GEMM> {
   }
 };
 template <>
-struct Mfma<KIND_F16_CONV> : Mfma<KIND_F16_GEMM> {};
+struct Mfma<KIND_F16_GEMM, 16> {
+  typedef f32x4 acc_t;
+  __device__ __forceinline__ static void run(acc_t& c, uint4 a, uint4 b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
+                                               __builtin_bit_cast(half8, b), c, 0, 0, 0);
+  }
+};
+template <int MB>
+struct Mfma<KIND_F16_CONV, MB> : Mfma<KIND_F16_GEMM, MB> {};
 template <>
-struct Mfma<KIND_U8I8_GEMM> {
+struct Mfma<KIND_U8I8_GEMM, 32> {
   typedef i32x16 acc_t;
   __device__ __forceinline__ static void run(acc_t& c, uint4 a, uint4 b) {
     c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                              __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<KIND_U8I8_GEMM, 16> {
+  typedef i32x4 acc_t;
+  __device__ __forceinline__ static void run(acc_t& c, uint4 a, uint4 b) {
+    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a),
                                               __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
   }
 };
@@ -471,57 +458,40 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int EB = (KIND == KIND_U8I8_GEMM) ? 1 : 2;
   constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int MB = IGC_MFMA_DIM;          // MFMA output block: MB x MB
+  constexpr int FM = TM / MB, FN = TN / MB;
+  constexpr int NE = MB * MB / 64;          // accumulator elements per lane
+  constexpr int LPR = 64 / MB;              // lanes sharing one row of a fragment
   constexpr int SA = BM * KT_BYTES, SB = BN * KT_BYTES;  // stage sizes
   constexpr bool INT8 = KIND == KIND_U8I8_GEMM;
-  // Operand roles: one operand streams straight into a 3-stage LDS ring (X),
-  // the other goes through 2 register staging sets into a 2-stage ring (Y).
-  // The u8 A of the integer GEMM takes the register path so that its
-  // u8 -> s8 conversion happens once, on the way into LDS, rather than on
-  // every fragment read.
-  constexpr bool A_IN_X = !INT8;
-  constexpr int SX = A_IN_X ? SA : SB, SY = A_IN_X ? SB : SA;
-  typedef typename std::conditional<
-      KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
-      typename std::conditional<A_IN_X, RowDmaLoader<NT, BM, EB, FAST>,
-                                RowRegLoader<NT, BM, EB, FAST, true>>::type>::type ALoader;
-  typedef typename std::conditional<A_IN_X, RowRegLoader<NT, BN, EB, FAST>,
-                                    RowDmaLoader<NT, BN, EB, FAST>>::type BLoader;
-  typedef typename std::conditional<A_IN_X, BLoader, ALoader>::type YLoader;  // register path
-  constexpr int NCH_Y = YLoader::NCH;
-  // vector-memory instructions per K tile per lane (the X loads count only on
-  // the direct-to-LDS path; element-wise loads are waited for by the compiler
-  // before they are used)
-  constexpr int NLX = FAST ? DmaShape<NT, A_IN_X ? BM : BN>::NQ : 0;
-  constexpr int NVM = NLX + (FAST ? NCH_Y : 0);
+  typedef typename std::conditional<KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
+                                    RowDmaLoader<NT, BM, EB, FAST>>::type ALoader;
+  typedef RowDmaLoader<NT, BN, EB, FAST> BLoader;
+  // direct-to-LDS loads per K tile per wave (counted by vmcnt); the
+  // element-wise path of unaligned operands is waited for as it goes
+  constexpr int NLA = FAST ? ALoader::NPART : 0;
+  constexpr int NLB = FAST ? BLoader::NPART : 0;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(FM <= 4 && BM >= BN, "epilogue staging reuses the stage arrays");
-  static_assert(NVM < 64, "vmcnt range");
-  typedef typename Mfma<KIND>::acc_t acc_t;
+  static_assert(TM <= 128 && BM >= BN && FN <= FM, "epilogue staging reuses the stage arrays");
+  static_assert(NLA + NLB < 64, "vmcnt range");
+  typedef typename Mfma<KIND, MB>::acc_t acc_t;
 
-  // One LDS array per stage: the compiler then knows which stage each
-  // direct-to-LDS load writes and waits for exactly that one.
-  __shared__ __attribute__((aligned(16))) uint8_t sx0[SX];
-  __shared__ __attribute__((aligned(16))) uint8_t sx1[SX];
-  __shared__ __attribute__((aligned(16))) uint8_t sx2[SX];
-  __shared__ __attribute__((aligned(16))) uint8_t sy0[SY];
-  __shared__ __attribute__((aligned(16))) uint8_t sy1[SY];
-  auto stX = [&](auto U) -> uint8_t* {
-    constexpr int u = decltype(U)::value % 3;
-    if constexpr (u == 0) return sx0;
-    if constexpr (u == 1) return sx1;
-    return sx2;
-  };
-  auto stY = [&](auto U) -> uint8_t* {
-    constexpr int u = decltype(U)::value % 2;
-    if constexpr (u == 0) return sy0;
-    return sy1;
-  };
+  // One LDS array per stage: A in 3 stages, B in 2 (160 KiB at 256 x 256).
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[SA];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[SA];
+  __shared__ __attribute__((aligned(16))) uint8_t sa2[SA];
+  __shared__ __attribute__((aligned(16))) uint8_t sb0[SB];
+  __shared__ __attribute__((aligned(16))) uint8_t sb1[SB];
   auto stA = [&](auto U) -> uint8_t* {
-    if constexpr (A_IN_X) return stX(U); else return stY(U);
+    constexpr int u = decltype(U)::value % 3;
+    if constexpr (u == 0) return sa0;
+    if constexpr (u == 1) return sa1;
+    return sa2;
   };
   auto stB = [&](auto U) -> uint8_t* {
-    if constexpr (A_IN_X) return stY(U); else return stX(U);
+    constexpr int u = decltype(U)::value % 2;
+    if constexpr (u == 0) return sb0;
+    return sb1;
   };
 
   int tm, tn;
@@ -547,7 +517,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+      for (int e = 0; e < NE; ++e) acc[i][j][e] = 0;
 
   // Per-lane partial sums of A' rows / B columns (u8 x i8 with zero points).
   int rsum[FM], csum[FN];
@@ -560,110 +530,123 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 
   const int nk = (p.K * EB + KT_BYTES - 1) / KT_BYTES;
 
-  // Fragments, double-buffered in registers: lane l reads row l % 32 of its
-  // 32-row block, 16-byte chunk 2*ks + l/32 (k-step ks covers 32 bytes of K).
-  const int frow = lane & 31;
-  const int fhalf = lane >> 5;
+  // Fragments, double-buffered in registers: lane l reads row l % MB of its
+  // MB-row block, 16-byte chunk LPR * ks + l / MB (a k-step is 16 * LPR bytes
+  // of K: 64 for 16 x 16 blocks, 32 for 32 x 32).
+  const int frow = lane % MB;
+  const int fhalf = lane / MB;
   uint4 fa[2][FM], fb[2][FN];
-  auto read_frags = [&](const uint8_t* As, const uint8_t* Bs, int ks, uint4 (&a)[FM], uint4 (&b)[FN]) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) a[i] = lds_read16(As, swz(wm * TM + i * 32 + frow, ks * 2 + fhalf));
-#pragma unroll
-    for (int j = 0; j < FN; ++j) b[j] = lds_read16(Bs, swz(wn * TN + j * 32 + frow, ks * 2 + fhalf));
+  auto read_a = [&](const uint8_t* As, int ks, int i, uint4& a) {
+    a = lds_read16(As, swz(wm * TM + i * MB + frow, ks * LPR + fhalf));
   };
-  auto mfmas = [&](const uint4 (&a)[FM], const uint4 (&b)[FN]) {
+  auto read_b = [&](const uint8_t* Bs, int ks, int j, uint4& b) {
+    b = lds_read16(Bs, swz(wn * TN + j * MB + frow, ks * LPR + fhalf));
+  };
+  constexpr int KSTEPS = KT_BYTES / (16 * LPR);
+  static_assert(KSTEPS % 2 == 0, "the fragment double buffer returns to set 0 after a tile");
+
+  // One chunk of a k-step: the FN MFMAs of fragment row c, with the reads of
+  // the next k-step's fragments that belong to row c (A fragment c and the
+  // B fragments j with j * FM / FN == c) and the direct-to-LDS loads given by
+  // `issue`.  Program order is the issue order: the first MFMA goes before the
+  // loads so the matrix pipe is busy while they issue, and the compiler may
+  // not move anything across a chunk boundary.  The u8 A operand is turned
+  // into A' = A xor 0x80 (A - 128 as a signed byte) just before use.
+  auto chunk = [&](int c, const uint4 (&a)[FM], const uint4 (&b)[FN], const uint8_t* As_n,
+                   const uint8_t* Bs_n, int ks_n, uint4 (&an)[FM], uint4 (&bn)[FN], auto issue) {
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 ac = a[c];
+    if constexpr (INT8) {
+      ac.x ^= 0x80808080u;
+      ac.y ^= 0x80808080u;
+      ac.z ^= 0x80808080u;
+      ac.w ^= 0x80808080u;
+    }
+    Mfma<KIND, MB>::run(acc[c][0], ac, b[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    issue();
+    __builtin_amdgcn_sched_barrier(0);
+    read_a(As_n, ks_n, c, an[c]);
+    int nrd = 1;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      if (j * FM / FN == c) {
+        read_b(Bs_n, ks_n, j, bn[j]);
+        ++nrd;
+      }
+#pragma unroll
+    for (int j = 1; j < FN; ++j) Mfma<KIND, MB>::run(acc[c][j], ac, b[j]);
     if constexpr (SUMS) {
+      rsum[c] = sum_bytes(ac, rsum[c]);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) rsum[i] = sum_bytes(a[i], rsum[i]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) csum[j] = sum_bytes(b[j], csum[j]);
+      for (int j = 0; j < FN; ++j)
+        if (j * FM / FN == c) csum[j] = sum_bytes(b[j], csum[j]);
     }
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) Mfma<KIND>::run(acc[i][j], a[i], b[j]);
+    for (int q = 1; q < FN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      if (q <= nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
   };
-  constexpr int NMF = FM * FN;  // MFMAs per k-step
-  constexpr int NRD = FM + FN;  // fragment reads per k-step
-  constexpr int KSTEPS = KT_BYTES / 32;
 
-  // The two operand paths: X straight into LDS, Y through registers.
-  auto x_load = [&](uint8_t* st, int kt) {
-    if constexpr (A_IN_X) la.load(st, kt); else lb.load(st, kt);
-  };
-  auto y_load = [&](uint4 (&r)[NCH_Y], int kt) {
-    if constexpr (A_IN_X) lb.load(r, kt); else la.load(r, kt);
-  };
-  auto y_store = [&](uint8_t* st, const uint4 (&r)[NCH_Y]) {
-    if constexpr (A_IN_X) lb.store(st, r); else la.store(st, r);
-  };
-  uint4 ry[2][NCH_Y];  // register staging sets
-
-  // Prologue: tiles 0 and 1 in flight; tile 0 in LDS.
-  x_load(sx0, 0);
-  y_load(ry[0], 0);
-  x_load(sx1, 1);
-  y_load(ry[1], 1);
-  y_store(sy0, ry[0]);
-  wait_vmcnt_lgkm0<NVM>();
+  // Prologue: tiles 0 and 1 in flight, tile 0 landed, its first fragments read.
+  la.load(sa0, 0);
+  lb.load(sb0, 0);
+  la.load(sa1, 1);
+  lb.load(sb1, 1);
+  wait_vmcnt_lgkm0<NLA + NLB>();
   __builtin_amdgcn_s_barrier();
-  read_frags(stA(std::integral_constant<int, 0>()), stB(std::integral_constant<int, 0>()), 0, fa[0], fb[0]);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) read_a(sa0, 0, i, fa[0][i]);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) read_b(sb0, 0, j, fb[0][j]);
 
-  // K tile kt: X operand in stage kt % 3 (the stage of tile kt+2 is the one
-  // tile kt-1 used), Y operand in stage kt % 2, Y of tile kt+2 in staging set
-  // kt % 2.  Region 1: loads of tile kt+2, k-steps 0..KSTEPS-2 of tile kt,
-  // staging set of tile kt+1 -> Y stage (kt+1) % 2.  Then wait until every
-  // load issued before this iteration has landed (X of tile kt+1 included)
-  // and every LDS access of this wave is done, and barrier.  Region 2: the
-  // last k-step's MFMAs run over the reads of the next tile's first
-  // fragments.  The instruction scheduler is asked to spread the memory
-  // instructions between the MFMAs, so the in-order wave never stalls behind
-  // a burst of them.
+  // K tile kt: A in stage kt % 3, B in stage kt % 2.  On entry tiles kt+1 are
+  // in flight.  Region 1: k-steps 0..KSTEPS-2 of tile kt, issuing the loads of
+  // A tile kt+2 into the stage tile kt-1 used.  Then wait until A and B of
+  // tile kt+1 have landed (only A of kt+2 may still be in flight) and every
+  // LDS access of this wave is done, and barrier: every wave is then past
+  // its reads of tile kt.  Region 2: the last k-step of tile kt, issuing the
+  // loads of B tile kt+2 into tile kt's B stage and reading tile kt+1's first
+  // fragments.  [TIR-COMPILER] §2.2/§4.4 pipeline, two tiles deep for A, one
+  // and a half for B.
+  constexpr int NS1 = (KSTEPS - 1) * FM;  // chunks in region 1
   auto tile = [&](int kt, auto U) {
     constexpr int u = decltype(U)::value;
     const uint8_t* As = stA(U);
     const uint8_t* Bs = stB(U);
-    x_load(stX(std::integral_constant<int, u + 2>()), kt + 2);
-    y_load(ry[u % 2], kt + 2);
+    uint8_t* const An = stA(std::integral_constant<int, u + 2>());
+    uint8_t* const Bn = stB(std::integral_constant<int, u + 2>());
     int buf = 0;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS - 1; ++ks) {
-      read_frags(As, Bs, ks + 1, fa[buf ^ 1], fb[buf ^ 1]);
-      mfmas(fa[buf], fb[buf]);
+#pragma unroll
+      for (int c = 0; c < FM; ++c) {
+        const int slot = ks * FM + c;
+        chunk(c, fa[buf], fb[buf], As, Bs, ks + 1, fa[buf ^ 1], fb[buf ^ 1], [&]() {
+#pragma unroll
+          for (int i = 0; i < ALoader::NPART; ++i)
+            if (i * NS1 / ALoader::NPART == slot) la.part(An, kt + 2, i);
+        });
+      }
       buf ^= 1;
     }
-    y_store(stY(std::integral_constant<int, u + 1>()), ry[(u + 1) % 2]);
-    {
-      int rd = 0, vm = 0, wr = 0;
-#pragma unroll
-      for (int m = 0; m < (KSTEPS - 1) * NMF; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        if ((m & 1) == 0 && rd < (KSTEPS - 1) * NRD) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-          ++rd;
-        }
-        if (m % 3 == 0 && vm < NLX + NCH_Y) {
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
-          ++vm;
-        }
-        if (m % 3 == 1 && m >= NMF && wr < NCH_Y) {
-          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
-          ++wr;
-        }
-      }
-    }
-    wait_vmcnt_lgkm0<NVM>();
+    la.advance();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt_lgkm0<NLA>();
     __builtin_amdgcn_s_barrier();
-    read_frags(stA(std::integral_constant<int, u + 1>()), stB(std::integral_constant<int, u + 1>()), 0,
-               fa[buf ^ 1], fb[buf ^ 1]);
-    mfmas(fa[buf], fb[buf]);
+    const uint8_t* As1 = stA(std::integral_constant<int, u + 1>());
+    const uint8_t* Bs1 = stB(std::integral_constant<int, u + 1>());
 #pragma unroll
-    for (int q = 0; q < NMF; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int c = 0; c < FM; ++c) {
+      chunk(c, fa[buf], fb[buf], As1, Bs1, 0, fa[buf ^ 1], fb[buf ^ 1], [&]() {
+#pragma unroll
+        for (int i = 0; i < BLoader::NPART; ++i)
+          if (i * FM / BLoader::NPART == c) lb.part(Bn, kt + 2, i);
+      });
     }
+    lb.advance();
   };
-  static_assert(KSTEPS % 2 == 0, "the fragment double buffer returns to set 0 after a tile");
   for (int kt = 0; kt < nk; kt += 6) {
     tile(kt, std::integral_constant<int, 0>());
     if (kt + 1 < nk) tile(kt + 1, std::integral_constant<int, 1>());
@@ -686,41 +669,51 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // quantization run element-wise on them, and results leave in 16-byte
   // (fp32/int32) or 4-byte (int8) stores.
   //
-  // Accumulator layout of a 32x32 MFMA tile: lane l holds column l % 32 and,
-  // in register e, row 8*(e/4) + 4*(l/32) + e%4.
-  const int ccol = lane & 31;
-  const int rbase = 4 * (lane >> 5);
-  // Staging arrays for 32-row blocks: the three X stages and the first Y
+  // Accumulator layout of an MFMA output block: lane l holds column l % MB
+  // and, in register e, row 4*(l/16) + e of a 16 x 16 block, or row
+  // 8*(e/4) + 4*(l/32) + e%4 of a 32 x 32 block.
+  const int ccol = lane % MB;
+  auto acc_row = [&](int e) { return MB == 16 ? 4 * (lane >> 4) + e : 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); };
+  // Staging arrays for 32-row blocks: the three A stages and the first B
   // stage (each holds 32 x BN x 4 bytes since BN <= BM); the zero-point sums
-  // go to the second Y stage.
+  // go to the second B stage.
   auto stage_rt = [&](int u) -> uint8_t* {  // u is a constant after unrolling
-    return u == 0 ? sx0 : u == 1 ? sx1 : u == 2 ? sx2 : sy0;
+    return u == 0 ? sa0 : u == 1 ? sa1 : u == 2 ? sa2 : sb0;
   };
   static_assert(32 * BN * 4 <= SB && (BM + BN) * 4 <= SB, "staging and sums fit in the stages");
-  int* const sums = reinterpret_cast<int*>(sy1);
-  auto stage_off = [](int rl, int c) {  // rl: row within a 32-row array; c: column
-    return rl * (BN * 4) + (((c >> 2) ^ (8 * ((rl >> 2) & 1))) << 4) + (c & 3) * 4;
+  int* const sums = reinterpret_cast<int*>(sb1);
+  // rl: row within a 32-row array; c: column.  The 16-byte chunk index is
+  // XOR-ed with a function of the row so that the row groups written by one
+  // staging store (2 of 32 columns, or 4 of 16) land on disjoint banks.
+  auto stage_off = [](int rl, int c) {
+    const int x = MB == 16 ? 4 * ((rl >> 2) & 3) : 8 * ((rl >> 2) & 1);
+    return rl * (BN * 4) + (((c >> 2) ^ x) << 4) + (c & 3) * 4;
   };
 
   uint32_t kzz = 0;
   if constexpr (SUMS) {
-    // Complete the row / column sums (the two K halves live in lanes l, l^32)
-    // and publish them through LDS.
+    // Complete the row / column sums (the K parts of one row live in lanes
+    // l, l + MB, ...) and publish them through LDS.
+    auto lane_total = [&](int v) {
+      v += __shfl_xor(v, 32);
+      if constexpr (MB == 16) v += __shfl_xor(v, 16);
+      return v;
+    };
     if (want_rsum) {
       // K-tail padding loads as byte 0 and is stored as A' = -128: add those
       // terms back.
       const int pad_fix = 128 * (nk * KT_BYTES - p.K);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int t = rsum[i] + __shfl_xor(rsum[i], 32) + pad_fix;
-        if (lane < 32) sums[wm * TM + i * 32 + lane] = t;
+        const int t = lane_total(rsum[i]) + pad_fix;
+        if (lane < MB) sums[wm * TM + i * MB + lane] = t;
       }
     }
     if (want_csum) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int t = csum[j] + __shfl_xor(csum[j], 32);
-        if (lane < 32) sums[BM + wn * TN + j * 32 + lane] = t;
+        const int t = lane_total(csum[j]);
+        if (lane < MB) sums[BM + wn * TN + j * MB + lane] = t;
       }
     }
   }
@@ -738,15 +731,15 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     if (wm == h) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        uint8_t* arr = stage_rt(i);
+        uint8_t* arr = stage_rt((i * MB) / 32);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
+          for (int e = 0; e < NE; ++e) {
             // copy the element out first: bit-casting a vector-element lvalue
             // directly reads element 0 with this compiler
             const auto val = acc[i][j][e];
-            const int off = stage_off(8 * (e >> 2) + rbase + (e & 3), wn * TN + j * 32 + ccol);
+            const int off = stage_off((i * MB) % 32 + acc_row(e), wn * TN + j * MB + ccol);
             *reinterpret_cast<int32_t*>(arr + off) = __builtin_bit_cast(int32_t, val);
           }
       }
