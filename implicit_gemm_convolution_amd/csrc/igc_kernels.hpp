@@ -176,6 +176,13 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 #ifndef IGC_DMA_ASM
 #define IGC_DMA_ASM 1
 #endif
+// Direct-to-LDS load at byte offset off + soff (both range-checked against
+// the descriptor's size: past it, the lanes read zeros).
+__device__ __forceinline__ void dma16s(const Rsrc& r, uint8_t* lds, uint32_t off, uint32_t soff) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0)
+               : "memory");
+}
 __device__ __forceinline__ void dma16(const Rsrc& r, uint8_t* lds, uint32_t off) {
   if constexpr (IGC_DMA_ASM) {
     const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
@@ -215,7 +222,14 @@ struct DmaShape {
 // u8 x i8 GEMM): rows of K.
 //  FAST: 16-byte aligned rows, K a multiple of the chunk: direct-to-LDS loads.
 //  else: element-wise loads, written to LDS with the same layout.
-template <int NT, int ROWS, int EB, bool FAST>
+//  TAIL_FIRST (FAST only): the partial K tile, if any, is tile 0 -- it holds
+//  bytes [0, t) of each row, t = K*EB - 128*(nk-1) -- and tile kt >= 1 holds
+//  bytes [t + 128*(kt-1), t + 128*kt).  Only tile 0 then needs a per-lane K
+//  bound; every later load is one scalar offset away from this lane's fixed
+//  offset, with no vector arithmetic.  Otherwise tile kt holds bytes
+//  [128*kt, 128*kt + 128) and the K tail is masked in the last tile.  The
+//  two operands of a kernel must use the same order.
+template <int NT, int ROWS, int EB, bool FAST, bool TAIL_FIRST = false>
 struct RowDmaLoader {
   typedef DmaShape<NT, ROWS> Sh;
   const uint8_t* base;  // row 0 of this tile
@@ -224,7 +238,9 @@ struct RowDmaLoader {
   int K;
   Rsrc rsrc;
   uint32_t lane_off;    // byte offset of this lane's first row and chunk
+  uint32_t lane_off0;   // same, or OOB past the K bound of tile 0 (TAIL_FIRST)
   uint32_t row_step;    // bytes between this lane's rows (uniform)
+  int kpad;             // 128 * nk - K * EB: zero bytes in the partial tile
 
   __device__ __forceinline__ void init(const uint8_t* ptr, long long ld, int r0, int nrows, int k) {
     ld_bytes = ld * EB;
@@ -236,6 +252,9 @@ struct RowDmaLoader {
       rsrc = make_rsrc(base, (uint32_t)extent);
       lane_off = (uint32_t)(Sh::lane_row() * ld_bytes) + (uint32_t)(Sh::lane_chunk() * CHUNK_BYTES);
       row_step = (uint32_t)(8 * Sh::NWAVES * ld_bytes);
+      const int nk = (K * EB + KT_BYTES - 1) / KT_BYTES;
+      kpad = nk * KT_BYTES - K * EB;
+      lane_off0 = Sh::lane_chunk() * CHUNK_BYTES < KT_BYTES - kpad ? lane_off : OOB;
     }
   }
 
@@ -243,14 +262,25 @@ struct RowDmaLoader {
   // calls part(tile, kt, i), i = 0..NPART-1, then advance(); rows past the
   // operand and k past K read as zero bytes.  FAST: part i is one
   // direct-to-LDS load of 8 rows per wave; else part 0 does it all.
+  // TAIL_FIRST: part() serves tiles kt >= 1 and part0() tile 0.
   static constexpr int NPART = FAST ? Sh::NQ : 1;
   __device__ __forceinline__ void advance() const {}
   __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
 #pragma unroll
-    for (int i = 0; i < NPART; ++i) part(tile, kt, i);
+    for (int i = 0; i < NPART; ++i) {
+      if (TAIL_FIRST && kt == 0)
+        part0(tile, i);
+      else
+        part(tile, kt, i);
+    }
+  }
+  __device__ __forceinline__ void part0(uint8_t* tile, int i) const {
+    dma16s(rsrc, Sh::dst(tile, i), lane_off0, (uint32_t)(i * row_step));
   }
   __device__ __forceinline__ void part(uint8_t* tile, int kt, int i) const {
-    if (FAST) {
+    if (FAST && TAIL_FIRST) {
+      dma16s(rsrc, Sh::dst(tile, i), lane_off, (uint32_t)(kt * KT_BYTES - kpad) + (uint32_t)(i * row_step));
+    } else if (FAST) {
       const bool kin = kt * KT_BYTES + Sh::lane_chunk() * CHUNK_BYTES < K * EB;
       dma16(rsrc, Sh::dst(tile, i), kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
     } else {
@@ -464,9 +494,11 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int LPR = 64 / MB;              // lanes sharing one row of a fragment
   constexpr int SA = BM * KT_BYTES, SB = BN * KT_BYTES;  // stage sizes
   constexpr bool INT8 = KIND == KIND_U8I8_GEMM;
+  // (the im2col operand walks K in order, so the conv's B does too)
+  constexpr bool TAIL_FIRST = FAST && KIND != KIND_F16_CONV;
   typedef typename std::conditional<KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
-                                    RowDmaLoader<NT, BM, EB, FAST>>::type ALoader;
-  typedef RowDmaLoader<NT, BN, EB, FAST> BLoader;
+                                    RowDmaLoader<NT, BM, EB, FAST, TAIL_FIRST>>::type ALoader;
+  typedef RowDmaLoader<NT, BN, EB, FAST, TAIL_FIRST> BLoader;
   // direct-to-LDS loads per K tile per wave (counted by vmcnt); the
   // element-wise path of unaligned operands is waited for as it goes
   constexpr int NLA = FAST ? ALoader::NPART : 0;

@@ -67,7 +67,7 @@ def test_fast_kernels_load_straight_into_lds_and_stream_outputs(asm):
         kind, bm, bn, fast = _params(name)
         if not fast:
             continue
-        assert re.search(r"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], 0 offen lds", body), name
+        assert re.search(r"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], (0|s\d+) offen lds", body), name
         assert re.search(r"global_store_dword(x4)? .* nt", body), name
 
 
