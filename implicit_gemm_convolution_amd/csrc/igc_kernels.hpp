@@ -577,35 +577,43 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int KSTEPS = KT_BYTES / (16 * LPR);
   static_assert(KSTEPS % 2 == 0, "the fragment double buffer returns to set 0 after a tile");
 
-  // One chunk of a k-step: the FN MFMAs of fragment row c, with the reads of
-  // the next k-step's fragments that belong to row c (A fragment c and the
-  // B fragments j with j * FM / FN == c) and the direct-to-LDS loads given by
-  // `issue`.  Program order is the issue order: the first MFMA goes before the
+  // One chunk of a k-step: the FN MFMAs of fragment row c, with its share of
+  // the reads of the next k-step's fragments and the direct-to-LDS loads given
+  // by `issue`.  Program order is the issue order: the first MFMA goes before the
   // loads so the matrix pipe is busy while they issue, and the compiler may
-  // not move anything across a chunk boundary.  The u8 A operand is turned
-  // into A' = A xor 0x80 (A - 128 as a signed byte) just before use.
+  // not move anything across a chunk boundary.  The u8 A operand becomes
+  // A' = A xor 0x80 (A - 128 as a signed byte) one chunk ahead of use: `ax`
+  // carries row c's converted fragment in, and `a_up` (the next chunk's raw
+  // fragment) is converted between this chunk's MFMAs.
+  uint4 ax = make_uint4(0, 0, 0, 0);
   auto chunk = [&](int c, const uint4 (&a)[FM], const uint4 (&b)[FN], const uint8_t* As_n,
-                   const uint8_t* Bs_n, int ks_n, uint4 (&an)[FM], uint4 (&bn)[FN], auto issue) {
+                   const uint8_t* Bs_n, int ks_n, uint4 (&an)[FM], uint4 (&bn)[FN], const uint4& a_up,
+                   auto issue) {
     __builtin_amdgcn_sched_barrier(0);
-    uint4 ac = a[c];
-    if constexpr (INT8) {
-      ac.x ^= 0x80808080u;
-      ac.y ^= 0x80808080u;
-      ac.z ^= 0x80808080u;
-      ac.w ^= 0x80808080u;
-    }
+    const uint4 ac = INT8 ? ax : a[c];
     Mfma<KIND, MB>::run(acc[c][0], ac, b[0]);
     __builtin_amdgcn_sched_barrier(0);
     issue();
     __builtin_amdgcn_sched_barrier(0);
-    read_a(As_n, ks_n, c, an[c]);
-    int nrd = 1;
+    // next k-step's fragments: all B first (the next k-step's first chunk
+    // uses every one of them), then A in row order
+    int nrd = 0;
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      if (j * FM / FN == c) {
-        read_b(Bs_n, ks_n, j, bn[j]);
+    for (int r = 0; r < FN + FM; ++r)
+      if (r * FM / (FN + FM) == c) {
+        if (r < FN)
+          read_b(Bs_n, ks_n, r, bn[r]);
+        else
+          read_a(As_n, ks_n, r - FN, an[r - FN]);
         ++nrd;
       }
+    uint4 axn = a_up;
+    if constexpr (INT8) {
+      axn.x ^= 0x80808080u;
+      axn.y ^= 0x80808080u;
+      axn.z ^= 0x80808080u;
+      axn.w ^= 0x80808080u;
+    }
 #pragma unroll
     for (int j = 1; j < FN; ++j) Mfma<KIND, MB>::run(acc[c][j], ac, b[j]);
     if constexpr (SUMS) {
@@ -614,11 +622,22 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       for (int j = 0; j < FN; ++j)
         if (j * FM / FN == c) csum[j] = sum_bytes(b[j], csum[j]);
     }
+    // between the MFMAs: the reads first, then the vector ALU work
+    constexpr int NV = (INT8 ? 4 : 0) + (SUMS ? 8 : 0);
+    int nv = 0;
 #pragma unroll
     for (int q = 1; q < FN; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      if (q <= nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      if (q <= nrd) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      } else if (nv < NV) {
+        const int k = (NV - nv + (FN - 1 - q)) / (FN - q);  // spread evenly
+#pragma unroll
+        for (int t = 0; t < k; ++t) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // vector ALU
+        nv += k;
+      }
     }
+    if constexpr (INT8) ax = axn;
   };
 
   // Prologue: tiles 0 and 1 in flight, tile 0 landed, its first fragments read.
@@ -632,6 +651,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   for (int i = 0; i < FM; ++i) read_a(sa0, 0, i, fa[0][i]);
 #pragma unroll
   for (int j = 0; j < FN; ++j) read_b(sb0, 0, j, fb[0][j]);
+  if constexpr (INT8) {
+    ax = fa[0][0];
+    ax.x ^= 0x80808080u;
+    ax.y ^= 0x80808080u;
+    ax.z ^= 0x80808080u;
+    ax.w ^= 0x80808080u;
+  }
 
   // K tile kt: A in stage kt % 3, B in stage kt % 2.  On entry tiles kt+1 are
   // in flight.  Region 1: k-steps 0..KSTEPS-2 of tile kt, issuing the loads of
@@ -655,7 +681,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 #pragma unroll
       for (int c = 0; c < FM; ++c) {
         const int slot = ks * FM + c;
-        chunk(c, fa[buf], fb[buf], As, Bs, ks + 1, fa[buf ^ 1], fb[buf ^ 1], [&]() {
+        chunk(c, fa[buf], fb[buf], As, Bs, ks + 1, fa[buf ^ 1], fb[buf ^ 1],
+              c + 1 < FM ? fa[buf][c + 1 < FM ? c + 1 : 0] : fa[buf ^ 1][0], [&]() {
 #pragma unroll
           for (int i = 0; i < ALoader::NPART; ++i)
             if (i * NS1 / ALoader::NPART == slot) la.part(An, kt + 2, i);
@@ -671,7 +698,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     const uint8_t* Bs1 = stB(std::integral_constant<int, u + 1>());
 #pragma unroll
     for (int c = 0; c < FM; ++c) {
-      chunk(c, fa[buf], fb[buf], As1, Bs1, 0, fa[buf ^ 1], fb[buf ^ 1], [&]() {
+      chunk(c, fa[buf], fb[buf], As1, Bs1, 0, fa[buf ^ 1], fb[buf ^ 1],
+            c + 1 < FM ? fa[buf][c + 1 < FM ? c + 1 : 0] : fa[buf ^ 1][0], [&]() {
 #pragma unroll
         for (int i = 0; i < BLoader::NPART; ++i)
           if (i * FM / BLoader::NPART == c) lb.part(Bn, kt + 2, i);
