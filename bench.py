@@ -141,8 +141,17 @@ class Runner:
         """Time `steps` back-to-back launches on the current stream between two
         HIP events: the average launch duration is the elapsed time / steps
         (no event commands between the launches, as a caller would run them)."""
-        for _ in range(warmup):
-            self.call()
+        if warmup is None:
+            # until 0.25 s of work has run (at least 10 launches)
+            warmup, t0 = 0, time.perf_counter()
+            while warmup < 10 or time.perf_counter() - t0 < 0.25:
+                for _ in range(10):
+                    self.call()
+                warmup += 10
+                torch.cuda.synchronize()
+        else:
+            for _ in range(warmup):
+                self.call()
         torch.cuda.synchronize()
         t_all0 = torch.cuda.Event(enable_timing=True)
         t_all1 = torch.cuda.Event(enable_timing=True)
@@ -232,7 +241,9 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed launches first (default: as many as take 0.25 s, since the GPU's "
+                         "clock reaches its steady state only after ~20 ms of sustained load)")
     ap.add_argument("--workload", default="c3", choices=synth.WORKLOADS)
     ap.add_argument("--only", action="store_true", help="measure the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -299,7 +310,7 @@ def main(argv=None) -> int:
         "unit": head["unit"],
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": head["warmup"],
         "ms_per_step": round(head["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",

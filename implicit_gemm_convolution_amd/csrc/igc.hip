@@ -3,8 +3,12 @@
 // stream.  All arithmetic happens in the kernels of igc_kernels.hpp.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -54,6 +58,65 @@ int check_device(int* dev_out) {
   return IGC_OK;
 }
 
+// Per-device compute-unit count (0 = not read yet).
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus(int dev) {
+  int n = g_cus[dev].load(std::memory_order_acquire);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    g_cus[dev].store(n, std::memory_order_release);
+  }
+  return n;
+}
+
+// Stream-K workspace, one per (device, stream) so that launches on different
+// streams never share it: partial tiles and per-tile arrival counters (zeroed
+// once when allocated; the kernel leaves them at zero).  It grows on demand
+// and is kept until the process ends.
+struct SkWorkspace {
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  int* cnt = nullptr;
+  size_t cnt_n = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, SkWorkspace> g_ws;
+
+int sk_workspace(int dev, hipStream_t stream, size_t ws_bytes, size_t cnt_n, float** ws, int** cnt) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  SkWorkspace& w = g_ws[std::make_pair(dev, stream)];
+  if (w.ws_bytes < ws_bytes || w.cnt_n < cnt_n) {
+    if (w.ws || w.cnt) {
+      // earlier launches on this stream may still use the old buffers
+      if (hipStreamSynchronize(stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(IGC_EHIP, "hipStreamSynchronize failed before growing the stream-K workspace");
+      }
+      (void)hipFree(w.ws);
+      (void)hipFree(w.cnt);
+      w = SkWorkspace();
+    }
+    const size_t nb = std::max(ws_bytes, w.ws_bytes), nc = std::max(cnt_n, w.cnt_n);
+    if (hipMalloc(&w.ws, nb) != hipSuccess || hipMalloc(reinterpret_cast<void**>(&w.cnt), nc * sizeof(int)) != hipSuccess ||
+        hipMemsetAsync(w.cnt, 0, nc * sizeof(int), stream) != hipSuccess) {
+      (void)hipGetLastError();
+      if (w.ws) (void)hipFree(w.ws);
+      if (w.cnt) (void)hipFree(w.cnt);
+      w = SkWorkspace();
+      return fail(IGC_EHIP, "cannot allocate the stream-K workspace (%zu bytes)", nb);
+    }
+    w.ws_bytes = nb;
+    w.cnt_n = nc;
+  }
+  *ws = static_cast<float*>(w.ws);
+  *cnt = w.cnt;
+  return IGC_OK;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Tile variants.  The large tile keeps the most MFMA work per LDS byte; the
@@ -78,12 +141,57 @@ int choose_variant(int M, int N) {
   return V_64x64;
 }
 
+// Stream-K (shared tiles): when the 256x256 tiles do not fill the last
+// round of compute units, the whole rounds run as whole tiles and the rest
+// of the tiles' K-tile iterations are split evenly over up to one workgroup
+// per compute unit (at least 4 iterations each).  fp16 GEMM and conv only.
+// It pays only when the idle part of the last round is worth more than the
+// cost of publishing and summing the partial tiles, measured on MI355X at
+// about 26 K-tile iterations (4096^2 conv tiles: 392 tiles on 256 CUs, 36
+// iterations each, ran 12% slower split).  IGC_STREAMK=0 never splits,
+// IGC_STREAMK=2 splits whenever the last round is partial (tests).
+int streamk_mode() {
+  const char* s = std::getenv("IGC_STREAMK");
+  if (s && s[0] == '0') return 0;
+  if (s && s[0] == '2') return 2;
+  return 1;
+}
+constexpr long long kStreamKFixupIters = 26;
+
 template <int KIND, int BM, int BN, int WM, int WN, bool FAST, bool SUMS>
 int launch_one(igc::Params p, hipStream_t stream) {
   p.tiles_m = (int)ceil_div(p.M, BM);
   p.tiles_n = (int)ceil_div(p.N, BN);
   long long grid = (long long)p.tiles_m * p.tiles_n;
   if (grid > 0x7fffffffLL) return fail(IGC_EUNSUPPORTED, "too many tiles (%lld)", grid);
+  p.dp_tiles = (int)grid;
+  p.sk_wgs = 0;
+  p.sk_iters = 0;
+  if constexpr (BM == 256 && BN == 256 && FAST && !SUMS && KIND != igc::KIND_U8I8_GEMM) {
+    int dev = 0;
+    const int mode = streamk_mode();
+    if (mode && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
+      const long long cus = device_cus(dev);
+      const long long nk = ceil_div((long long)p.K * 2, igc::KT_BYTES);
+      // iterations the last round leaves idle, per compute unit
+      const long long idle = (cus - grid % cus) * nk / cus;
+      if (grid > cus && grid % cus != 0 && nk >= 4 && (mode == 2 || idle > kStreamKFixupIters)) {
+        const long long dp = grid / cus * cus;
+        const long long iters = (grid - dp) * nk;
+        const long long wgs = std::min(cus, std::max(1LL, iters / 4));
+        float* ws = nullptr;
+        int* cnt = nullptr;
+        if (int st = sk_workspace(dev, stream, (size_t)(2 * wgs * BM * BN * 4), (size_t)(grid - dp), &ws, &cnt))
+          return st;
+        p.dp_tiles = (int)dp;
+        p.sk_wgs = (int)wgs;
+        p.sk_iters = iters;
+        p.ws = ws;
+        p.cnt = cnt;
+        grid = dp + wgs;
+      }
+    }
+  }
   hipLaunchKernelGGL((igc::gemm_kernel<KIND, BM, BN, WM, WN, FAST, SUMS>), dim3((unsigned)grid),
                      dim3(64 * WM * WN), 0, stream, p);
   hipError_t e = hipGetLastError();

@@ -97,27 +97,48 @@ struct Params {
   const float* bias;
   // 16-byte (int8: 4-byte) vector stores allowed for each output
   int vec_c, vec_d, vec_q;
+  // Work split.  Workgroups [0, dp_tiles) each compute one whole tile.  The
+  // remaining tiles_m*tiles_n - dp_tiles tiles are shared by sk_wgs
+  // workgroups as one range of sk_iters K-tile iterations (stream-K):
+  // workgroup dp_tiles + g runs iterations [sk_start(g), sk_start(g+1)).  A
+  // tile split between workgroups is summed through ws (two partial-tile
+  // slots per stream-K workgroup) by whichever contributor finishes last, as
+  // counted in cnt (one counter per stream-K tile, zero between launches).
+  int dp_tiles;
+  int sk_wgs;
+  long long sk_iters;
+  float* ws;
+  int* cnt;
 };
+
+__device__ __forceinline__ long long sk_start(const Params& p, int g) {
+  return (long long)g * p.sk_iters / p.sk_wgs;
+}
+// the stream-K workgroup whose range holds iteration x
+__device__ __forceinline__ int sk_owner(const Params& p, long long x) {
+  return (int)(((x + 1) * p.sk_wgs - 1) / p.sk_iters);
+}
 
 // ---------------------------------------------------------------------------
 // Tile scheduling.  The dispatcher hands workgroups to the 8 XCDs round-robin
-// (workgroup b runs on XCD b % 8).  When the tile count divides by 8, logical
-// tile ids are regrouped so that each XCD owns a contiguous run of them, and
-// the run is laid out in groups of GROUP_M tile-rows, so the workgroups that
-// share an XCD's L2 also share A and B panels.
+// (workgroup b runs on XCD b % 8).  When the whole-tile count divides by 8,
+// logical tile ids are regrouped so that each XCD owns a contiguous run of
+// them, and logical tiles are laid out in groups of GROUP_M tile-rows, so the
+// workgroups that share an XCD's L2 also share A and B panels.
 // ---------------------------------------------------------------------------
 template <int GROUP_M>
-__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
-  const int total = p.tiles_m * p.tiles_n;
-  int bid = blockIdx.x;
-  if ((total & 7) == 0) bid = (bid & 7) * (total >> 3) + (bid >> 3);
+__device__ __forceinline__ void tile_coords(const Params& p, int t, int& tm, int& tn) {
   const int per_group = GROUP_M * p.tiles_n;
-  const int group = bid / per_group;
+  const int group = t / per_group;
   const int first_m = group * GROUP_M;
   const int gsize = min(p.tiles_m - first_m, GROUP_M);
-  const int in_group = bid - group * per_group;
+  const int in_group = t - group * per_group;
   tm = first_m + in_group % gsize;
   tn = in_group / gsize;
+}
+// logical tile of whole-tile workgroup b
+__device__ __forceinline__ int dp_tile(const Params& p, int b) {
+  return (p.dp_tiles & 7) == 0 ? (b & 7) * (p.dp_tiles >> 3) + (b >> 3) : b;
 }
 
 // LDS has 64 banks of 4 bytes and serves a 16-byte-per-lane access 16 lanes
@@ -151,6 +172,11 @@ __device__ __forceinline__ void store4_nt(void* dst, uint32_t v) {
 // Buffer descriptors and direct-to-LDS loads.
 // ---------------------------------------------------------------------------
 constexpr uint32_t OOB = 0x80000000u;  // descriptors are limited to < 2^31 bytes
+// Cache policy of a buffer access coherent across the XCDs of the device
+// (each XCD has its own L2): device ("agent") scope, sc1.  Stream-K partial
+// tiles are written and read this way, so they need no cache-wide
+// write-back or invalidation.
+constexpr int CPOL_DEV = 16;
 
 // A buffer descriptor, both as the compiler's resource type (for the
 // compiler-visible loads) and as the four raw words (for the inline-assembly
@@ -171,22 +197,26 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 // neither reorders it (program order is the schedule) nor inserts its own,
 // conservative vmcnt waits before later LDS reads (it cannot tell the stage
 // arrays apart across the loop's back edge).  Every wait for these loads is
-// explicit in the kernel.  One wait state separates the M0 write from the
-// load.  IGC_DMA_ASM=0 selects the compiler builtin instead.
+// explicit in the kernel, and so are the wait states before the load (see
+// dma16s).  IGC_DMA_ASM=0 selects the compiler builtin instead.
 #ifndef IGC_DMA_ASM
 #define IGC_DMA_ASM 1
 #endif
 // Direct-to-LDS load at byte offset off + soff (both range-checked against
 // the descriptor's size: past it, the lanes read zeros).
+// Five wait states: the compiler may produce the scalar operands (offset,
+// descriptor, M0) with vector instructions (v_readfirstlane, or v_readlane
+// when it spills scalar registers), and a vector memory instruction may only
+// read an SGPR written by a VALU instruction five wait states later.
 __device__ __forceinline__ void dma16s(const Rsrc& r, uint8_t* lds, uint32_t off, uint32_t soff) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0)
+  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0)
                : "memory");
 }
 __device__ __forceinline__ void dma16(const Rsrc& r, uint8_t* lds, uint32_t off) {
   if constexpr (IGC_DMA_ASM) {
     const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(r.d), "{m0}"(m0) : "memory");
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(r.d), "{m0}"(m0) : "memory");
   } else {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r.r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
@@ -225,8 +255,9 @@ struct DmaShape {
 //  TAIL_FIRST (FAST only): the partial K tile, if any, is tile 0 -- it holds
 //  bytes [0, t) of each row, t = K*EB - 128*(nk-1) -- and tile kt >= 1 holds
 //  bytes [t + 128*(kt-1), t + 128*kt).  Only tile 0 then needs a per-lane K
-//  bound; every later load is one scalar offset away from this lane's fixed
-//  offset, with no vector arithmetic.  Otherwise tile kt holds bytes
+//  bound; every later load is one scalar offset (the K position) away from
+//  one of this lane's fixed offsets (one per row group), with no vector
+//  arithmetic.  Otherwise tile kt holds bytes
 //  [128*kt, 128*kt + 128) and the K tail is masked in the last tile.  The
 //  two operands of a kernel must use the same order.
 template <int NT, int ROWS, int EB, bool FAST, bool TAIL_FIRST = false>
@@ -241,6 +272,7 @@ struct RowDmaLoader {
   uint32_t lane_off0;   // same, or OOB past the K bound of tile 0 (TAIL_FIRST)
   uint32_t row_step;    // bytes between this lane's rows (uniform)
   int kpad;             // 128 * nk - K * EB: zero bytes in the partial tile
+  uint32_t voff[TAIL_FIRST ? Sh::NQ : 1];  // lane_off + i * row_step (TAIL_FIRST)
 
   __device__ __forceinline__ void init(const uint8_t* ptr, long long ld, int r0, int nrows, int k) {
     ld_bytes = ld * EB;
@@ -252,9 +284,13 @@ struct RowDmaLoader {
       rsrc = make_rsrc(base, (uint32_t)extent);
       lane_off = (uint32_t)(Sh::lane_row() * ld_bytes) + (uint32_t)(Sh::lane_chunk() * CHUNK_BYTES);
       row_step = (uint32_t)(8 * Sh::NWAVES * ld_bytes);
-      const int nk = (K * EB + KT_BYTES - 1) / KT_BYTES;
+      const int nk = max(1, (K * EB + KT_BYTES - 1) / KT_BYTES);
       kpad = nk * KT_BYTES - K * EB;
       lane_off0 = Sh::lane_chunk() * CHUNK_BYTES < KT_BYTES - kpad ? lane_off : OOB;
+      if constexpr (TAIL_FIRST) {
+#pragma unroll
+        for (int i = 0; i < Sh::NQ; ++i) voff[i] = lane_off + (uint32_t)(i * row_step);
+      }
     }
   }
 
@@ -278,8 +314,8 @@ struct RowDmaLoader {
     dma16s(rsrc, Sh::dst(tile, i), lane_off0, (uint32_t)(i * row_step));
   }
   __device__ __forceinline__ void part(uint8_t* tile, int kt, int i) const {
-    if (FAST && TAIL_FIRST) {
-      dma16s(rsrc, Sh::dst(tile, i), lane_off, (uint32_t)(kt * KT_BYTES - kpad) + (uint32_t)(i * row_step));
+    if constexpr (FAST && TAIL_FIRST) {
+      dma16s(rsrc, Sh::dst(tile, i), voff[i], (uint32_t)(kt * KT_BYTES - kpad));
     } else if (FAST) {
       const bool kin = kt * KT_BYTES + Sh::lane_chunk() * CHUNK_BYTES < K * EB;
       dma16(rsrc, Sh::dst(tile, i), kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
@@ -330,7 +366,7 @@ struct Im2colLoader {
   __device__ __forceinline__ int row_h(int j) const { return hw[j] >> 16; }
   __device__ __forceinline__ int row_w(int j) const { return (int)(int16_t)(hw[j] & 0xffff); }
 
-  __device__ __forceinline__ void init(const Params& p, int m0) {
+  __device__ __forceinline__ void init(const Params& p, int m0, int kt0) {
     x = p.A;
     H = p.H; W = p.W; C = p.C; S = p.S; K = p.K;
     if (FAST) rsrc = make_rsrc(x, (uint32_t)((long long)p.Nb * H * W * C * 2));
@@ -353,8 +389,8 @@ struct Im2colLoader {
         hw[j] = INT32_MIN;
       }
     }
-    // tap of k = chunk*8 (K tile 0)
-    const int k0 = FAST ? Sh::lane_chunk() * 8 : 0;
+    // tap of k = chunk*8 of K tile kt0
+    const int k0 = FAST ? kt0 * 64 + Sh::lane_chunk() * 8 : 0;
     const int rs = k0 / C;
     cur_c = k0 - rs * C;
     cur_r = rs / S;
@@ -475,7 +511,20 @@ __device__ __forceinline__ int sum_bytes(uint4 v, int acc) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_lgkm0() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  // The waitcnt and barrier builtins do not order memory accesses for the
+  // compiler (they are "no memory" intrinsics): empty asm statements with a
+  // memory clobber keep LDS reads and writes on their side of them.
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier without a memory fence (a fence would wait for every
+// direct-to-LDS load in flight); pair it with wait_vmcnt_lgkm0.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -494,6 +543,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int LPR = 64 / MB;              // lanes sharing one row of a fragment
   constexpr int SA = BM * KT_BYTES, SB = BN * KT_BYTES;  // stage sizes
   constexpr bool INT8 = KIND == KIND_U8I8_GEMM;
+  // stream-K (shared tiles) is compiled for the fp16 kinds; the integer GEMM
+  // always gets whole tiles (the host sets dp_tiles accordingly)
+  constexpr bool SK = !INT8 && !SUMS;
   // (the im2col operand walks K in order, so the conv's B does too)
   constexpr bool TAIL_FIRST = FAST && KIND != KIND_F16_CONV;
   typedef typename std::conditional<KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
@@ -526,17 +578,46 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     return sb1;
   };
 
-  int tm, tn;
-  tile_coords<8>(p, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int tid = threadIdx.x;
+  // (K = 0 still runs one all-zero K tile, so the outputs are written)
+  const int nk = max(1, (p.K * EB + KT_BYTES - 1) / KT_BYTES);
+
+  // This workgroup's K-tile iterations: one whole tile, or a stream-K range
+  // that may start and end inside tiles.  It is walked in segments of one
+  // tile each.
+  long long it, it_end;
+  if ((int)blockIdx.x < p.dp_tiles) {
+    it = (long long)dp_tile(p, blockIdx.x) * nk;
+    it_end = it + nk;
+  } else {
+    const int g = blockIdx.x - p.dp_tiles;
+    const long long base = (long long)p.dp_tiles * nk;
+    it = base + sk_start(p, g);
+    it_end = base + sk_start(p, g + 1);
+  }
+  bool first_seg = true;
+  while (it < it_end) {
+  // The thread and wave indices pass through an empty asm each segment, so
+  // the compiler cannot hoist the many lane-dependent LDS addresses (fragment
+  // reads, epilogue staging) out of this loop and keep them live across the
+  // whole K loop.
+  int tid_v = threadIdx.x;
+  asm volatile("" : "+v"(tid_v));
+  int wave_s = wave_id();
+  asm volatile("" : "+s"(wave_s));
+  const int tid = tid_v;
   const int lane = tid & 63;
-  const int wave = wave_id();
+  const int wave = wave_s;
   const int wm = wave / WN, wn = wave % WN;
+  const int t = (int)(it / nk);
+  const int k0 = (int)(it - (long long)t * nk);
+  const int k1 = (int)min((long long)nk, (long long)k0 + (it_end - it));
+  int tm, tn;
+  tile_coords<8>(p, t, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
 
   ALoader la;
   if constexpr (KIND == KIND_F16_CONV) {
-    la.init(p, m0);
+    la.init(p, m0, k0);
   } else {
     la.init(p.A, p.lda, m0, p.M, p.K);
   }
@@ -559,8 +640,6 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   for (int j = 0; j < FN; ++j) csum[j] = 0;
   const bool want_rsum = SUMS && p.zB != 0 && wn == 0;
   const bool want_csum = SUMS && p.zAp != 0 && wm == 0;
-
-  const int nk = (p.K * EB + KT_BYTES - 1) / KT_BYTES;
 
   // Fragments, double-buffered in registers: lane l reads row l % MB of its
   // MB-row block, 16-byte chunk LPR * ks + l / MB (a k-step is 16 * LPR bytes
@@ -641,12 +720,12 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   };
 
   // Prologue: tiles 0 and 1 in flight, tile 0 landed, its first fragments read.
-  la.load(sa0, 0);
-  lb.load(sb0, 0);
-  la.load(sa1, 1);
-  lb.load(sb1, 1);
+  la.load(sa0, k0);
+  lb.load(sb0, k0);
+  la.load(sa1, k0 + 1);
+  lb.load(sb1, k0 + 1);
   wait_vmcnt_lgkm0<NLA + NLB>();
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < FM; ++i) read_a(sa0, 0, i, fa[0][i]);
 #pragma unroll
@@ -693,7 +772,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     la.advance();
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt_lgkm0<NLA>();
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     const uint8_t* As1 = stA(std::integral_constant<int, u + 1>());
     const uint8_t* Bs1 = stB(std::integral_constant<int, u + 1>());
 #pragma unroll
@@ -707,18 +786,18 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     }
     lb.advance();
   };
-  for (int kt = 0; kt < nk; kt += 6) {
+  for (int kt = k0; kt < k1; kt += 6) {
     tile(kt, std::integral_constant<int, 0>());
-    if (kt + 1 < nk) tile(kt + 1, std::integral_constant<int, 1>());
-    if (kt + 2 < nk) tile(kt + 2, std::integral_constant<int, 2>());
-    if (kt + 3 < nk) tile(kt + 3, std::integral_constant<int, 3>());
-    if (kt + 4 < nk) tile(kt + 4, std::integral_constant<int, 4>());
-    if (kt + 5 < nk) tile(kt + 5, std::integral_constant<int, 5>());
+    if (kt + 1 < k1) tile(kt + 1, std::integral_constant<int, 1>());
+    if (kt + 2 < k1) tile(kt + 2, std::integral_constant<int, 2>());
+    if (kt + 3 < k1) tile(kt + 3, std::integral_constant<int, 3>());
+    if (kt + 4 < k1) tile(kt + 4, std::integral_constant<int, 4>());
+    if (kt + 5 < k1) tile(kt + 5, std::integral_constant<int, 5>());
   }
-  // Loads past the last tile may still be writing (zeros): drain them before
+  // Loads past the segment's last tile may still be writing: drain them before
   // the epilogue reuses the stage arrays.
   wait_vmcnt_lgkm0<0>();
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
 
   // ------------------------------------------------------------------ epilogue
   // The accumulators are staged through LDS one wave-row at a time (TM rows;
@@ -786,6 +865,107 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   const int col = n0 + lcol;
   const int rr0 = tid / GPR;
 
+  // Stream-K.  A segment that is only part of its tile first publishes the
+  // tile's partial sums (mode 1: the staged tile, row-major, in this
+  // workgroup's slot of ws) and counts itself in; the contributor that
+  // counts last runs the epilogue again in mode 2, adding the others'
+  // partials as each group of 4 columns leaves LDS: own + other for two
+  // contributors (one add, the same either way round), else every partial in
+  // workgroup order.  Mode 0: a whole tile, straight to the outputs.
+  int mode = (!SK || (k0 == 0 && k1 == nk)) ? 0 : 1;
+  const int g = (int)blockIdx.x - p.dp_tiles;
+  const int j_sk = t - p.dp_tiles;
+  const long long xs = (long long)j_sk * nk;  // tile start in the stream-K range
+  int g_lo = 0, g_hi = 0;
+  if (mode) {
+    g_lo = sk_owner(p, xs);
+    g_hi = sk_owner(p, xs + nk - 1);
+  }
+  constexpr int SLOT = BM * BN * 4;  // bytes per partial tile
+  auto slot_of = [&](int gg) { return (2 * gg + (sk_start(p, gg) >= xs ? 0 : 1)) * SLOT; };
+  const __amdgpu_buffer_rsrc_t wsr =
+      __builtin_amdgcn_make_buffer_rsrc(p.ws, (short)0, 2 * p.sk_wgs * SLOT, 0x00020000);
+  // One group of 4 columns of one row leaves for the outputs.
+  auto emit = [&](uint4 v, int lrow) {
+    const int row = m0 + lrow;
+      if (row < p.M && col < p.N) {
+        const bool full = col + 3 < p.N;
+        if constexpr (!INT8) {
+          float* dst = p.Cf + (long long)row * p.ldcf + col;
+          if (full && p.vec_c) {
+            store16_nt(dst, v);
+          } else {
+            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+  #pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (col + q < p.N) dst[q] = __builtin_bit_cast(float, vv[q]);
+          }
+        } else {
+          // C = acc' - zA'*colsum(B) - zB*rowsum(A') + K*zA'*zB in wrapping
+          // 32-bit arithmetic; the true value fits in int32 (K <= 33025).
+          uint32_t rcorr = 0;
+          if constexpr (SUMS) rcorr = p.zB != 0 ? (uint32_t)p.zB * (uint32_t)sums[lrow] : 0u;
+          const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+          int32_t c[4];
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t ccorr = 0;
+            if constexpr (SUMS)
+              ccorr = p.zAp != 0 ? (uint32_t)p.zAp * (uint32_t)sums[BM + min(lcol + q, BN - 1)] : 0u;
+            c[q] = (int32_t)(vv[q] - ccorr - rcorr + kzz);
+          }
+          if (p.Ci) {
+            int32_t* dst = p.Ci + (long long)row * p.ldci + col;
+            if (full && p.vec_c) {
+              store16_nt(dst, make_uint4((uint32_t)c[0], (uint32_t)c[1], (uint32_t)c[2], (uint32_t)c[3]));
+            } else {
+  #pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (col + q < p.N) dst[q] = c[q];
+            }
+          }
+          float cf[4];
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) cf[q] = (float)c[q];  // round to nearest even
+          if (p.D) {
+            float* dst = p.D + (long long)row * p.ldd + col;
+            float d[4];
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) d[q] = cf[q] * p.dq;
+            if (full && p.vec_d) {
+              store16_nt(dst, make_uint4(__builtin_bit_cast(uint32_t, d[0]), __builtin_bit_cast(uint32_t, d[1]),
+                                         __builtin_bit_cast(uint32_t, d[2]), __builtin_bit_cast(uint32_t, d[3])));
+            } else {
+  #pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (col + q < p.N) dst[q] = d[q];
+            }
+          }
+          if (p.Qo) {
+            int8_t* dst = p.Qo + (long long)row * p.ldq + col;
+            uint32_t packed = 0;
+            int8_t qv[4];
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int cc = min(col + q, p.N - 1);
+              const float t = cf[q] * p.scale[cc];  // separately rounded: built with -ffp-contract=off
+              const float y = t + p.bias[cc];
+              float r = __builtin_rintf(y);         // half to even
+              r = fminf(fmaxf(r, -128.f), 127.f);
+              qv[q] = (int8_t)(int)r;
+              packed |= (uint32_t)(uint8_t)qv[q] << (8 * q);
+            }
+            if (full && p.vec_q) {
+              store4_nt(dst, packed);
+            } else {
+  #pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (col + q < p.N) dst[q] = qv[q];
+            }
+          }
+        }
+      }
+  };
 #pragma unroll
   for (int h = 0; h < WM; ++h) {
     if (wm == h) {
@@ -811,87 +991,72 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       const uint8_t* arr = stage_rt((pass * RPP) / 32);
       const int lrow = h * TM + rr;
       const int row = m0 + lrow;
-      if (row < p.M && col < p.N) {
-        const uint4 v = *reinterpret_cast<const uint4*>(arr + stage_off(rr & 31, lcol));
-        const bool full = col + 3 < p.N;
-        if constexpr (!INT8) {
-          float* dst = p.Cf + (long long)row * p.ldcf + col;
-          if (full && p.vec_c) {
-            store16_nt(dst, v);
-          } else {
-            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (col + q < p.N) dst[q] = __builtin_bit_cast(float, vv[q]);
-          }
-        } else {
-          // C = acc' - zA'*colsum(B) - zB*rowsum(A') + K*zA'*zB in wrapping
-          // 32-bit arithmetic; the true value fits in int32 (K <= 33025).
-          uint32_t rcorr = 0;
-          if constexpr (SUMS) rcorr = p.zB != 0 ? (uint32_t)p.zB * (uint32_t)sums[lrow] : 0u;
-          const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-          int32_t c[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            uint32_t ccorr = 0;
-            if constexpr (SUMS)
-              ccorr = p.zAp != 0 ? (uint32_t)p.zAp * (uint32_t)sums[BM + min(lcol + q, BN - 1)] : 0u;
-            c[q] = (int32_t)(vv[q] - ccorr - rcorr + kzz);
-          }
-          if (p.Ci) {
-            int32_t* dst = p.Ci + (long long)row * p.ldci + col;
-            if (full && p.vec_c) {
-              store16_nt(dst, make_uint4((uint32_t)c[0], (uint32_t)c[1], (uint32_t)c[2], (uint32_t)c[3]));
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (col + q < p.N) dst[q] = c[q];
-            }
-          }
-          float cf[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) cf[q] = (float)c[q];  // round to nearest even
-          if (p.D) {
-            float* dst = p.D + (long long)row * p.ldd + col;
-            float d[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) d[q] = cf[q] * p.dq;
-            if (full && p.vec_d) {
-              store16_nt(dst, make_uint4(__builtin_bit_cast(uint32_t, d[0]), __builtin_bit_cast(uint32_t, d[1]),
-                                         __builtin_bit_cast(uint32_t, d[2]), __builtin_bit_cast(uint32_t, d[3])));
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (col + q < p.N) dst[q] = d[q];
-            }
-          }
-          if (p.Qo) {
-            int8_t* dst = p.Qo + (long long)row * p.ldq + col;
-            uint32_t packed = 0;
-            int8_t qv[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int cc = min(col + q, p.N - 1);
-              const float t = cf[q] * p.scale[cc];  // separately rounded: built with -ffp-contract=off
-              const float y = t + p.bias[cc];
-              float r = __builtin_rintf(y);         // half to even
-              r = fminf(fmaxf(r, -128.f), 127.f);
-              qv[q] = (int8_t)(int)r;
-              packed |= (uint32_t)(uint8_t)qv[q] << (8 * q);
-            }
-            if (full && p.vec_q) {
-              store4_nt(dst, packed);
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q)
-                if (col + q < p.N) dst[q] = qv[q];
-            }
-          }
+      uint4 v = *reinterpret_cast<const uint4*>(arr + stage_off(rr & 31, lcol));
+      const int voff = (lrow * BN + lcol) * 4;
+      if constexpr (SK) {
+        if (mode == 1) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), wsr, voff,
+                                                 (2 * g + (first_seg ? 0 : 1)) * SLOT, CPOL_DEV);
+          continue;
         }
       }
+      if (mode == 0) emit(v, lrow);
     }
     __syncthreads();
   }
+  if constexpr (SK) if (mode == 1) {
+    // the partial is out (its device-coherent stores acknowledged): count
+    // this contributor in
+    wait_vmcnt_lgkm0<0>();
+    __syncthreads();
+    // (the flag lives in the idle second B stage; read as a wave-uniform
+    // value so the segment loop stays scalar)
+    volatile int* const s_last = reinterpret_cast<volatile int*>(sb1);
+    if (tid == 0) {
+      const int before = atomicAdd(p.cnt + j_sk, 1);
+      const int last = before == g_hi - g_lo;
+      if (last) __hip_atomic_store(p.cnt + j_sk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
+      *s_last = last;
+    }
+    __syncthreads();
+    const bool last = __builtin_amdgcn_readfirstlane(*s_last) != 0;
+    __syncthreads();
+    if (last) {
+      // every partial, this one included, in workgroup order (device-coherent
+      // loads: they read past this XCD's L2)
+      // rows in batches of RB, every load of a batch in flight at once
+      constexpr int RB = (BM / RPP) < 16 ? (BM / RPP) : 16;
+      static_assert((BM / RPP) % RB == 0, "row batches");
+      auto load_rows = [&](int slot, int lrow0, uint4 (&x)[RB]) {
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+          x[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               wsr, ((lrow0 + b * RPP) * BN + lcol) * 4, slot, CPOL_DEV));
+      };
+      for (int lrow0 = rr0; lrow0 < BM; lrow0 += RB * RPP) {
+        uint4 v[RB], w[RB];
+        load_rows(slot_of(g_lo), lrow0, v);
+        for (int gg = g_lo + 1; gg <= g_hi; ++gg) {
+          load_rows(slot_of(gg), lrow0, w);
+#pragma unroll
+          for (int b = 0; b < RB; ++b) {
+            if constexpr (INT8) {
+              v[b] = make_uint4(v[b].x + w[b].x, v[b].y + w[b].y, v[b].z + w[b].z, v[b].w + w[b].w);
+            } else {
+              const float4 f = __builtin_bit_cast(float4, v[b]), e = __builtin_bit_cast(float4, w[b]);
+              v[b] = __builtin_bit_cast(uint4, make_float4(f.x + e.x, f.y + e.y, f.z + e.z, f.w + e.w));
+            }
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < RB; ++b) emit(v[b], lrow0 + b * RPP);
+      }
+    }
+  }
+  if constexpr (!SK) break;  // one whole tile per workgroup: no loop
+  it += k1 - k0;
+  first_seg = false;
+  }  // segments
 }
 
 }  // namespace igc

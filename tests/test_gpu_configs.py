@@ -109,9 +109,11 @@ def test_c5_sampled_rows(igc, oracle):
     assert np.array_equal(Q, ref)
 
 
-def test_c4_sampled_pixels(igc, oracle):
+@pytest.mark.parametrize("streamk", ["1", "2"])
+def test_c4_sampled_pixels(igc, oracle, monkeypatch, streamk):
     import torch
 
+    monkeypatch.setenv("IGC_STREAMK", streamk)
     wl = synth.workload("c4")
     d = wl.dims
     x, w = wl.arrays["x"], wl.arrays["w"]
@@ -121,7 +123,10 @@ def test_c4_sampled_pixels(igc, oracle):
                              d["stride_h"], d["stride_w"], d["pad_h"], d["pad_w"], dx, dw, dy)
     M = d["M"]
     rng = np.random.default_rng(44)
-    pix = {0, 13, 14, 195, 196, 255, 256, M - 1, M - 196, 14 * 14 * 128 + 7 * 14 + 7}
+    # (with the split forced, tile rows 128.. of the 196 hold the tiles shared
+    # between workgroups: 392 tiles on 256 compute units)
+    pix = {0, 13, 14, 195, 196, 255, 256, M - 1, M - 196, 14 * 14 * 128 + 7 * 14 + 7,
+           128 * 256, 128 * 256 - 1, 150 * 256 + 77, 170 * 256 + 255, 190 * 256 + 1}
     pix |= set(rng.integers(0, M, 40).tolist())
     pix = np.array(sorted(pix))
     y = to_host(dy.reshape(M, d["Kout"])[pix.tolist()])

@@ -298,3 +298,43 @@ def test_conv_impulse(igc):
             if 0 <= p < H and 0 <= q < W:
                 want[0, p, q, :] = w[:, r, s, c0].astype(np.float32)
     assert np.array_equal(y, want)
+
+
+# ----------------------------------------------------------------- stream-K
+# More 256x256 tiles than one round of compute units, not a whole number of
+# rounds: the last tiles are shared between workgroups and summed through the
+# workspace.  The shared tiles are the last ones in the tile order, i.e. the
+# last tile rows here.
+def _sk_run(igc, A, Bt, monkeypatch, on):
+    monkeypatch.delenv("IGC_FORCE_VARIANT", raising=False)
+    monkeypatch.setenv("IGC_STREAMK", "2" if on else "0")
+    return run_f16(igc, A, Bt)
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (6144, 4096, 512),   # 384 tiles: 128 shared, two workgroups each
+    (4352, 4096, 1024),  # 272 tiles: 16 shared, four workgroups each
+    (4352, 4096, 648),   # partial K tile first, 11 K tiles
+])
+def test_streamk_integer_valued_exact(igc, oracle, monkeypatch, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    A = synth.f16_small_ints(rng, (M, K))
+    Bt = synth.f16_small_ints(rng, (N, K))
+    C = _sk_run(igc, A, Bt, monkeypatch, True)
+    C0 = _sk_run(igc, A, Bt, monkeypatch, False)
+    assert np.array_equal(C, C0)
+    rows = np.array(sorted({4095, 4096, 4097, M - 1} | set(rng.integers(4096, M, 24).tolist())
+                           | set(rng.integers(0, 4096, 8).tolist())))
+    assert np.array_equal(C[rows].astype(np.float64), oracle.gemm_f16(A[rows], Bt))
+
+
+def test_streamk_random_tolerance_and_deterministic(igc, oracle, monkeypatch):
+    M, N, K = 6144, 4096, 1024
+    rng = np.random.default_rng(17)
+    A = synth.f16_normal(rng, (M, K))
+    Bt = synth.f16_normal(rng, (N, K))
+    C1 = _sk_run(igc, A, Bt, monkeypatch, True)
+    C2 = _sk_run(igc, A, Bt, monkeypatch, True)
+    assert np.array_equal(C1, C2)
+    rows = np.array(sorted({4096, M - 1} | set(rng.integers(4096, M, 16).tolist())))
+    assert fp_rel_err(C1[rows], oracle.gemm_f16(A[rows], Bt)) <= FP_TOL
