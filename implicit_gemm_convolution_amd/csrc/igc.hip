@@ -218,8 +218,12 @@ int launch(const igc::Params& p, bool fast, hipStream_t stream) {
   int v = choose_variant(p.M, p.N);
   // The element-wise (unaligned) loaders need more registers; they stop at 128x128.
   if (!fast && (v == V_256x256 || v == V_256x128)) v = V_128x128;
-  return fast ? launch_variant<KIND, true, SUMS>(v, p, stream)
-              : launch_variant<KIND, false, SUMS>(v, p, stream);
+  if constexpr (KIND == igc::KIND_F16_CONV_C64) {
+    return launch_variant<KIND, true, SUMS>(v, p, stream);  // dispatched only with aligned operands
+  } else {
+    return fast ? launch_variant<KIND, true, SUMS>(v, p, stream)
+                : launch_variant<KIND, false, SUMS>(v, p, stream);
+  }
 }
 
 igc::Params zero_params() {
@@ -348,6 +352,9 @@ int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, in
   p.vec_c = aligned16(y) && Kout % 4 == 0;
   const bool fast = aligned16(x) && aligned16(w) && C % 8 == 0 && nx * 2 < (1LL << 31) &&
                     256LL * K * 2 < (1LL << 31);
+  // whole 64-channel K tiles within one tap: the uniform-tap loader
+  if (fast && C % 64 == 0 && (long long)R * S <= 31)
+    return launch<igc::KIND_F16_CONV_C64, false>(p, true, static_cast<hipStream_t>(stream));
   return launch<igc::KIND_F16_CONV, false>(p, fast, static_cast<hipStream_t>(stream));
 }
 

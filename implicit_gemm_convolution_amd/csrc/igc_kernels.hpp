@@ -64,7 +64,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define IGC_MFMA_DIM 16
 #endif
 
-enum Kind : int { KIND_F16_GEMM = 0, KIND_F16_CONV = 1, KIND_U8I8_GEMM = 2 };
+// KIND_F16_CONV_C64: the convolution when C % 64 == 0 and R*S <= 31, so a
+// K tile (64 channels) never straddles two taps and the tap is uniform.
+enum Kind : int { KIND_F16_GEMM = 0, KIND_F16_CONV = 1, KIND_U8I8_GEMM = 2, KIND_F16_CONV_C64 = 3 };
 
 constexpr int KT_BYTES = 128;    // bytes of K per tile row
 constexpr int CHUNK_BYTES = 16;  // one vector load
@@ -457,6 +459,90 @@ struct Im2colLoader {
   }
 };
 
+// The implicit-im2col A operand when C % 64 == 0 and R*S <= 31 (FAST only).
+// Every K tile is 64 channels of one tap (r, s), the same for all lanes, so
+// the tap walk is scalar.  A row's input pixel is a fixed per-lane offset;
+// the tap moves the buffer descriptor's base instead (scalar arithmetic), and
+// each row keeps a bit mask of the taps that fall inside the image (the zero
+// padding), so a load costs three vector instructions: the mask bit, a
+// compare and a select of the out-of-range offset.
+template <int NT, int ROWS>
+struct Im2colC64Loader {
+  typedef DmaShape<NT, ROWS> Sh;
+  static constexpr int NPART = Sh::NQ;
+  const uint8_t* x;
+  uint32_t bytes;       // size of x
+  int C, S, W, RS;
+  int p0;               // ph*W + pw: keeps the per-row offsets non-negative
+  uint32_t pixb[Sh::NQ];  // (pixel of tap (0,0) + p0) * C * 2 + chunk * 16
+  uint32_t mask[Sh::NQ];  // bit r*S+s: tap (r, s) of this row is inside the image
+  mutable int cur_r, cur_s, cur_c;  // tap and channel of the next K tile
+
+  __device__ __forceinline__ void init(const Params& p, int m0, int kt0) {
+    x = p.A;
+    C = p.C; S = p.S; W = p.W; RS = p.R * p.S;
+    bytes = (uint32_t)((long long)p.Nb * p.H * p.W * p.C * 2);
+    p0 = p.ph * p.W + p.pw;
+    const int PQ = p.P * p.Q;
+#pragma unroll
+    for (int j = 0; j < Sh::NQ; ++j) {
+      const int m = m0 + Sh::lane_row() + j * 8 * Sh::NWAVES;
+      pixb[j] = 0;
+      mask[j] = 0;
+      if (m < p.M) {
+        const int n = m / PQ;
+        const int pq = m - n * PQ;
+        const int pp = pq / p.Q;
+        const int qq = pq - pp * p.Q;
+        const int h0 = pp * p.sh - p.ph;
+        const int w0 = qq * p.sw - p.pw;
+        pixb[j] = (uint32_t)((n * p.H * p.W + h0 * p.W + w0 + p0) * C * 2 + Sh::lane_chunk() * CHUNK_BYTES);
+        uint32_t mk = 0;
+        for (int r = 0; r < p.R; ++r)
+          for (int s2 = 0; s2 < p.S; ++s2)
+            if ((unsigned)(h0 + r) < (unsigned)p.H && (unsigned)(w0 + s2) < (unsigned)p.W)
+              mk |= 1u << (r * p.S + s2);
+        mask[j] = mk;
+      }
+    }
+    const int k = kt0 * 64;
+    const int rs = k / C;
+    cur_c = k - rs * C;
+    cur_r = rs / S;
+    cur_s = rs - cur_r * S;
+  }
+  __device__ __forceinline__ void advance() const {
+    cur_c += 64;
+    if (cur_c == C) {
+      cur_c = 0;
+      if (++cur_s == S) {
+        cur_s = 0;
+        ++cur_r;
+      }
+    }
+  }
+  __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
+#pragma unroll
+    for (int j = 0; j < NPART; ++j) part(tile, kt, j);
+    advance();
+  }
+  __device__ __forceinline__ void part(uint8_t* tile, int, int j) const {
+    const int tap = cur_r * S + cur_s;
+    // tiles past the last tap (prefetch beyond K) use bit 31, never set
+    const int bit = tap < RS ? tap : 31;
+    const long long toff = ((long long)(cur_r * W + cur_s - p0) * C + cur_c) * 2;
+    const uint64_t base = (uint64_t)(uintptr_t)x + (uint64_t)toff;
+    // bytes of x past the moved base, at most 2^31 so that OOB stays out of
+    // range (0 once the tap has left x: every lane then reads zeros)
+    const long long left = (long long)bytes - toff;
+    const uint32_t num = left <= 0 ? 0u : left >= (long long)OOB ? OOB : (uint32_t)left;
+    Rsrc r;
+    r.d = i32x4{(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)num, 0x00020000};
+    const uint32_t vo = ((mask[j] >> bit) & 1u) ? pixb[j] : OOB;
+    dma16s(r, Sh::dst(tile, j), vo, 0);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // MFMA wrappers.  One call = one 32 x 32 output tile, 32 bytes of K per row.
 // ---------------------------------------------------------------------------
@@ -481,6 +567,8 @@ struct Mfma<KIND_F16_GEMM, 16> {
 };
 template <int MB>
 struct Mfma<KIND_F16_CONV, MB> : Mfma<KIND_F16_GEMM, MB> {};
+template <int MB>
+struct Mfma<KIND_F16_CONV_C64, MB> : Mfma<KIND_F16_GEMM, MB> {};
 template <>
 struct Mfma<KIND_U8I8_GEMM, 32> {
   typedef i32x16 acc_t;
@@ -547,9 +635,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // always gets whole tiles (the host sets dp_tiles accordingly)
   constexpr bool SK = !INT8 && !SUMS;
   // (the im2col operand walks K in order, so the conv's B does too)
-  constexpr bool TAIL_FIRST = FAST && KIND != KIND_F16_CONV;
-  typedef typename std::conditional<KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
-                                    RowDmaLoader<NT, BM, EB, FAST, TAIL_FIRST>>::type ALoader;
+  constexpr bool CONV = KIND == KIND_F16_CONV || KIND == KIND_F16_CONV_C64;
+  constexpr bool TAIL_FIRST = FAST && !CONV;
+  typedef typename std::conditional<
+      KIND == KIND_F16_CONV_C64, Im2colC64Loader<NT, BM>,
+      typename std::conditional<KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
+                                RowDmaLoader<NT, BM, EB, FAST, TAIL_FIRST>>::type>::type ALoader;
+  static_assert(KIND != KIND_F16_CONV_C64 || FAST, "the uniform-tap conv loader needs aligned operands");
   typedef RowDmaLoader<NT, BN, EB, FAST, TAIL_FIRST> BLoader;
   // direct-to-LDS loads per K tile per wave (counted by vmcnt); the
   // element-wise path of unaligned operands is waited for as it goes
@@ -616,7 +708,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   const int m0 = tm * BM, n0 = tn * BN;
 
   ALoader la;
-  if constexpr (KIND == KIND_F16_CONV) {
+  if constexpr (CONV) {
     la.init(p, m0, k0);
   } else {
     la.init(p.A, p.lda, m0, p.M, p.K);

@@ -257,6 +257,11 @@ CONV_CASES = [
     (1, 7, 9, 3, 13, 3, 3, (1, 2), (1, 0)),       # C % 8 != 0, odd Kout
     (2, 6, 6, 24, 20, 3, 2, (2, 1), (0, 1)),
     (1, 30, 30, 8, 300, 3, 3, (1, 1), (1, 1)),    # M = 900 rows, N ragged
+    # C % 64 == 0 and R*S <= 31: the uniform-tap loader
+    (2, 13, 10, 64, 40, 5, 5, (2, 2), (2, 2)),
+    (1, 12, 12, 128, 64, 3, 3, (2, 1), (0, 1)),
+    (1, 8, 8, 64, 64, 1, 1, (1, 1), (0, 0)),
+    (1, 9, 9, 64, 32, 7, 7, (1, 1), (3, 3)),      # R*S = 49: the general loader
 ]
 
 
