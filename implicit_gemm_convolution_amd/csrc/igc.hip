@@ -122,7 +122,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Tile variants.  The large tile keeps the most MFMA work per LDS byte; the
 // smaller ones exist so that small problems still spread over the 256 CUs
 // (the multi-kernel-per-shape dispatch of [GEMM-TVM] §4.3, done at run time).
-enum Variant { V_AUTO = -1, V_256x256 = 0, V_128x128 = 1, V_64x64 = 2, V_256x128 = 3, V_COUNT = 4 };
+enum Variant { V_AUTO = -1, V_256x256 = 0, V_128x128 = 1, V_64x64 = 2, V_256x128 = 3, V_224x256 = 4, V_COUNT = 5 };
 
 int forced_variant() {
   const char* s = std::getenv("IGC_FORCE_VARIANT");
@@ -133,10 +133,20 @@ int forced_variant() {
 
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
-int choose_variant(int M, int N) {
+// Large problems run on one workgroup per compute unit, in rounds of `cus`
+// tiles, so their time goes as (rounds) x (tile area).  224 x 256 tiles are
+// taken over 256 x 256 when that cost is lower: e.g. M = 50176, N = 512
+// (the 256 x 14 x 14 conv) needs 392 tiles of 256 rows, two rounds with the
+// second 53% full, but 448 tiles of 224 rows, two rounds of 7/8 the work.
+int choose_variant(int M, int N, int cus) {
   int f = forced_variant();
   if (f != V_AUTO) return f;
-  if (ceil_div(M, 256) * ceil_div(N, 256) >= 192) return V_256x256;
+  const long long t256 = ceil_div(M, 256) * ceil_div(N, 256);
+  if (t256 >= 192) {
+    const long long t224 = ceil_div(M, 224) * ceil_div(N, 256);
+    const long long c256 = ceil_div(t256, cus) * 256, c224 = ceil_div(t224, cus) * 224;
+    return c224 < c256 ? V_224x256 : V_256x256;
+  }
   if (ceil_div(M, 128) * ceil_div(N, 128) >= 192) return V_128x128;
   return V_64x64;
 }
@@ -202,6 +212,9 @@ int launch_one(igc::Params p, hipStream_t stream) {
 template <int KIND, bool FAST, bool SUMS>
 int launch_variant(int v, const igc::Params& p, hipStream_t stream) {
   switch (v) {
+    case V_224x256:
+      if constexpr (FAST) return launch_one<KIND, 224, 256, 2, 2, FAST, SUMS>(p, stream);
+      [[fallthrough]];
     case V_256x256:
       if constexpr (FAST) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, stream);
       [[fallthrough]];
@@ -214,10 +227,10 @@ int launch_variant(int v, const igc::Params& p, hipStream_t stream) {
 }
 
 template <int KIND, bool SUMS>
-int launch(const igc::Params& p, bool fast, hipStream_t stream) {
-  int v = choose_variant(p.M, p.N);
+int launch(const igc::Params& p, bool fast, hipStream_t stream, int dev) {
+  int v = choose_variant(p.M, p.N, device_cus(dev));
   // The element-wise (unaligned) loaders need more registers; they stop at 128x128.
-  if (!fast && (v == V_256x256 || v == V_256x128)) v = V_128x128;
+  if (!fast && (v == V_256x256 || v == V_256x128 || v == V_224x256)) v = V_128x128;
   if constexpr (KIND == igc::KIND_F16_CONV_C64) {
     return launch_variant<KIND, true, SUMS>(v, p, stream);  // dispatched only with aligned operands
   } else {
@@ -276,7 +289,7 @@ int gemm_f16f32(int M, int N, int K, const void* A, int lda, const void* B, int 
   // Buffer descriptors of the fast path cover one tile of rows and must stay below 2^31 bytes.
   const bool fast = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 &&
                     256LL * lda * 2 < (1LL << 31) && 256LL * ldb * 2 < (1LL << 31);
-  return launch<igc::KIND_F16_GEMM, false>(p, fast, static_cast<hipStream_t>(stream));
+  return launch<igc::KIND_F16_GEMM, false>(p, fast, static_cast<hipStream_t>(stream), dev);
 }
 
 int gemm_u8i8_zp(int M, int N, int K, const uint8_t* A, int lda, int zA, const int8_t* B, int ldb,
@@ -316,8 +329,8 @@ int gemm_u8i8_zp(int M, int N, int K, const uint8_t* A, int lda, int zA, const i
                     K % 16 == 0 && 256LL * lda < (1LL << 31) && 256LL * ldb < (1LL << 31);
   // The zero-point sums are compiled only into the kernels that need them.
   if (p.zAp != 0 || p.zB != 0)
-    return launch<igc::KIND_U8I8_GEMM, true>(p, fast, static_cast<hipStream_t>(stream));
-  return launch<igc::KIND_U8I8_GEMM, false>(p, fast, static_cast<hipStream_t>(stream));
+    return launch<igc::KIND_U8I8_GEMM, true>(p, fast, static_cast<hipStream_t>(stream), dev);
+  return launch<igc::KIND_U8I8_GEMM, false>(p, fast, static_cast<hipStream_t>(stream), dev);
 }
 
 int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h,
@@ -354,8 +367,8 @@ int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, in
                     256LL * K * 2 < (1LL << 31);
   // whole 64-channel K tiles within one tap: the uniform-tap loader
   if (fast && C % 64 == 0 && (long long)R * S <= 31)
-    return launch<igc::KIND_F16_CONV_C64, false>(p, true, static_cast<hipStream_t>(stream));
-  return launch<igc::KIND_F16_CONV, false>(p, fast, static_cast<hipStream_t>(stream));
+    return launch<igc::KIND_F16_CONV_C64, false>(p, true, static_cast<hipStream_t>(stream), dev);
+  return launch<igc::KIND_F16_CONV, false>(p, fast, static_cast<hipStream_t>(stream), dev);
 }
 
 }  // extern "C"

@@ -630,6 +630,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int NE = MB * MB / 64;          // accumulator elements per lane
   constexpr int LPR = 64 / MB;              // lanes sharing one row of a fragment
   constexpr int SA = BM * KT_BYTES, SB = BN * KT_BYTES;  // stage sizes
+  // The A stage arrays also stage 32 output rows of BN fp32/int32 each in
+  // the epilogue, so a tile with BM < BN allocates them at that size.
+  constexpr int SA_ALLOC = SA > 32 * BN * 4 ? SA : 32 * BN * 4;
   constexpr bool INT8 = KIND == KIND_U8I8_GEMM;
   // stream-K (shared tiles) is compiled for the fp16 kinds; the integer GEMM
   // always gets whole tiles (the host sets dp_tiles accordingly)
@@ -647,15 +650,15 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // element-wise path of unaligned operands is waited for as it goes
   constexpr int NLA = FAST ? ALoader::NPART : 0;
   constexpr int NLB = FAST ? BLoader::NPART : 0;
-  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
-  static_assert(TM <= 128 && BM >= BN && FN <= FM, "epilogue staging reuses the stage arrays");
+  static_assert(TM % MB == 0 && TM % 16 == 0 && TN % 32 == 0, "wave tile must be whole MFMA blocks");
+  static_assert(TM <= 128, "epilogue staging reuses the stage arrays (at most four 32-row arrays)");
   static_assert(NLA + NLB < 64, "vmcnt range");
   typedef typename Mfma<KIND, MB>::acc_t acc_t;
 
   // One LDS array per stage: A in 3 stages, B in 2 (160 KiB at 256 x 256).
-  __shared__ __attribute__((aligned(16))) uint8_t sa0[SA];
-  __shared__ __attribute__((aligned(16))) uint8_t sa1[SA];
-  __shared__ __attribute__((aligned(16))) uint8_t sa2[SA];
+  __shared__ __attribute__((aligned(16))) uint8_t sa0[SA_ALLOC];
+  __shared__ __attribute__((aligned(16))) uint8_t sa1[SA_ALLOC];
+  __shared__ __attribute__((aligned(16))) uint8_t sa2[SA_ALLOC];
   __shared__ __attribute__((aligned(16))) uint8_t sb0[SB];
   __shared__ __attribute__((aligned(16))) uint8_t sb1[SB];
   auto stA = [&](auto U) -> uint8_t* {
@@ -911,7 +914,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   auto stage_rt = [&](int u) -> uint8_t* {  // u is a constant after unrolling
     return u == 0 ? sa0 : u == 1 ? sa1 : u == 2 ? sa2 : sb0;
   };
-  static_assert(32 * BN * 4 <= SB && (BM + BN) * 4 <= SB, "staging and sums fit in the stages");
+  static_assert(32 * BN * 4 <= SB && 32 * BN * 4 <= SA_ALLOC && (BM + BN) * 4 <= SB,
+                "staging and sums fit in the stages");
   int* const sums = reinterpret_cast<int*>(sb1);
   // rl: row within a 32-row array; c: column.  The 16-byte chunk index is
   // XOR-ed with a function of the row so that the row groups written by one
@@ -1117,7 +1121,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       // every partial, this one included, in workgroup order (device-coherent
       // loads: they read past this XCD's L2)
       // rows in batches of RB, every load of a batch in flight at once
-      constexpr int RB = (BM / RPP) < 16 ? (BM / RPP) : 16;
+      constexpr int NROW = BM / RPP;
+      constexpr int RB = NROW % 16 == 0 ? 16 : NROW % 8 == 0 ? 8 : NROW % 4 == 0 ? 4 : NROW < 16 ? NROW : 1;
       static_assert((BM / RPP) % RB == 0, "row batches");
       auto load_rows = [&](int slot, int lrow0, uint4 (&x)[RB]) {
 #pragma unroll

@@ -109,10 +109,14 @@ def test_c5_sampled_rows(igc, oracle):
     assert np.array_equal(Q, ref)
 
 
-@pytest.mark.parametrize("streamk", ["1", "2"])
-def test_c4_sampled_pixels(igc, oracle, monkeypatch, streamk):
+# default: 224x256 tiles (448 tiles, two full rounds on 256 compute units);
+# forced: 256x256 tiles with the last round's tiles shared (stream-K)
+@pytest.mark.parametrize("variant,streamk", [(None, "1"), ("0", "2")])
+def test_c4_sampled_pixels(igc, oracle, monkeypatch, variant, streamk):
     import torch
 
+    if variant is not None:
+        monkeypatch.setenv("IGC_FORCE_VARIANT", variant)
     monkeypatch.setenv("IGC_STREAMK", streamk)
     wl = synth.workload("c4")
     d = wl.dims
@@ -125,7 +129,7 @@ def test_c4_sampled_pixels(igc, oracle, monkeypatch, streamk):
     rng = np.random.default_rng(44)
     # (with the split forced, tile rows 128.. of the 196 hold the tiles shared
     # between workgroups: 392 tiles on 256 compute units)
-    pix = {0, 13, 14, 195, 196, 255, 256, M - 1, M - 196, 14 * 14 * 128 + 7 * 14 + 7,
+    pix = {0, 13, 14, 195, 196, 223, 224, 255, 256, M - 1, M - 196, M - 224, 14 * 14 * 128 + 7 * 14 + 7,
            128 * 256, 128 * 256 - 1, 150 * 256 + 77, 170 * 256 + 255, 190 * 256 + 1}
     pix |= set(rng.integers(0, M, 40).tolist())
     pix = np.array(sorted(pix))
