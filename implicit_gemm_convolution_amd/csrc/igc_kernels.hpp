@@ -960,6 +960,21 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   const int lcol = (tid % GPR) * 4;
   const int col = n0 + lcol;
   const int rr0 = tid / GPR;
+  // A thread's 4 columns are the same in every row it emits: their
+  // requantize scale and bias are loaded once, before the rows (loaded per
+  // row, each pass waited for its own loads behind the previous pass's
+  // stores, which may alias them).
+  float q_scale[4] = {0.f, 0.f, 0.f, 0.f}, q_bias[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (INT8) {
+    if (p.Qo) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cc = min(col + q, p.N - 1);
+        q_scale[q] = p.scale[cc];
+        q_bias[q] = p.bias[cc];
+      }
+    }
+  }
 
   // Stream-K.  A segment that is only part of its tile first publishes the
   // tile's partial sums (mode 1: the staged tile, row-major, in this
@@ -1043,9 +1058,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
             int8_t qv[4];
   #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int cc = min(col + q, p.N - 1);
-              const float t = cf[q] * p.scale[cc];  // separately rounded: built with -ffp-contract=off
-              const float y = t + p.bias[cc];
+              const float t = cf[q] * q_scale[q];  // separately rounded: built with -ffp-contract=off
+              const float y = t + q_bias[q];
               float r = __builtin_rintf(y);         // half to even
               r = fminf(fmaxf(r, -128.f), 127.f);
               qv[q] = (int8_t)(int)r;
