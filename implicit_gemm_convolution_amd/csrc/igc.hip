@@ -168,7 +168,7 @@ int streamk_mode() {
 }
 constexpr long long kStreamKFixupIters = 26;
 
-template <int KIND, int BM, int BN, int WM, int WN, bool FAST, bool SUMS>
+template <int KIND, int BM, int BN, int WM, int WN, bool FAST, bool SUMS, int DEPTH = 2>
 int launch_one(igc::Params p, hipStream_t stream) {
   p.tiles_m = (int)ceil_div(p.M, BM);
   p.tiles_n = (int)ceil_div(p.N, BN);
@@ -202,7 +202,7 @@ int launch_one(igc::Params p, hipStream_t stream) {
       }
     }
   }
-  hipLaunchKernelGGL((igc::gemm_kernel<KIND, BM, BN, WM, WN, FAST, SUMS>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((igc::gemm_kernel<KIND, BM, BN, WM, WN, FAST, SUMS, DEPTH>), dim3((unsigned)grid),
                      dim3(64 * WM * WN), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -228,7 +228,8 @@ int launch_variant(int v, const igc::Params& p, hipStream_t stream) {
 
 template <int KIND, bool SUMS>
 int launch(const igc::Params& p, bool fast, hipStream_t stream, int dev) {
-  int v = choose_variant(p.M, p.N, device_cus(dev));
+  const int cus = device_cus(dev);
+  int v = choose_variant(p.M, p.N, cus);
   // The element-wise (unaligned) loaders need more registers; they stop at 128x128.
   if (!fast && (v == V_256x256 || v == V_256x128 || v == V_224x256)) v = V_128x128;
   if constexpr (KIND == igc::KIND_F16_CONV_C64) {

@@ -51,8 +51,19 @@
 
 #include <climits>
 #include <type_traits>
+#include <utility>
 
 namespace igc {
+
+// f(std::integral_constant<int, i>()) for i = 0 .. N-1, in order.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>());
+}
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -274,6 +285,7 @@ struct RowDmaLoader {
   uint32_t lane_off0;   // same, or OOB past the K bound of tile 0 (TAIL_FIRST)
   uint32_t row_step;    // bytes between this lane's rows (uniform)
   int kpad;             // 128 * nk - K * EB: zero bytes in the partial tile
+  int nk;               // K tiles
   uint32_t voff[TAIL_FIRST ? Sh::NQ : 1];  // lane_off + i * row_step (TAIL_FIRST)
 
   __device__ __forceinline__ void init(const uint8_t* ptr, long long ld, int r0, int nrows, int k) {
@@ -286,7 +298,7 @@ struct RowDmaLoader {
       rsrc = make_rsrc(base, (uint32_t)extent);
       lane_off = (uint32_t)(Sh::lane_row() * ld_bytes) + (uint32_t)(Sh::lane_chunk() * CHUNK_BYTES);
       row_step = (uint32_t)(8 * Sh::NWAVES * ld_bytes);
-      const int nk = max(1, (K * EB + KT_BYTES - 1) / KT_BYTES);
+      nk = max(1, (K * EB + KT_BYTES - 1) / KT_BYTES);
       kpad = nk * KT_BYTES - K * EB;
       lane_off0 = Sh::lane_chunk() * CHUNK_BYTES < KT_BYTES - kpad ? lane_off : OOB;
       if constexpr (TAIL_FIRST) {
@@ -317,7 +329,9 @@ struct RowDmaLoader {
   }
   __device__ __forceinline__ void part(uint8_t* tile, int kt, int i) const {
     if constexpr (FAST && TAIL_FIRST) {
-      dma16s(rsrc, Sh::dst(tile, i), voff[i], (uint32_t)(kt * KT_BYTES - kpad));
+      // tiles past K (prefetched by the pipeline, never multiplied) read
+      // out of range: zeros, no memory traffic
+      dma16s(rsrc, Sh::dst(tile, i), voff[i], kt < nk ? (uint32_t)(kt * KT_BYTES - kpad) : OOB);
     } else if (FAST) {
       const bool kin = kt * KT_BYTES + Sh::lane_chunk() * CHUNK_BYTES < K * EB;
       dma16(rsrc, Sh::dst(tile, i), kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
@@ -619,8 +633,14 @@ __device__ __forceinline__ void lds_barrier() {
 // The kernel.
 //  SUMS (u8 x i8 only): accumulate rowsum(A') / colsum(B) for the zero-point
 //  correction; not compiled when zA == 128 and zB == 0.
+//  DEPTH: K tiles in flight ahead of the one being multiplied.  A has
+//  DEPTH + 1 LDS stages; B has 2 at DEPTH 2 (the 160 KiB of LDS at 256 x 256)
+//  and DEPTH + 1 otherwise.  Every launch uses DEPTH 2: deeper rings for the
+//  small tiles of short K loops (up to 7 tiles ahead) measured no faster on
+//  MI355X, whose small launches are bound by fixed costs and a low clock,
+//  not by load latency.
 // ---------------------------------------------------------------------------
-template <int KIND, int BM, int BN, int WM, int WN, bool FAST, bool SUMS = false>
+template <int KIND, int BM, int BN, int WM, int WN, bool FAST, bool SUMS = false, int DEPTH = 2>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int NT = 64 * WM * WN;
   constexpr int EB = (KIND == KIND_U8I8_GEMM) ? 1 : 2;
@@ -652,26 +672,25 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int NLB = FAST ? BLoader::NPART : 0;
   static_assert(TM % MB == 0 && TM % 16 == 0 && TN % 32 == 0, "wave tile must be whole MFMA blocks");
   static_assert(TM <= 128, "epilogue staging reuses the stage arrays (at most four 32-row arrays)");
-  static_assert(NLA + NLB < 64, "vmcnt range");
+  static_assert(DEPTH >= 2 && (DEPTH == 2 || FAST), "deep pipelines need the direct-to-LDS loaders");
+  static_assert((DEPTH - 1) * (NLA + NLB) < 64, "vmcnt range");
   typedef typename Mfma<KIND, MB>::acc_t acc_t;
 
-  // One LDS array per stage: A in 3 stages, B in 2 (160 KiB at 256 x 256).
-  __shared__ __attribute__((aligned(16))) uint8_t sa0[SA_ALLOC];
-  __shared__ __attribute__((aligned(16))) uint8_t sa1[SA_ALLOC];
-  __shared__ __attribute__((aligned(16))) uint8_t sa2[SA_ALLOC];
-  __shared__ __attribute__((aligned(16))) uint8_t sb0[SB];
-  __shared__ __attribute__((aligned(16))) uint8_t sb1[SB];
-  auto stA = [&](auto U) -> uint8_t* {
-    constexpr int u = decltype(U)::value % 3;
-    if constexpr (u == 0) return sa0;
-    if constexpr (u == 1) return sa1;
-    return sa2;
-  };
-  auto stB = [&](auto U) -> uint8_t* {
-    constexpr int u = decltype(U)::value % 2;
-    if constexpr (u == 0) return sb0;
-    return sb1;
-  };
+  // LDS stage rings (DEPTH 2: A in 3 stages, B in 2, 160 KiB at 256 x 256);
+  // the loop below is unrolled over UNR tiles so every stage is a
+  // compile-time LDS address.
+  constexpr int RA = DEPTH + 1, RB = DEPTH == 2 ? 2 : DEPTH + 1;
+  constexpr int UNR = RA == RB ? RA : RA * RB;
+  static_assert(RA >= 3 && RB >= 2, "the epilogue stages through A stages 0-2 and B stages 0-1");
+  __shared__ __attribute__((aligned(16))) uint8_t sa_ring[RA][SA_ALLOC];
+  __shared__ __attribute__((aligned(16))) uint8_t sb_ring[RB][SB];
+  uint8_t* const sa0 = sa_ring[0];
+  uint8_t* const sa1 = sa_ring[1];
+  uint8_t* const sa2 = sa_ring[2];
+  uint8_t* const sb0 = sb_ring[0];
+  uint8_t* const sb1 = sb_ring[1];
+  auto stA = [&](auto U) -> uint8_t* { return sa_ring[decltype(U)::value % RA]; };
+  auto stB = [&](auto U) -> uint8_t* { return sb_ring[decltype(U)::value % RB]; };
 
   // (K = 0 still runs one all-zero K tile, so the outputs are written)
   const int nk = max(1, (p.K * EB + KT_BYTES - 1) / KT_BYTES);
@@ -814,12 +833,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     if constexpr (INT8) ax = axn;
   };
 
-  // Prologue: tiles 0 and 1 in flight, tile 0 landed, its first fragments read.
-  la.load(sa0, k0);
-  lb.load(sb0, k0);
-  la.load(sa1, k0 + 1);
-  lb.load(sb1, k0 + 1);
-  wait_vmcnt_lgkm0<NLA + NLB>();
+  // Prologue: tiles 0 .. DEPTH-1 in flight, tile 0 landed, its first
+  // fragments read.
+  static_for<DEPTH>([&](auto D) {
+    la.load(stA(D), k0 + decltype(D)::value);
+    lb.load(stB(D), k0 + decltype(D)::value);
+  });
+  wait_vmcnt_lgkm0<(DEPTH - 1) * (NLA + NLB)>();
   lds_barrier();
 #pragma unroll
   for (int i = 0; i < FM; ++i) read_a(sa0, 0, i, fa[0][i]);
@@ -833,22 +853,24 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     ax.w ^= 0x80808080u;
   }
 
-  // K tile kt: A in stage kt % 3, B in stage kt % 2.  On entry tiles kt+1 are
-  // in flight.  Region 1: k-steps 0..KSTEPS-2 of tile kt, issuing the loads of
-  // A tile kt+2 into the stage tile kt-1 used.  Then wait until A and B of
-  // tile kt+1 have landed (only A of kt+2 may still be in flight) and every
-  // LDS access of this wave is done, and barrier: every wave is then past
-  // its reads of tile kt.  Region 2: the last k-step of tile kt, issuing the
-  // loads of B tile kt+2 into tile kt's B stage and reading tile kt+1's first
-  // fragments.  [TIR-COMPILER] §2.2/§4.4 pipeline, two tiles deep for A, one
+  // K tile kt (D = DEPTH): A in stage kt % RA, B in stage kt % RB.  On entry
+  // tiles kt+1 .. kt+D-1 are in flight.  Region 1: k-steps 0..KSTEPS-2 of
+  // tile kt, issuing the loads of A tile kt+D into the stage tile kt-1 used.
+  // Then wait until A and B of tile kt+1 have landed (only the loads issued
+  // after them, of tiles kt+2 .. kt+D, may still be in flight) and every LDS
+  // access of this wave is done, and barrier: every wave is then past its
+  // reads of tile kt.  Region 2: the last k-step of tile kt, issuing the
+  // loads of B tile kt+D into stage (kt+D) % RB (tile kt's own at RB = D,
+  // tile kt-1's at RB = D+1) and reading tile kt+1's first fragments.
+  // [TIR-COMPILER] §2.2/§4.4 pipeline; at D = 2 two tiles deep for A, one
   // and a half for B.
   constexpr int NS1 = (KSTEPS - 1) * FM;  // chunks in region 1
   auto tile = [&](int kt, auto U) {
     constexpr int u = decltype(U)::value;
     const uint8_t* As = stA(U);
     const uint8_t* Bs = stB(U);
-    uint8_t* const An = stA(std::integral_constant<int, u + 2>());
-    uint8_t* const Bn = stB(std::integral_constant<int, u + 2>());
+    uint8_t* const An = stA(std::integral_constant<int, u + DEPTH>());
+    uint8_t* const Bn = stB(std::integral_constant<int, u + DEPTH>());
     int buf = 0;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS - 1; ++ks) {
@@ -859,14 +881,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
               c + 1 < FM ? fa[buf][c + 1 < FM ? c + 1 : 0] : fa[buf ^ 1][0], [&]() {
 #pragma unroll
           for (int i = 0; i < ALoader::NPART; ++i)
-            if (i * NS1 / ALoader::NPART == slot) la.part(An, kt + 2, i);
+            if (i * NS1 / ALoader::NPART == slot) la.part(An, kt + DEPTH, i);
         });
       }
       buf ^= 1;
     }
     la.advance();
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt_lgkm0<NLA>();
+    wait_vmcnt_lgkm0<(DEPTH - 2) * (NLA + NLB) + NLA>();
     lds_barrier();
     const uint8_t* As1 = stA(std::integral_constant<int, u + 1>());
     const uint8_t* Bs1 = stB(std::integral_constant<int, u + 1>());
@@ -876,18 +898,17 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
             c + 1 < FM ? fa[buf][c + 1 < FM ? c + 1 : 0] : fa[buf ^ 1][0], [&]() {
 #pragma unroll
         for (int i = 0; i < BLoader::NPART; ++i)
-          if (i * FM / BLoader::NPART == c) lb.part(Bn, kt + 2, i);
+          if (i * FM / BLoader::NPART == c) lb.part(Bn, kt + DEPTH, i);
       });
     }
     lb.advance();
   };
-  for (int kt = k0; kt < k1; kt += 6) {
+  for (int kt = k0; kt < k1; kt += UNR) {
     tile(kt, std::integral_constant<int, 0>());
-    if (kt + 1 < k1) tile(kt + 1, std::integral_constant<int, 1>());
-    if (kt + 2 < k1) tile(kt + 2, std::integral_constant<int, 2>());
-    if (kt + 3 < k1) tile(kt + 3, std::integral_constant<int, 3>());
-    if (kt + 4 < k1) tile(kt + 4, std::integral_constant<int, 4>());
-    if (kt + 5 < k1) tile(kt + 5, std::integral_constant<int, 5>());
+    static_for<UNR - 1>([&](auto J) {
+      constexpr int j = decltype(J)::value + 1;
+      if (kt + j < k1) tile(kt + j, std::integral_constant<int, j>());
+    });
   }
   // Loads past the segment's last tile may still be writing: drain them before
   // the epilogue reuses the stage arrays.

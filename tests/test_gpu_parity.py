@@ -74,6 +74,30 @@ def test_f16_integer_valued_bit_exact(igc, oracle, variant, M, N, K):
     assert np.array_equal(C.astype(np.float64), ref)
 
 
+# Small tiles in grids of one round of 256 compute units or less (ragged
+# edges, long K loops) and of several rounds (289-1156 tiles).
+@pytest.mark.parametrize("variant,M,N,K", [("2", 1088, 1088, 264), ("1", 2176, 2176, 136),
+                                           ("2", 200, 136, 2056), ("1", 300, 260, 1160)])
+def test_f16_small_tiles_one_and_several_rounds(igc, oracle, monkeypatch, variant, M, N, K):
+    monkeypatch.setenv("IGC_FORCE_VARIANT", variant)
+    rng = np.random.default_rng(M + N + K + 1)
+    A = synth.f16_small_ints(rng, (M, K))
+    Bt = synth.f16_small_ints(rng, (N, K))
+    C = run_f16(igc, A, Bt)
+    assert np.array_equal(C.astype(np.float64), oracle.gemm_f16(A, Bt))
+
+
+@pytest.mark.parametrize("variant,M,N,K", [("2", 1088, 1088, 400), ("1", 2176, 2176, 144),
+                                           ("2", 130, 70, 3000), ("1", 300, 260, 2064)])
+def test_u8i8_small_tiles_one_and_several_rounds(igc, oracle, monkeypatch, variant, M, N, K):
+    monkeypatch.setenv("IGC_FORCE_VARIANT", variant)
+    rng = np.random.default_rng(M + N + K + 2)
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = synth.i8_uniform(rng, (N, K))
+    got = run_u8i8(igc, A, 37, Bt, -5, outputs=("C",))
+    assert np.array_equal(got["C"].astype(np.int64), oracle.gemm_u8i8_naive(A, 37, Bt, -5))
+
+
 @pytest.mark.parametrize("variant", VARIANTS, indirect=True)
 @pytest.mark.parametrize("M,N,K", [(256, 256, 1024), (200, 300, 1000), (512, 128, 2048)])
 def test_f16_random_tolerance(igc, oracle, variant, M, N, K):

@@ -33,7 +33,7 @@ def asm(tmp_path_factory):
 
 
 def _params(demangled):
-    m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (true|false), (true|false)>", demangled)
+    m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (true|false), (true|false), (\d+)>", demangled)
     assert m, demangled
     kind, bm, bn, wm, wn = (int(m.group(i)) for i in range(1, 6))
     return kind, bm, bn, m.group(6) == "true"
@@ -58,7 +58,7 @@ def test_no_scratch_and_lds_within_limit(asm):
         lds = int(re.search(r"\.amdhsa_group_segment_fixed_size (\d+)", meta).group(1))
         assert lds <= 160 * 1024, name
         scratch = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", meta).group(1))
-        if bm == 256 and bn == 256:
+        if bn == 256:
             assert scratch == 0, (name, scratch)
 
 
