@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_conv2d_direct_at.argtypes = conv_args + [_p, _p, _p, _i64, _p]
         L.oracle_conv2d_im2col.argtypes = conv_args + [_p, _p, _p]
         L.oracle_im2col_f16.argtypes = [_i64] * 10 + [_p, _p]
+        L.oracle_conv2d_u8i8_direct_at.argtypes = conv_args + [_p, _i64, _p, _i64, _p, _i64, _p]
+        L.oracle_im2col_u8.argtypes = [_i64] * 10 + [_p, _i64, _p]
         L.oracle_conv_out_dim.argtypes = [_i64] * 4
         L.oracle_conv_out_dim.restype = _i64
         L.oracle_num_threads.restype = ctypes.c_int
@@ -230,3 +232,50 @@ def conv2d_im2col(x: np.ndarray, w: np.ndarray, stride=(1, 1), pad=(0, 0)) -> np
     y = np.empty((Nb, P, Q, Kout), np.float64)
     lib().oracle_conv2d_im2col(*dims, _ptr(x), _ptr(w), _ptr(y))
     return y
+
+
+def _qconv_shapes(x, w, stride, pad):
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    assert x.dtype == np.uint8 and w.dtype == np.int8
+    Nb, H, W, C = x.shape
+    Kout, R, S, C2 = w.shape
+    assert C == C2
+    sh, sw = stride
+    ph, pw = pad
+    return x, w, (Nb, H, W, C, Kout, R, S, sh, sw, ph, pw)
+
+
+def conv2d_u8i8_direct_at(x: np.ndarray, zA: int, w: np.ndarray, zB: int, pixels,
+                          stride=(1, 1), pad=(0, 0)) -> np.ndarray:
+    """O8 at listed output pixels m=(n*P+p)*Q+q: sum over the in-image taps of
+    (x - zA)(w - zB), x NHWC uint8, w KRSC int8; returns len(pixels) x Kout int64."""
+    x, w, dims = _qconv_shapes(x, w, stride, pad)
+    pix = np.ascontiguousarray(pixels, np.int64)
+    y = np.empty((pix.size, dims[4]), np.int64)
+    lib().oracle_conv2d_u8i8_direct_at(*dims, _ptr(x), int(zA), _ptr(w), int(zB), _ptr(pix), pix.size,
+                                       _ptr(y))
+    return y
+
+
+def conv2d_u8i8_direct(x: np.ndarray, zA: int, w: np.ndarray, zB: int, stride=(1, 1),
+                       pad=(0, 0)) -> np.ndarray:
+    """O8: the whole NHWC int64 output."""
+    Nb, H, W, _ = x.shape
+    Kout, R, S, _ = w.shape
+    P, Q = conv_out_dim(H, R, stride[0], pad[0]), conv_out_dim(W, S, stride[1], pad[1])
+    y = conv2d_u8i8_direct_at(x, zA, w, zB, np.arange(Nb * P * Q), stride, pad)
+    return y.reshape(Nb, P, Q, Kout)
+
+
+def im2col_u8(x: np.ndarray, zA: int, R: int, S: int, stride=(1, 1), pad=(0, 0)) -> np.ndarray:
+    """u8 im2col with the padding filled with the zero point zA."""
+    x = np.ascontiguousarray(x)
+    assert x.dtype == np.uint8
+    Nb, H, W, C = x.shape
+    sh, sw = stride
+    ph, pw = pad
+    P, Q = conv_out_dim(H, R, sh, ph), conv_out_dim(W, S, sw, pw)
+    col = np.empty((Nb * P * Q, R * S * C), np.uint8)
+    lib().oracle_im2col_u8(Nb, H, W, C, R, S, sh, sw, ph, pw, _ptr(x), int(zA), _ptr(col))
+    return col

@@ -333,6 +333,74 @@ void oracle_conv2d_im2col(int64_t Nb, int64_t H, int64_t W, int64_t C, int64_t K
   free(col);
 }
 
+/* ------------------------------------------------------------------------ */
+/* O8. Quantized convolution: u8 activations x i8 weights with zero points.   */
+/* It joins the two definitions above: the quantized product of [GEMM-TVM]    */
+/* §2.3, (x_q - zp_x) * (w_q - zp_w), summed over the taps of the             */
+/* convolution of [CONV-TC] "Preparation and algorithm".  The padding holds    */
+/* the real value 0, whose u8 code is zp_x (the reading taken here), so a     */
+/* padded tap contributes (zp_x - zp_x) * (w - zp_w) = 0.                     */
+/*   y[n,p,q,ko] = sum_{r,s,c} (x[n, p*sh+r-ph, q*sw+s-pw, c] - zA)           */
+/*                             * (w[ko,r,s,c] - zB)                          */
+/* over the taps inside the input.  Exact in int64.  Layouts as O6 (x NHWC     */
+/* uint8, w KRSC int8, y NHWC int64); written at a list of output pixels.      */
+/* ------------------------------------------------------------------------ */
+void oracle_conv2d_u8i8_direct_at(int64_t Nb, int64_t H, int64_t W, int64_t C, int64_t Kout,
+                                  int64_t R, int64_t S, int64_t sh, int64_t sw,
+                                  int64_t ph, int64_t pw,
+                                  const uint8_t* x, int64_t zA, const int8_t* w, int64_t zB,
+                                  const int64_t* pix, int64_t npix, int64_t* y) {
+  int64_t P = oracle_conv_out_dim(H, R, sh, ph);
+  int64_t Q = oracle_conv_out_dim(W, S, sw, pw);
+  (void)Nb;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < npix; ++i) {
+    int64_t m = pix[i];
+    int64_t n = m / (P * Q);
+    int64_t p = (m / Q) % P;
+    int64_t q = m % Q;
+    for (int64_t ko = 0; ko < Kout; ++ko) {
+      int64_t acc = 0;
+      for (int64_t r = 0; r < R; ++r) {
+        for (int64_t s = 0; s < S; ++s) {
+          int64_t h = p * sh + r - ph;
+          int64_t ww = q * sw + s - pw;
+          if (h < 0 || h >= H || ww < 0 || ww >= W) continue; /* padding: x - zA = 0 */
+          for (int64_t c = 0; c < C; ++c)
+            acc += ((int64_t)x[((n * H + h) * W + ww) * C + c] - zA) *
+                   ((int64_t)w[((ko * R + r) * S + s) * C + c] - zB);
+        }
+      }
+      y[i * Kout + ko] = acc;
+    }
+  }
+}
+
+/* Explicit u8 im2col for O8: Acol[m][(r*S + s)*C + c] is the input byte, or  */
+/* the zero point zA where the tap falls in the padding.  Followed by O2 on   */
+/* (Acol, zA) and (w, zB) it must reproduce O8.                               */
+void oracle_im2col_u8(int64_t Nb, int64_t H, int64_t W, int64_t C,
+                      int64_t R, int64_t S, int64_t sh, int64_t sw,
+                      int64_t ph, int64_t pw, const uint8_t* x, int64_t zA, uint8_t* col) {
+  int64_t P = oracle_conv_out_dim(H, R, sh, ph);
+  int64_t Q = oracle_conv_out_dim(W, S, sw, pw);
+  int64_t Kdim = R * S * C;
+  for (int64_t n = 0; n < Nb; ++n)
+    for (int64_t p = 0; p < P; ++p)
+      for (int64_t q = 0; q < Q; ++q) {
+        int64_t m = (n * P + p) * Q + q;
+        for (int64_t r = 0; r < R; ++r)
+          for (int64_t s = 0; s < S; ++s) {
+            int64_t h = p * sh + r - ph;
+            int64_t ww = q * sw + s - pw;
+            int inside = h >= 0 && h < H && ww >= 0 && ww < W;
+            for (int64_t c = 0; c < C; ++c)
+              col[m * Kdim + (r * S + s) * C + c] =
+                  inside ? x[((n * H + h) * W + ww) * C + c] : (uint8_t)zA;
+          }
+      }
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

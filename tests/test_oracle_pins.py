@@ -341,3 +341,98 @@ def test_conv_sizes_match_printed_tutorial_sizes(oracle):
     d = wl.dims
     assert (d["H"], d["W"], d["C"], d["Kout"], d["R"], d["S"]) == (
         c["height"], c["width"], c["in_channels"], c["out_channels"], c["kernel_h"], c["kernel_w"])
+
+
+# --------------------------------------------------------------------------
+# O8: quantized convolution (u8 activations x i8 weights, zero points; the
+# padding holds the zero point, i.e. the real value 0)
+# --------------------------------------------------------------------------
+QCONV_CASES = [
+    # Nb, H, W, C, Kout, R, S, stride, pad, zA, zB
+    (2, 5, 6, 3, 4, 3, 3, (1, 1), (1, 1), 128, 3),
+    (1, 7, 5, 2, 3, 3, 2, (2, 1), (1, 0), 37, -5),
+    (3, 4, 4, 5, 2, 1, 1, (1, 1), (0, 0), 0, 0),
+    (1, 6, 6, 4, 3, 5, 5, (1, 1), (2, 2), 255, 127),
+    (2, 9, 8, 3, 2, 3, 3, (2, 2), (1, 1), 100, -128),
+]
+
+
+def _qconv_inputs(rng, case):
+    Nb, H, W, C, Kout, R, S = case[:7]
+    x = synth.u8_uniform(rng, (Nb, H, W, C))
+    w = rng.integers(-128, 128, (Kout, R, S, C)).astype(np.int8)
+    return x, w
+
+
+@pytest.mark.parametrize("case", QCONV_CASES)
+def test_qconv_equals_zero_point_im2col_then_naive_gemm(oracle, case):
+    Nb, H, W, C, Kout, R, S, st, pd, zA, zB = case
+    rng = np.random.default_rng(sum(case[:7]) + zA)
+    x, w = _qconv_inputs(rng, case)
+    y = oracle.conv2d_u8i8_direct(x, zA, w, zB, st, pd)
+    col = oracle.im2col_u8(x, zA, R, S, st, pd)
+    ref = oracle.gemm_u8i8_naive(col, zA, w.reshape(Kout, R * S * C), zB)
+    assert np.array_equal(y.reshape(-1, Kout), ref)
+
+
+@pytest.mark.parametrize("case", QCONV_CASES)
+def test_qconv_vs_scipy_correlate_of_shifted_values(oracle, case):
+    # the real-valued view: (x - zA) zero-padded, correlated with (w - zB)
+    from scipy.signal import correlate2d
+
+    Nb, H, W, C, Kout, R, S, (sh, sw), (ph, pw), zA, zB = case
+    rng = np.random.default_rng(5 * sum(case[:7]) + zA)
+    x, w = _qconv_inputs(rng, case)
+    y = oracle.conv2d_u8i8_direct(x, zA, w, zB, (sh, sw), (ph, pw))
+    xd = np.pad(x.astype(np.float64) - zA, ((0, 0), (ph, ph), (pw, pw), (0, 0)))
+    wd = w.astype(np.float64) - zB
+    P, Q = y.shape[1], y.shape[2]
+    ref = np.zeros(y.shape, np.float64)
+    for n in range(Nb):
+        for k in range(Kout):
+            acc = sum(correlate2d(xd[n, :, :, c], wd[k, :, :, c], mode="valid") for c in range(C))
+            ref[n, :, :, k] = acc[::sh, ::sw][:P, :Q]
+    assert np.array_equal(y.astype(np.float64), ref)  # integers far below 2^53: exact
+
+
+def test_qconv_brute_force_python_ints(oracle):
+    Nb, H, W, C, Kout, R, S, (sh, sw), (ph, pw), zA, zB = 1, 4, 3, 2, 2, 3, 3, (1, 1), (1, 1), 77, 9
+    rng = np.random.default_rng(99)
+    x, w = _qconv_inputs(rng, (Nb, H, W, C, Kout, R, S))
+    y = oracle.conv2d_u8i8_direct(x, zA, w, zB, (sh, sw), (ph, pw))
+    for p in range(y.shape[1]):
+        for q in range(y.shape[2]):
+            for k in range(Kout):
+                acc = 0
+                for r in range(R):
+                    for s in range(S):
+                        h, ww = p * sh + r - ph, q * sw + s - pw
+                        for c in range(C):
+                            xv = int(x[0, h, ww, c]) if 0 <= h < H and 0 <= ww < W else zA
+                            acc += (xv - zA) * (int(w[k, r, s, c]) - zB)
+                assert int(y[0, p, q, k]) == acc
+
+
+def test_qconv_special_cases(oracle):
+    Nb, H, W, C, Kout, R, S = 2, 5, 4, 3, 3, 3, 3
+    rng = np.random.default_rng(31)
+    x, w = _qconv_inputs(rng, (Nb, H, W, C, Kout, R, S))
+    # activations at the zero point, or weights at theirs: exactly zero
+    assert not oracle.conv2d_u8i8_direct(np.full_like(x, 61), 61, w, 4, (1, 1), (1, 1)).any()
+    assert not oracle.conv2d_u8i8_direct(x, 61, np.full_like(w, -7), -7, (1, 1), (1, 1)).any()
+    # x - zA = 1 and w - zB = 1 everywhere: each output counts its in-image
+    # taps times C (the padded taps contribute nothing, not (0 - zA)(w - zB))
+    y = oracle.conv2d_u8i8_direct(np.full_like(x, 201), 200, np.full_like(w, -3), -4, (1, 1), (1, 1))
+    rows = np.array([min(p + 1, H - 1) - max(p - 1, 0) + 1 for p in range(H)])
+    cols = np.array([min(q + 1, W - 1) - max(q - 1, 0) + 1 for q in range(W)])
+    want = (rows[:, None] * cols[None, :] * C).astype(np.int64)
+    assert np.array_equal(y, np.broadcast_to(want[None, :, :, None], y.shape))
+    # 1x1 filter, no padding: the u8 x i8 GEMM of the pixels
+    w1 = w[:, :1, :1, :]
+    y1 = oracle.conv2d_u8i8_direct(x, 90, w1, -2, (1, 1), (0, 0))
+    ref = oracle.gemm_u8i8_naive(x.reshape(-1, C), 90, w1.reshape(Kout, C), -2)
+    assert np.array_equal(y1.reshape(-1, Kout), ref)
+    # a listed subset of pixels equals those rows of the whole output
+    pix = np.array([0, 7, 19, Nb * H * W - 1])
+    at = oracle.conv2d_u8i8_direct_at(x, 13, w, 5, pix, (1, 1), (1, 1))
+    assert np.array_equal(at, oracle.conv2d_u8i8_direct(x, 13, w, 5, (1, 1), (1, 1)).reshape(-1, Kout)[pix])
