@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     Epilogue,
     IGCError,
     conv2d_implicit_gemm,
+    conv2d_u8i8_zp,
     device_check,
     gemm_f16f32,
     gemm_u8i8_zp,

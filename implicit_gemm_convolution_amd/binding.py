@@ -28,7 +28,7 @@ IGC_EHIP = -4
 IGC_ENODEV = -5
 
 # Every symbol include/igc.h declares.
-EXPORTED = ("gemm_f16f32", "gemm_u8i8_zp", "conv2d_implicit_gemm",
+EXPORTED = ("gemm_f16f32", "gemm_u8i8_zp", "conv2d_implicit_gemm", "conv2d_u8i8_zp",
             "igc_status_string", "igc_last_error", "igc_device_check")
 
 
@@ -77,6 +77,8 @@ def load() -> ctypes.CDLL:
     L.gemm_u8i8_zp.restype = i
     L.conv2d_implicit_gemm.argtypes = [i] * 11 + [p, p, p, p]
     L.conv2d_implicit_gemm.restype = i
+    L.conv2d_u8i8_zp.argtypes = [i] * 11 + [p, i, p, i, ctypes.POINTER(Epilogue), p]
+    L.conv2d_u8i8_zp.restype = i
     L.igc_status_string.argtypes = [i]
     L.igc_status_string.restype = ctypes.c_char_p
     L.igc_last_error.argtypes = []
@@ -151,3 +153,13 @@ def conv2d_implicit_gemm(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad
     st = load().conv2d_implicit_gemm(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w,
                                      _addr(x), _addr(w), _addr(y), _stream(stream))
     return _check(st, "conv2d_implicit_gemm") if check else st
+
+
+def conv2d_u8i8_zp(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, x, zA, w, zB, *,
+                   C_i32=None, ldc=0, D_f32=None, ldd=0, dq_scale=0.0, Q_i8=None, ldq=0,
+                   scale_n=None, bias_n=None, stream=None, check=True) -> int:
+    ep = Epilogue(_addr(C_i32), ldc, _addr(D_f32), ldd, float(dq_scale), _addr(Q_i8), ldq,
+                  _addr(scale_n), _addr(bias_n))
+    st = load().conv2d_u8i8_zp(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, _addr(x), zA,
+                               _addr(w), zB, ctypes.byref(ep), _stream(stream))
+    return _check(st, "conv2d_u8i8_zp") if check else st

@@ -246,6 +246,31 @@ igc::Params zero_params() {
   return p;
 }
 
+// Validation shared by the two convolutions; fills the im2col part of p.
+int conv_params(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h, int stride_w,
+                int pad_h, int pad_w, igc::Params& p, long long* nx_out) {
+  if (Nb <= 0 || H <= 0 || W <= 0 || C <= 0 || Kout <= 0 || R <= 0 || S <= 0)
+    return fail(IGC_EINVAL, "non-positive dimension");
+  if (stride_h <= 0 || stride_w <= 0 || pad_h < 0 || pad_w < 0)
+    return fail(IGC_EINVAL, "bad stride or padding");
+  const long long P = ((long long)H + 2LL * pad_h - R) / stride_h + 1;
+  const long long Q = ((long long)W + 2LL * pad_w - S) / stride_w + 1;
+  if ((long long)H + 2LL * pad_h < R || (long long)W + 2LL * pad_w < S || P < 1 || Q < 1)
+    return fail(IGC_EINVAL, "filter larger than the padded input");
+  const long long M = (long long)Nb * P * Q;
+  const long long K = (long long)R * S * C;
+  const long long nx = (long long)Nb * H * W * C;
+  if (M > 0x7fffffffLL || K > 0x7fffffffLL || nx > 0x7fffffffLL ||
+      (long long)Kout * K > 0x7fffffffLL || M * Kout > (1LL << 62))
+    return fail(IGC_EUNSUPPORTED, "tensor index exceeds 32 bits");
+  p.M = (int)M; p.N = Kout; p.K = (int)K;
+  p.Nb = Nb; p.H = H; p.W = W; p.C = C; p.R = R; p.S = S;
+  p.sh = stride_h; p.sw = stride_w; p.ph = pad_h; p.pw = pad_w;
+  p.P = (int)P; p.Q = (int)Q;
+  *nx_out = nx;
+  return IGC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -334,38 +359,61 @@ int gemm_u8i8_zp(int M, int N, int K, const uint8_t* A, int lda, int zA, const i
   return launch<igc::KIND_U8I8_GEMM, false>(p, fast, static_cast<hipStream_t>(stream), dev);
 }
 
+int conv2d_u8i8_zp(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h, int stride_w,
+                   int pad_h, int pad_w, const uint8_t* x, int zA, const int8_t* w, int zB,
+                   const igc_u8i8_epilogue* ep, void* stream) {
+  g_last_error[0] = 0;
+  igc::Params p = zero_params();
+  long long nx = 0;
+  if (int st = conv_params(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, p, &nx)) return st;
+  if (!x || !w) return fail(IGC_EINVAL, "x or w is NULL");
+  if (zA < 0 || zA > 255) return fail(IGC_EINVAL, "zA=%d outside [0, 255]", zA);
+  if (zB < -128 || zB > 127) return fail(IGC_EINVAL, "zB=%d outside [-128, 127]", zB);
+  if (!ep) return fail(IGC_EINVAL, "epilogue descriptor is NULL");
+  if (!ep->C_i32 && !ep->D_f32 && !ep->Q_i8) return fail(IGC_EINVAL, "no output requested");
+  if (p.K > 33025) return fail(IGC_EOVERFLOW, "K=R*S*C=%d > 33025 can overflow int32", p.K);
+  const int N = Kout;
+  if (ep->C_i32 && ep->ldc < N) return fail(IGC_EINVAL, "ldc=%d < Kout=%d", ep->ldc, N);
+  if (ep->D_f32 && ep->ldd < N) return fail(IGC_EINVAL, "ldd=%d < Kout=%d", ep->ldd, N);
+  if (ep->Q_i8) {
+    if (ep->ldq < N) return fail(IGC_EINVAL, "ldq=%d < Kout=%d", ep->ldq, N);
+    if (!ep->scale_n || !ep->bias_n) return fail(IGC_EINVAL, "Q_i8 needs scale_n and bias_n");
+  }
+  int dev;
+  if (int s = check_device(&dev)) return s;
+  p.A = x; p.lda = 0;
+  p.B = reinterpret_cast<const uint8_t*>(w); p.ldb = p.K;
+  p.zAp = zA - 128; p.zB = zB;
+  p.Ci = ep->C_i32; p.ldci = ep->ldc;
+  p.D = ep->D_f32; p.ldd = ep->ldd; p.dq = ep->dq_scale;
+  p.Qo = ep->Q_i8; p.ldq = ep->ldq; p.scale = ep->scale_n; p.bias = ep->bias_n;
+  p.vec_c = aligned16(ep->C_i32) && ep->ldc % 4 == 0;
+  p.vec_d = aligned16(ep->D_f32) && ep->ldd % 4 == 0;
+  p.vec_q = (reinterpret_cast<uintptr_t>(ep->Q_i8) & 3u) == 0 && ep->ldq % 4 == 0;
+  // whole 128-channel K tiles within one tap: the uniform-tap loader
+  const bool fast = aligned16(x) && aligned16(w) && C % 128 == 0 && (long long)R * S <= 31 &&
+                    nx < (1LL << 31) && 256LL * p.K < (1LL << 31);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.zAp != 0 || p.zB != 0) return launch<igc::KIND_U8I8_CONV, true>(p, fast, st, dev);
+  return launch<igc::KIND_U8I8_CONV, false>(p, fast, st, dev);
+}
+
 int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h,
                          int stride_w, int pad_h, int pad_w, const void* x, const void* w, float* y,
                          void* stream) {
   g_last_error[0] = 0;
-  if (Nb <= 0 || H <= 0 || W <= 0 || C <= 0 || Kout <= 0 || R <= 0 || S <= 0)
-    return fail(IGC_EINVAL, "non-positive dimension");
-  if (stride_h <= 0 || stride_w <= 0 || pad_h < 0 || pad_w < 0)
-    return fail(IGC_EINVAL, "bad stride or padding");
+  igc::Params p = zero_params();
+  long long nx = 0;
+  if (int st = conv_params(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, p, &nx)) return st;
   if (!x || !w || !y) return fail(IGC_EINVAL, "x, w or y is NULL");
-  const long long P = ((long long)H + 2LL * pad_h - R) / stride_h + 1;
-  const long long Q = ((long long)W + 2LL * pad_w - S) / stride_w + 1;
-  if ((long long)H + 2LL * pad_h < R || (long long)W + 2LL * pad_w < S || P < 1 || Q < 1)
-    return fail(IGC_EINVAL, "filter larger than the padded input");
-  const long long M = (long long)Nb * P * Q;
-  const long long K = (long long)R * S * C;
-  const long long nx = (long long)Nb * H * W * C;
-  if (M > 0x7fffffffLL || K > 0x7fffffffLL || nx > 0x7fffffffLL ||
-      (long long)Kout * K > 0x7fffffffLL || M * Kout > (1LL << 62))
-    return fail(IGC_EUNSUPPORTED, "tensor index exceeds 32 bits");
   int dev;
   if (int s = check_device(&dev)) return s;
-  igc::Params p = zero_params();
-  p.M = (int)M; p.N = Kout; p.K = (int)K;
   p.A = static_cast<const uint8_t*>(x); p.lda = 0;
-  p.B = static_cast<const uint8_t*>(w); p.ldb = K;
-  p.Nb = Nb; p.H = H; p.W = W; p.C = C; p.R = R; p.S = S;
-  p.sh = stride_h; p.sw = stride_w; p.ph = pad_h; p.pw = pad_w;
-  p.P = (int)P; p.Q = (int)Q;
+  p.B = static_cast<const uint8_t*>(w); p.ldb = p.K;
   p.Cf = y; p.ldcf = Kout;
   p.vec_c = aligned16(y) && Kout % 4 == 0;
   const bool fast = aligned16(x) && aligned16(w) && C % 8 == 0 && nx * 2 < (1LL << 31) &&
-                    256LL * K * 2 < (1LL << 31);
+                    256LL * p.K * 2 < (1LL << 31);
   // whole 64-channel K tiles within one tap: the uniform-tap loader
   if (fast && C % 64 == 0 && (long long)R * S <= 31)
     return launch<igc::KIND_F16_CONV_C64, false>(p, true, static_cast<hipStream_t>(stream), dev);

@@ -77,7 +77,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // KIND_F16_CONV_C64: the convolution when C % 64 == 0 and R*S <= 31, so a
 // K tile (64 channels) never straddles two taps and the tap is uniform.
-enum Kind : int { KIND_F16_GEMM = 0, KIND_F16_CONV = 1, KIND_U8I8_GEMM = 2, KIND_F16_CONV_C64 = 3 };
+// KIND_U8I8_CONV: the quantized convolution (u8 activations x i8 weights
+// with zero points); with FAST it needs C % 128 == 0 and R*S <= 31 (uniform
+// taps of 128 channels), else the element-wise im2col loader.
+enum Kind : int {
+  KIND_F16_GEMM = 0,
+  KIND_F16_CONV = 1,
+  KIND_U8I8_GEMM = 2,
+  KIND_F16_CONV_C64 = 3,
+  KIND_U8I8_CONV = 4
+};
 
 constexpr int KT_BYTES = 128;    // bytes of K per tile row
 constexpr int CHUNK_BYTES = 16;  // one vector load
@@ -367,14 +376,18 @@ struct RowDmaLoader {
 // is decoded once per row at kernel start.  FAST (C % 8 == 0): the 8 channels
 // of a chunk share one tap (r, s); each lane tracks the (r, s, c) of its chunk
 // and advances it by the 64 channels of one K tile.
-template <int NT, int ROWS, bool FAST>
+// EB = 1 (u8 activations, element-wise only): the padding holds the zero
+// point zA, the code of the real value 0, instead of 0.
+template <int NT, int ROWS, bool FAST, int EB = 2>
 struct Im2colLoader {
+  static_assert(EB == 2 || !FAST, "u8 activations take the element-wise or the uniform-tap loader");
   typedef DmaShape<NT, ROWS> Sh;
   static constexpr int NR = FAST ? Sh::NQ : ROWS * CPR / NT;  // rows per lane
   const uint8_t* x;
   int pix[NR];  // pixel index in x of (n, p*sh - ph, q*sw - pw), i.e. of tap (0, 0)
   int hw[NR];   // (p*sh - ph) << 16 | (q*sw - pw) & 0xffff; INT32_MIN for rows past M
   int H, W, C, S, K;
+  uint8_t padv;  // u8 padding value (zA)
   Rsrc rsrc;
   // tap of this lane's chunk for the next K tile to be loaded (FAST)
   mutable int cur_r, cur_s, cur_c;
@@ -385,6 +398,7 @@ struct Im2colLoader {
   __device__ __forceinline__ void init(const Params& p, int m0, int kt0) {
     x = p.A;
     H = p.H; W = p.W; C = p.C; S = p.S; K = p.K;
+    padv = (uint8_t)(p.zAp + 128);
     if (FAST) rsrc = make_rsrc(x, (uint32_t)((long long)p.Nb * H * W * C * 2));
     const int PQ = p.P * p.Q;
 #pragma unroll
@@ -424,6 +438,18 @@ struct Im2colLoader {
     if ((unsigned)h >= (unsigned)H || (unsigned)w >= (unsigned)W) return 0;
     return reinterpret_cast<const uint16_t*>(x)[(long long)(pix[j] + r * W + s) * C + c];
   }
+  // u8: past K (and rows past M) 0, like the row operands' K tail; padding zA
+  __device__ __forceinline__ uint8_t elem8(int j, int k) const {
+    if (hw[j] == INT32_MIN || k >= K) return 0;
+    const int rs = k / C;
+    const int c = k - rs * C;
+    const int r = rs / S;
+    const int s = rs - r * S;
+    const int h = row_h(j) + r;
+    const int w = row_w(j) + s;
+    if ((unsigned)h >= (unsigned)H || (unsigned)w >= (unsigned)W) return padv;
+    return x[(long long)(pix[j] + r * W + s) * C + c];
+  }
 
   // Loading K tile kt takes NPART calls part(tile, kt, j) and then
   // advance().  FAST: K tiles must be loaded in order 0, 1, 2, ... (advance()
@@ -456,7 +482,7 @@ struct Im2colLoader {
       const bool ok = kin && (unsigned)h < (unsigned)H && (unsigned)w < (unsigned)W;
       const uint32_t off = ((uint32_t)(pix[j] + tap) * (uint32_t)C + (uint32_t)cur_c) * 2u;
       dma16(rsrc, Sh::dst(tile, j), ok ? off : OOB);
-    } else {
+    } else if constexpr (EB == 2) {
       const int c = threadIdx.x & 7;
       const int k0 = kt * 64 + c * 8;
 #pragma unroll
@@ -469,33 +495,52 @@ struct Im2colLoader {
         __builtin_memcpy(&v, e, 16);
         lds_write16(tile, swz(row, c), v);
       }
+    } else {
+      const int c = threadIdx.x & 7;
+      const int k0 = kt * 128 + c * 16;
+#pragma unroll
+      for (int j = 0; j < NR; ++j) {
+        const int row = (threadIdx.x >> 3) + j * (NT / 8);
+        uint8_t e[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) e[i] = elem8(j, k0 + i);
+        uint4 v;
+        __builtin_memcpy(&v, e, 16);
+        lds_write16(tile, swz(row, c), v);
+      }
     }
   }
 };
 
-// The implicit-im2col A operand when C % 64 == 0 and R*S <= 31 (FAST only).
-// Every K tile is 64 channels of one tap (r, s), the same for all lanes, so
-// the tap walk is scalar.  A row's input pixel is a fixed per-lane offset;
-// the tap moves the buffer descriptor's base instead (scalar arithmetic), and
-// each row keeps a bit mask of the taps that fall inside the image (the zero
-// padding), so a load costs three vector instructions: the mask bit, a
-// compare and a select of the out-of-range offset.
-template <int NT, int ROWS>
+// The implicit-im2col A operand when a K tile (128 bytes: 64 fp16 or 128 u8
+// channels) always lies in one tap: C a multiple of it and R*S <= 31 (FAST
+// only).  The tap (r, s) is then the same for all lanes, so the tap walk is
+// scalar.  A row's input pixel is a fixed per-lane offset; the tap moves the
+// buffer descriptor's base instead (scalar arithmetic), and each row keeps a
+// bit mask of the taps that fall inside the image (the zero padding), so a
+// load costs three vector instructions: the mask bit, a compare and a select
+// of the out-of-range offset.  Padded chunks land as zero bytes; for u8
+// activations fix_pad() then overwrites them with the zero point zA.
+template <int NT, int ROWS, int EB = 2>
 struct Im2colC64Loader {
   typedef DmaShape<NT, ROWS> Sh;
   static constexpr int NPART = Sh::NQ;
+  static constexpr int CPT = KT_BYTES / EB;  // channels per K tile
   const uint8_t* x;
   uint32_t bytes;       // size of x
   int C, S, W, RS;
   int p0;               // ph*W + pw: keeps the per-row offsets non-negative
-  uint32_t pixb[Sh::NQ];  // (pixel of tap (0,0) + p0) * C * 2 + chunk * 16
+  uint32_t pixb[Sh::NQ];  // (pixel of tap (0,0) + p0) * C * EB + chunk * 16
   uint32_t mask[Sh::NQ];  // bit r*S+s: tap (r, s) of this row is inside the image
   mutable int cur_r, cur_s, cur_c;  // tap and channel of the next K tile
+  mutable int fix_tap, fix_c;       // tap and channel of the next tile fix_pad() visits
+  uint32_t padv4;                   // zA in every byte
 
   __device__ __forceinline__ void init(const Params& p, int m0, int kt0) {
     x = p.A;
     C = p.C; S = p.S; W = p.W; RS = p.R * p.S;
-    bytes = (uint32_t)((long long)p.Nb * p.H * p.W * p.C * 2);
+    bytes = (uint32_t)((long long)p.Nb * p.H * p.W * p.C * EB);
+    padv4 = (uint32_t)(uint8_t)(p.zAp + 128) * 0x01010101u;
     p0 = p.ph * p.W + p.pw;
     const int PQ = p.P * p.Q;
 #pragma unroll
@@ -510,7 +555,7 @@ struct Im2colC64Loader {
         const int qq = pq - pp * p.Q;
         const int h0 = pp * p.sh - p.ph;
         const int w0 = qq * p.sw - p.pw;
-        pixb[j] = (uint32_t)((n * p.H * p.W + h0 * p.W + w0 + p0) * C * 2 + Sh::lane_chunk() * CHUNK_BYTES);
+        pixb[j] = (uint32_t)((n * p.H * p.W + h0 * p.W + w0 + p0) * C * EB + Sh::lane_chunk() * CHUNK_BYTES);
         uint32_t mk = 0;
         for (int r = 0; r < p.R; ++r)
           for (int s2 = 0; s2 < p.S; ++s2)
@@ -519,14 +564,16 @@ struct Im2colC64Loader {
         mask[j] = mk;
       }
     }
-    const int k = kt0 * 64;
+    const int k = kt0 * CPT;
     const int rs = k / C;
     cur_c = k - rs * C;
     cur_r = rs / S;
     cur_s = rs - cur_r * S;
+    fix_tap = rs;
+    fix_c = cur_c;
   }
   __device__ __forceinline__ void advance() const {
-    cur_c += 64;
+    cur_c += CPT;
     if (cur_c == C) {
       cur_c = 0;
       if (++cur_s == S) {
@@ -544,7 +591,7 @@ struct Im2colC64Loader {
     const int tap = cur_r * S + cur_s;
     // tiles past the last tap (prefetch beyond K) use bit 31, never set
     const int bit = tap < RS ? tap : 31;
-    const long long toff = ((long long)(cur_r * W + cur_s - p0) * C + cur_c) * 2;
+    const long long toff = ((long long)(cur_r * W + cur_s - p0) * C + cur_c) * EB;
     const uint64_t base = (uint64_t)(uintptr_t)x + (uint64_t)toff;
     // bytes of x past the moved base, at most 2^31 so that OOB stays out of
     // range (0 once the tap has left x: every lane then reads zeros)
@@ -554,6 +601,23 @@ struct Im2colC64Loader {
     r.d = i32x4{(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)num, 0x00020000};
     const uint32_t vo = ((mask[j] >> bit) & 1u) ? pixb[j] : OOB;
     dma16s(r, Sh::dst(tile, j), vo, 0);
+  }
+  // After this lane's loads of the next K tile (in order, one call per tile)
+  // have landed in `tile`: its padded chunks get zA.  Each lane rewrites only
+  // the LDS slots its own direct-to-LDS loads filled.  Tiles past the last
+  // tap (prefetched, never multiplied) are left alone.
+  __device__ __forceinline__ void fix_pad(uint8_t* tile) const {
+    if (fix_tap < RS) {
+      const uint4 zv = make_uint4(padv4, padv4, padv4, padv4);
+#pragma unroll
+      for (int j = 0; j < NPART; ++j)
+        if (!((mask[j] >> fix_tap) & 1u)) lds_write16(Sh::dst(tile, j), (threadIdx.x & 63) * CHUNK_BYTES, zv);
+    }
+    fix_c += CPT;
+    if (fix_c == C) {
+      fix_c = 0;
+      ++fix_tap;
+    }
   }
 };
 
@@ -583,6 +647,8 @@ template <int MB>
 struct Mfma<KIND_F16_CONV, MB> : Mfma<KIND_F16_GEMM, MB> {};
 template <int MB>
 struct Mfma<KIND_F16_CONV_C64, MB> : Mfma<KIND_F16_GEMM, MB> {};
+template <int MB>
+struct Mfma<KIND_U8I8_CONV, MB> : Mfma<KIND_U8I8_GEMM, MB> {};
 template <>
 struct Mfma<KIND_U8I8_GEMM, 32> {
   typedef i32x16 acc_t;
@@ -643,7 +709,8 @@ __device__ __forceinline__ void lds_barrier() {
 template <int KIND, int BM, int BN, int WM, int WN, bool FAST, bool SUMS = false, int DEPTH = 2>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int NT = 64 * WM * WN;
-  constexpr int EB = (KIND == KIND_U8I8_GEMM) ? 1 : 2;
+  constexpr bool INT8 = KIND == KIND_U8I8_GEMM || KIND == KIND_U8I8_CONV;
+  constexpr int EB = INT8 ? 1 : 2;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int MB = IGC_MFMA_DIM;          // MFMA output block: MB x MB
   constexpr int FM = TM / MB, FN = TN / MB;
@@ -653,16 +720,18 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // The A stage arrays also stage 32 output rows of BN fp32/int32 each in
   // the epilogue, so a tile with BM < BN allocates them at that size.
   constexpr int SA_ALLOC = SA > 32 * BN * 4 ? SA : 32 * BN * 4;
-  constexpr bool INT8 = KIND == KIND_U8I8_GEMM;
   // stream-K (shared tiles) is compiled for the fp16 kinds; the integer GEMM
   // always gets whole tiles (the host sets dp_tiles accordingly)
   constexpr bool SK = !INT8 && !SUMS;
   // (the im2col operand walks K in order, so the conv's B does too)
-  constexpr bool CONV = KIND == KIND_F16_CONV || KIND == KIND_F16_CONV_C64;
+  constexpr bool CONV = KIND == KIND_F16_CONV || KIND == KIND_F16_CONV_C64 || KIND == KIND_U8I8_CONV;
+  // u8 activations through the uniform-tap loader: padded chunks land as
+  // zeros and are rewritten with zA before the barrier that publishes a tile
+  constexpr bool PADFIX = KIND == KIND_U8I8_CONV && FAST;
   constexpr bool TAIL_FIRST = FAST && !CONV;
   typedef typename std::conditional<
-      KIND == KIND_F16_CONV_C64, Im2colC64Loader<NT, BM>,
-      typename std::conditional<KIND == KIND_F16_CONV, Im2colLoader<NT, BM, FAST>,
+      KIND == KIND_F16_CONV_C64 || PADFIX, Im2colC64Loader<NT, BM, EB>,
+      typename std::conditional<KIND == KIND_F16_CONV || KIND == KIND_U8I8_CONV, Im2colLoader<NT, BM, FAST, EB>,
                                 RowDmaLoader<NT, BM, EB, FAST, TAIL_FIRST>>::type>::type ALoader;
   static_assert(KIND != KIND_F16_CONV_C64 || FAST, "the uniform-tap conv loader needs aligned operands");
   typedef RowDmaLoader<NT, BN, EB, FAST, TAIL_FIRST> BLoader;
@@ -840,6 +909,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     lb.load(stB(D), k0 + decltype(D)::value);
   });
   wait_vmcnt_lgkm0<(DEPTH - 1) * (NLA + NLB)>();
+  if constexpr (PADFIX) {
+    la.fix_pad(stA(std::integral_constant<int, 0>()));
+    wait_vmcnt_lgkm0<(DEPTH - 1) * (NLA + NLB)>();
+  }
   lds_barrier();
 #pragma unroll
   for (int i = 0; i < FM; ++i) read_a(sa0, 0, i, fa[0][i]);
@@ -889,6 +962,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     la.advance();
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt_lgkm0<(DEPTH - 2) * (NLA + NLB) + NLA>();
+    if constexpr (PADFIX) {
+      la.fix_pad(stA(std::integral_constant<int, u + 1>()));
+      wait_vmcnt_lgkm0<(DEPTH - 2) * (NLA + NLB) + NLA>();
+    }
     lds_barrier();
     const uint8_t* As1 = stA(std::integral_constant<int, u + 1>());
     const uint8_t* Bs1 = stB(std::integral_constant<int, u + 1>());

@@ -148,6 +148,36 @@ int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S,
                          const void* x, const void* w, float* y,
                          void* stream);
 
+/*
+ * conv2d_u8i8_zp -- quantized 2-D convolution: u8 activations x i8 weights
+ * with input zero points, int32 accumulation and the same fused outputs as
+ * gemm_u8i8_zp (int32, dequantized fp32, requantized int8 per output
+ * channel).
+ *
+ * Definition: the quantized product of [GEMM-TVM] §2.3,
+ * (x_q - zp_x) * (w_q - zp_w), summed over the taps of the convolution of
+ * [CONV-TC] "Preparation and algorithm":
+ *   C[n,p,q,k] = sum_{r,s,c} (xpad[n, p*stride_h + r, q*stride_w + s, c] - zA)
+ *                            * (w[k,r,s,c] - zB)
+ * where the padding holds the real value 0, i.e. the code zA, so a padded
+ * tap contributes nothing.  Dilation 1, groups 1, cross-correlation.
+ *
+ *   x  uint8 NHWC [Nb][H][W][C], zA in [0, 255]
+ *   w  int8  KRSC [Kout][R][S][C], zB in [-128, 127]
+ *   outputs (ep, as for gemm_u8i8_zp) row-major [Nb*P*Q][Kout] = NHWC, with
+ *   the per-output-channel scale_n / bias_n indexed by k.
+ *
+ * GEMM view: M = Nb*P*Q, N = Kout, K = R*S*C (k = (r*S + s)*C + c).
+ * 16-byte aligned x and w with C a multiple of 128 and R*S <= 31 take the
+ * fast path; every other shape an element-wise one.
+ * Errors: as conv2d_implicit_gemm, plus those of gemm_u8i8_zp for zA, zB,
+ * the epilogue descriptor and K = R*S*C > 33025 (IGC_EOVERFLOW).
+ */
+int conv2d_u8i8_zp(int Nb, int H, int W, int C, int Kout, int R, int S,
+                   int stride_h, int stride_w, int pad_h, int pad_w,
+                   const uint8_t* x, int zA, const int8_t* w, int zB,
+                   const igc_u8i8_epilogue* ep, void* stream);
+
 /* Diagnostics. */
 const char* igc_status_string(int status); /* static string for a status code              */
 const char* igc_last_error(void);          /* detail of this thread's last failure, or ""  */

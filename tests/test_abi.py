@@ -32,9 +32,9 @@ def igc():
     return m
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     fns = declared_functions()
-    for name in ("gemm_f16f32", "gemm_u8i8_zp", "conv2d_implicit_gemm"):
+    for name in ("gemm_f16f32", "gemm_u8i8_zp", "conv2d_implicit_gemm", "conv2d_u8i8_zp"):
         assert name in fns
 
 
@@ -110,6 +110,30 @@ def test_conv_validation(igc):
     assert f(x=None) == E
     assert f(R=7, ph=1) == E                           # filter larger than the padded input
     assert f(Nb=1 << 20, H=1 << 10, W=1 << 10, C=8) == igc.IGC_EUNSUPPORTED
+
+
+def test_qconv_validation(igc):
+    E = igc.IGC_EINVAL
+
+    def f(Nb=1, H=4, W=4, C=128, Kout=8, R=3, S=3, sh=1, sw=1, ph=1, pw=1, x=1, zA=128, w=1, zB=0, **kw):
+        kw.setdefault("C_i32", 1)
+        kw.setdefault("ldc", Kout)
+        return igc.conv2d_u8i8_zp(Nb, H, W, C, Kout, R, S, sh, sw, ph, pw, x, zA, w, zB, check=False, **kw)
+
+    assert f(Nb=0) == E
+    assert f(sh=0) == E
+    assert f(R=7, ph=1) == E                           # filter larger than the padded input
+    assert f(x=None) == E
+    assert f(w=None) == E
+    assert f(zA=256) == E
+    assert f(zB=-129) == E
+    assert f(C_i32=None) == E                          # no output requested
+    assert f(ldc=7) == E
+    assert f(C_i32=None, Q_i8=1, ldq=8) == E           # Q without scale/bias
+    assert f(C=3670, R=3, S=3) == igc.IGC_EOVERFLOW    # K = 33030
+    assert f(Nb=1 << 20, H=1 << 10, W=1 << 10, C=8) == igc.IGC_EUNSUPPORTED
+    st = igc.load().conv2d_u8i8_zp(1, 4, 4, 128, 8, 3, 3, 1, 1, 1, 1, 1, 128, 1, 0, None, None)
+    assert st == E                                     # NULL epilogue descriptor
 
 
 def test_valid_call_without_gpu_reports_nodev(igc):

@@ -369,3 +369,75 @@ def test_streamk_random_tolerance_and_deterministic(igc, oracle, monkeypatch):
     assert np.array_equal(C1, C2)
     rows = np.array(sorted({4096, M - 1} | set(rng.integers(4096, M, 16).tolist())))
     assert fp_rel_err(C1[rows], oracle.gemm_f16(A[rows], Bt)) <= FP_TOL
+
+
+# ----------------------------------------------------------------- quantized conv
+def run_qconv(igc, x, zA, w, zB, stride, pad, outputs=("C",), scale=None, bias=None, dq=0.0):
+    import torch
+
+    Nb, H, W, C = x.shape
+    Kout, R, S, _ = w.shape
+    P = (H + 2 * pad[0] - R) // stride[0] + 1
+    Q = (W + 2 * pad[1] - S) // stride[1] + 1
+    M = Nb * P * Q
+    dx, dw = to_dev(x), to_dev(w)
+    out, kw = {}, dict(dq_scale=dq)
+    if "C" in outputs:
+        out["C"] = empty_dev((M, Kout), torch.int32)
+        kw.update(C_i32=out["C"], ldc=Kout)
+    if "D" in outputs:
+        out["D"] = empty_dev((M, Kout), torch.float32)
+        kw.update(D_f32=out["D"], ldd=Kout)
+    if "Q" in outputs:
+        out["Q"] = empty_dev((M, Kout), torch.int8)
+        dS, dBi = to_dev(scale.astype(np.float32)), to_dev(bias.astype(np.float32))
+        out["_keep"] = (dS, dBi)
+        kw.update(Q_i8=out["Q"], ldq=Kout, scale_n=dS, bias_n=dBi)
+    igc.conv2d_u8i8_zp(Nb, H, W, C, Kout, R, S, stride[0], stride[1], pad[0], pad[1], dx, zA, dw, zB, **kw)
+    return {k: to_host(v) for k, v in out.items() if not k.startswith("_")}
+
+
+QCONV_CASES = [
+    # Nb, H, W, C, Kout, R, S, stride, pad, zA, zB
+    (1, 14, 14, 256, 512, 3, 3, (1, 1), (1, 1), 100, 0),    # one image of the 256-batch shape
+    (2, 9, 11, 128, 96, 3, 3, (1, 1), (1, 1), 128, 3),      # uniform taps, zA' = 0
+    (2, 13, 10, 128, 40, 5, 5, (2, 2), (2, 2), 37, -5),
+    (1, 12, 12, 256, 64, 3, 3, (2, 1), (0, 1), 255, 127),
+    (3, 8, 8, 128, 24, 1, 1, (1, 1), (0, 0), 0, -128),
+    (2, 9, 11, 64, 96, 3, 3, (1, 1), (1, 1), 90, 2),        # C % 128 != 0: element-wise
+    (1, 7, 9, 3, 13, 3, 3, (1, 2), (1, 0), 200, -1),
+    (1, 9, 9, 128, 32, 7, 7, (1, 1), (3, 3), 17, 4),        # R*S = 49: element-wise
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("case", QCONV_CASES)
+def test_qconv_int32_bit_exact(igc, oracle, variant, case):
+    Nb, H, W, C, Kout, R, S, st, pd, zA, zB = case
+    rng = np.random.default_rng(sum(case[:7]) + zA)
+    x = synth.u8_uniform(rng, (Nb, H, W, C))
+    w = synth.i8_uniform(rng, (Kout, R, S, C))
+    got = run_qconv(igc, x, zA, w, zB, st, pd)
+    P = (H + 2 * pd[0] - R) // st[0] + 1
+    Q = (W + 2 * pd[1] - S) // st[1] + 1
+    ref = oracle.conv2d_u8i8_direct_at(x, zA, w, zB, np.arange(Nb * P * Q), st, pd)
+    assert np.array_equal(got["C"].astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("case", [QCONV_CASES[0], QCONV_CASES[2], QCONV_CASES[5]])
+def test_qconv_dequant_and_requant_bit_exact(igc, oracle, case):
+    Nb, H, W, C, Kout, R, S, st, pd, zA, zB = case
+    rng = np.random.default_rng(3 * sum(case[:7]) + zA)
+    x = synth.u8_uniform(rng, (Nb, H, W, C))
+    w = synth.i8_uniform(rng, (Kout, R, S, C))
+    # scales near 1/sigma(C), so most requantized outputs are not saturated
+    scale = (rng.uniform(0.5, 2.0, Kout) * 40.0 / (74.0 * 74.0 * np.sqrt(R * S * C))).astype(np.float32)
+    bias = rng.standard_normal(Kout).astype(np.float32)
+    got = run_qconv(igc, x, zA, w, zB, st, pd, outputs=("C", "D", "Q"), scale=scale, bias=bias,
+                    dq=float(oracle.dequant_scale(0.02, 0.01)))
+    P = (H + 2 * pd[0] - R) // st[0] + 1
+    Q = (W + 2 * pd[1] - S) // st[1] + 1
+    Cref = oracle.conv2d_u8i8_direct_at(x, zA, w, zB, np.arange(Nb * P * Q), st, pd)
+    assert np.array_equal(got["C"].astype(np.int64), Cref)
+    assert np.array_equal(got["D"], oracle.dequant(Cref, 0.02, 0.01))
+    assert np.array_equal(got["Q"], oracle.requant(Cref, scale, bias))
