@@ -44,7 +44,9 @@ PEAK_F16_TFLOPS = 2516.6
 PEAK_I8_TOPS = 5033.2
 HBM_GBPS = 8000.0
 SRC_FILES = ("implicit_gemm_convolution_amd/csrc/igc.hip",
-             "implicit_gemm_convolution_amd/csrc/igc_kernels.hpp")
+             "implicit_gemm_convolution_amd/csrc/igc_kernels.hpp",
+             "implicit_gemm_convolution_amd/csrc/igc_host.hpp",
+             "implicit_gemm_convolution_amd/csrc/igc_launch.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
@@ -64,6 +66,8 @@ def algorithmic_bytes(wl) -> int:
         return 2 * (M * K + N * K) + 4 * M * N
     if wl.kind == "conv_f16":
         return wl.arrays["x"].nbytes + wl.arrays["w"].nbytes + 4 * M * N
+    if wl.kind == "conv_u8i8":
+        return wl.arrays["x"].nbytes + wl.arrays["w"].nbytes + M * N + 8 * N
     out = 0
     for o in wl.params["outputs"]:
         out += {"C_i32": 4, "D_f32": 4, "Q_i8": 1}[o] * M * N
@@ -112,6 +116,18 @@ class Runner:
                                    kw.get("dq_scale", 0.0), a("Q_i8"), kw.get("ldq", 0),
                                    a("scale_n"), a("bias_n"))
             self.call = self._direct("gemm_u8i8_zp", M, N, K, A.data_ptr(), K, zA, B.data_ptr(), K, zB,
+                                     ctypes.byref(self.ep), self.stream)
+            self.dtype, self.peak, self.unit = "i8", PEAK_I8_TOPS, "TOPS"
+        elif wl.kind == "conv_u8i8":
+            pr = wl.params
+            x, w = t(wl.arrays["x"]), t(wl.arrays["w"])
+            S, Bi = t(wl.arrays["scale"]), t(wl.arrays["bias"])
+            Q = torch.empty((d["M"], d["N"]), dtype=torch.int8, device=dev)
+            self.keep = [x, w, S, Bi, Q]
+            self.ep = igc.Epilogue(None, 0, None, 0, 0.0, Q.data_ptr(), d["N"], S.data_ptr(), Bi.data_ptr())
+            args = (d["Nb"], d["H"], d["W"], d["C"], d["Kout"], d["R"], d["S"], d["stride_h"],
+                    d["stride_w"], d["pad_h"], d["pad_w"])
+            self.call = self._direct("conv2d_u8i8_zp", *args, x.data_ptr(), pr["zA"], w.data_ptr(), pr["zB"],
                                      ctypes.byref(self.ep), self.stream)
             self.dtype, self.peak, self.unit = "i8", PEAK_I8_TOPS, "TOPS"
         else:
@@ -196,6 +212,11 @@ def cpu_baseline(wl, budget_s: float) -> dict:
                 oracle.dequant(C, pr["sA"], pr["sB"])
             if "Q_i8" in pr["outputs"]:
                 oracle.requant(C, wl.arrays["scale"], wl.arrays["bias"])
+        elif wl.kind == "conv_u8i8":
+            pr = wl.params
+            C = oracle.conv2d_u8i8_direct_at(wl.arrays["x"], pr["zA"], wl.arrays["w"], pr["zB"], rows,
+                                             (d["stride_h"], d["stride_w"]), (d["pad_h"], d["pad_w"]))
+            oracle.requant(C, wl.arrays["scale"], wl.arrays["bias"])
         else:
             oracle.conv2d_direct_at(wl.arrays["x"], wl.arrays["w"], rows,
                                     (d["stride_h"], d["stride_w"]), (d["pad_h"], d["pad_w"]))
@@ -209,8 +230,8 @@ def cpu_baseline(wl, budget_s: float) -> dict:
     n = int(min(d["M"], max(n, n * budget_s / max(t, 1e-9))))
     t = run(n)
     ops = 2.0 * n * d["N"] * d["K"]
-    unit = "TOPS" if wl.kind == "gemm_u8i8" else "TFLOPS"
-    what = "output pixels" if wl.kind == "conv_f16" else "output rows"
+    unit = "TOPS" if wl.kind in ("gemm_u8i8", "conv_u8i8") else "TFLOPS"
+    what = "output pixels" if wl.kind.startswith("conv") else "output rows"
     return dict(value=ops / t / 1e12, unit=unit, cores=cores, kind="oracle",
                 sample=f"first {n} of {d['M']} {what} of {wl.name} (all {d['N']} columns, "
                        f"K={d['K']}), {t:.1f} s on {cores} threads",

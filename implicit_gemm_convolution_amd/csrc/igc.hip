@@ -1,6 +1,8 @@
 // igc.hip -- the C ABI of libigc.so (declared in include/igc.h): argument
-// validation, device check, kernel-variant choice and launch on the caller's
-// stream.  All arithmetic happens in the kernels of igc_kernels.hpp.
+// validation, device check, and the host state of the launches (error
+// detail, compute-unit counts, stream-K workspaces).  Variant choice and the
+// launches themselves are in igc_host.hpp, instantiated in igc_launch.hip;
+// all arithmetic happens in the kernels of igc_kernels.hpp.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -14,9 +16,8 @@
 #include <cstring>
 
 #include "../../include/igc.h"
-#include "igc_kernels.hpp"
-
-namespace {
+#include "igc_host.hpp"
+namespace igc_host {
 
 thread_local char g_last_error[512] = "";
 
@@ -30,7 +31,6 @@ int fail(int status, const char* fmt, ...) {
 }
 
 // Per-device architecture cache: 0 unknown, 1 gfx950, -1 other.
-constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];
 
 int check_device(int* dev_out) {
@@ -117,129 +117,6 @@ int sk_workspace(int dev, hipStream_t stream, size_t ws_bytes, size_t cnt_n, flo
   return IGC_OK;
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-// Tile variants.  The large tile keeps the most MFMA work per LDS byte; the
-// smaller ones exist so that small problems still spread over the 256 CUs
-// (the multi-kernel-per-shape dispatch of [GEMM-TVM] §4.3, done at run time).
-enum Variant { V_AUTO = -1, V_256x256 = 0, V_128x128 = 1, V_64x64 = 2, V_256x128 = 3, V_224x256 = 4, V_COUNT = 5 };
-
-int forced_variant() {
-  const char* s = std::getenv("IGC_FORCE_VARIANT");
-  if (!s || !*s) return V_AUTO;
-  int v = std::atoi(s);
-  return (v >= 0 && v < V_COUNT) ? v : V_AUTO;
-}
-
-long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
-
-// Large problems run on one workgroup per compute unit, in rounds of `cus`
-// tiles, so their time goes as (rounds) x (tile area).  224 x 256 tiles are
-// taken over 256 x 256 when that cost is lower: e.g. M = 50176, N = 512
-// (the 256 x 14 x 14 conv) needs 392 tiles of 256 rows, two rounds with the
-// second 53% full, but 448 tiles of 224 rows, two rounds of 7/8 the work.
-int choose_variant(int M, int N, int cus) {
-  int f = forced_variant();
-  if (f != V_AUTO) return f;
-  const long long t256 = ceil_div(M, 256) * ceil_div(N, 256);
-  if (t256 >= 192) {
-    const long long t224 = ceil_div(M, 224) * ceil_div(N, 256);
-    const long long c256 = ceil_div(t256, cus) * 256, c224 = ceil_div(t224, cus) * 224;
-    return c224 < c256 ? V_224x256 : V_256x256;
-  }
-  if (ceil_div(M, 128) * ceil_div(N, 128) >= 192) return V_128x128;
-  return V_64x64;
-}
-
-// Stream-K (shared tiles): when the 256x256 tiles do not fill the last
-// round of compute units, the whole rounds run as whole tiles and the rest
-// of the tiles' K-tile iterations are split evenly over up to one workgroup
-// per compute unit (at least 4 iterations each).  fp16 GEMM and conv only.
-// It pays only when the idle part of the last round is worth more than the
-// cost of publishing and summing the partial tiles, measured on MI355X at
-// about 26 K-tile iterations (4096^2 conv tiles: 392 tiles on 256 CUs, 36
-// iterations each, ran 12% slower split).  IGC_STREAMK=0 never splits,
-// IGC_STREAMK=2 splits whenever the last round is partial (tests).
-int streamk_mode() {
-  const char* s = std::getenv("IGC_STREAMK");
-  if (s && s[0] == '0') return 0;
-  if (s && s[0] == '2') return 2;
-  return 1;
-}
-constexpr long long kStreamKFixupIters = 26;
-
-template <int KIND, int BM, int BN, int WM, int WN, bool FAST, bool SUMS, int DEPTH = 2>
-int launch_one(igc::Params p, hipStream_t stream) {
-  p.tiles_m = (int)ceil_div(p.M, BM);
-  p.tiles_n = (int)ceil_div(p.N, BN);
-  long long grid = (long long)p.tiles_m * p.tiles_n;
-  if (grid > 0x7fffffffLL) return fail(IGC_EUNSUPPORTED, "too many tiles (%lld)", grid);
-  p.dp_tiles = (int)grid;
-  p.sk_wgs = 0;
-  p.sk_iters = 0;
-  if constexpr (BM == 256 && BN == 256 && FAST && !SUMS && KIND != igc::KIND_U8I8_GEMM) {
-    int dev = 0;
-    const int mode = streamk_mode();
-    if (mode && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
-      const long long cus = device_cus(dev);
-      const long long nk = ceil_div((long long)p.K * 2, igc::KT_BYTES);
-      // iterations the last round leaves idle, per compute unit
-      const long long idle = (cus - grid % cus) * nk / cus;
-      if (grid > cus && grid % cus != 0 && nk >= 4 && (mode == 2 || idle > kStreamKFixupIters)) {
-        const long long dp = grid / cus * cus;
-        const long long iters = (grid - dp) * nk;
-        const long long wgs = std::min(cus, std::max(1LL, iters / 4));
-        float* ws = nullptr;
-        int* cnt = nullptr;
-        if (int st = sk_workspace(dev, stream, (size_t)(2 * wgs * BM * BN * 4), (size_t)(grid - dp), &ws, &cnt))
-          return st;
-        p.dp_tiles = (int)dp;
-        p.sk_wgs = (int)wgs;
-        p.sk_iters = iters;
-        p.ws = ws;
-        p.cnt = cnt;
-        grid = dp + wgs;
-      }
-    }
-  }
-  hipLaunchKernelGGL((igc::gemm_kernel<KIND, BM, BN, WM, WN, FAST, SUMS, DEPTH>), dim3((unsigned)grid),
-                     dim3(64 * WM * WN), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return IGC_OK;
-}
-
-template <int KIND, bool FAST, bool SUMS>
-int launch_variant(int v, const igc::Params& p, hipStream_t stream) {
-  switch (v) {
-    case V_224x256:
-      if constexpr (FAST) return launch_one<KIND, 224, 256, 2, 2, FAST, SUMS>(p, stream);
-      [[fallthrough]];
-    case V_256x256:
-      if constexpr (FAST) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, stream);
-      [[fallthrough]];
-    case V_256x128:
-      if constexpr (FAST) return launch_one<KIND, 256, 128, 2, 2, FAST, SUMS>(p, stream);
-      [[fallthrough]];
-    case V_128x128: return launch_one<KIND, 128, 128, 2, 2, FAST, SUMS>(p, stream);
-    default: return launch_one<KIND, 64, 64, 2, 2, FAST, SUMS>(p, stream);
-  }
-}
-
-template <int KIND, bool SUMS>
-int launch(const igc::Params& p, bool fast, hipStream_t stream, int dev) {
-  const int cus = device_cus(dev);
-  int v = choose_variant(p.M, p.N, cus);
-  // The element-wise (unaligned) loaders need more registers; they stop at 128x128.
-  if (!fast && (v == V_256x256 || v == V_256x128 || v == V_224x256)) v = V_128x128;
-  if constexpr (KIND == igc::KIND_F16_CONV_C64) {
-    return launch_variant<KIND, true, SUMS>(v, p, stream);  // dispatched only with aligned operands
-  } else {
-    return fast ? launch_variant<KIND, true, SUMS>(v, p, stream)
-                : launch_variant<KIND, false, SUMS>(v, p, stream);
-  }
-}
-
 igc::Params zero_params() {
   igc::Params p;
   std::memset(&p, 0, sizeof(p));
@@ -271,7 +148,22 @@ int conv_params(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_
   return IGC_OK;
 }
 
-}  // namespace
+// The zero-point sums are compiled only into the kernels that need them:
+// rowsum(A') when zB != 0, colsum(B) when zA != 128.
+template <int KIND>
+int launch_u8i8(const igc::Params& p, bool fast, hipStream_t stream, int dev) {
+  const int sums = (p.zB != 0 ? igc::SUM_ROWS : 0) | (p.zAp != 0 ? igc::SUM_COLS : 0);
+  switch (sums) {
+    case 0: return launch<KIND, 0>(p, fast, stream, dev);
+    case 1: return launch<KIND, 1>(p, fast, stream, dev);
+    case 2: return launch<KIND, 2>(p, fast, stream, dev);
+    default: return launch<KIND, 3>(p, fast, stream, dev);
+  }
+}
+
+}  // namespace igc_host
+
+using namespace igc_host;
 
 extern "C" {
 
@@ -315,7 +207,7 @@ int gemm_f16f32(int M, int N, int K, const void* A, int lda, const void* B, int 
   // Buffer descriptors of the fast path cover one tile of rows and must stay below 2^31 bytes.
   const bool fast = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 &&
                     256LL * lda * 2 < (1LL << 31) && 256LL * ldb * 2 < (1LL << 31);
-  return launch<igc::KIND_F16_GEMM, false>(p, fast, static_cast<hipStream_t>(stream), dev);
+  return launch<igc::KIND_F16_GEMM, 0>(p, fast, static_cast<hipStream_t>(stream), dev);
 }
 
 int gemm_u8i8_zp(int M, int N, int K, const uint8_t* A, int lda, int zA, const int8_t* B, int ldb,
@@ -353,10 +245,7 @@ int gemm_u8i8_zp(int M, int N, int K, const uint8_t* A, int lda, int zA, const i
   p.vec_q = (reinterpret_cast<uintptr_t>(ep->Q_i8) & 3u) == 0 && ep->ldq % 4 == 0;
   const bool fast = aligned16(A) && aligned16(B) && lda % 16 == 0 && ldb % 16 == 0 &&
                     K % 16 == 0 && 256LL * lda < (1LL << 31) && 256LL * ldb < (1LL << 31);
-  // The zero-point sums are compiled only into the kernels that need them.
-  if (p.zAp != 0 || p.zB != 0)
-    return launch<igc::KIND_U8I8_GEMM, true>(p, fast, static_cast<hipStream_t>(stream), dev);
-  return launch<igc::KIND_U8I8_GEMM, false>(p, fast, static_cast<hipStream_t>(stream), dev);
+  return launch_u8i8<igc::KIND_U8I8_GEMM>(p, fast, static_cast<hipStream_t>(stream), dev);
 }
 
 int conv2d_u8i8_zp(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h, int stride_w,
@@ -394,8 +283,7 @@ int conv2d_u8i8_zp(int Nb, int H, int W, int C, int Kout, int R, int S, int stri
   const bool fast = aligned16(x) && aligned16(w) && C % 128 == 0 && (long long)R * S <= 31 &&
                     nx < (1LL << 31) && 256LL * p.K < (1LL << 31);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (p.zAp != 0 || p.zB != 0) return launch<igc::KIND_U8I8_CONV, true>(p, fast, st, dev);
-  return launch<igc::KIND_U8I8_CONV, false>(p, fast, st, dev);
+  return launch_u8i8<igc::KIND_U8I8_CONV>(p, fast, st, dev);
 }
 
 int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h,
@@ -416,8 +304,8 @@ int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, in
                     256LL * p.K * 2 < (1LL << 31);
   // whole 64-channel K tiles within one tap: the uniform-tap loader
   if (fast && C % 64 == 0 && (long long)R * S <= 31)
-    return launch<igc::KIND_F16_CONV_C64, false>(p, true, static_cast<hipStream_t>(stream), dev);
-  return launch<igc::KIND_F16_CONV, false>(p, fast, static_cast<hipStream_t>(stream), dev);
+    return launch<igc::KIND_F16_CONV_C64, 0>(p, true, static_cast<hipStream_t>(stream), dev);
+  return launch<igc::KIND_F16_CONV, 0>(p, fast, static_cast<hipStream_t>(stream), dev);
 }
 
 }  // extern "C"

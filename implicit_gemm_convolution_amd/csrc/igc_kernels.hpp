@@ -697,8 +697,9 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---------------------------------------------------------------------------
 // The kernel.
-//  SUMS (u8 x i8 only): accumulate rowsum(A') / colsum(B) for the zero-point
-//  correction; not compiled when zA == 128 and zB == 0.
+//  SUMS (u8 x i8 only): the zero-point sums the mainloop accumulates, a mask
+//  of SUM_ROWS (rowsum(A'), needed when zB != 0) and SUM_COLS (colsum(B),
+//  needed when zA != 128); each is compiled only into the kernels that use it.
 //  DEPTH: K tiles in flight ahead of the one being multiplied.  A has
 //  DEPTH + 1 LDS stages; B has 2 at DEPTH 2 (the 160 KiB of LDS at 256 x 256)
 //  and DEPTH + 1 otherwise.  Every launch uses DEPTH 2: deeper rings for the
@@ -706,7 +707,8 @@ __device__ __forceinline__ void lds_barrier() {
 //  MI355X, whose small launches are bound by fixed costs and a low clock,
 //  not by load latency.
 // ---------------------------------------------------------------------------
-template <int KIND, int BM, int BN, int WM, int WN, bool FAST, bool SUMS = false, int DEPTH = 2>
+constexpr int SUM_ROWS = 1, SUM_COLS = 2;
+template <int KIND, int BM, int BN, int WM, int WN, bool FAST, int SUMS = 0, int DEPTH = 2>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int NT = 64 * WM * WN;
   constexpr bool INT8 = KIND == KIND_U8I8_GEMM || KIND == KIND_U8I8_CONV;
@@ -722,7 +724,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int SA_ALLOC = SA > 32 * BN * 4 ? SA : 32 * BN * 4;
   // stream-K (shared tiles) is compiled for the fp16 kinds; the integer GEMM
   // always gets whole tiles (the host sets dp_tiles accordingly)
-  constexpr bool SK = !INT8 && !SUMS;
+  constexpr bool SK = !INT8 && SUMS == 0;
   // (the im2col operand walks K in order, so the conv's B does too)
   constexpr bool CONV = KIND == KIND_F16_CONV || KIND == KIND_F16_CONV_C64 || KIND == KIND_U8I8_CONV;
   // u8 activations through the uniform-tap loader: padded chunks land as
@@ -821,8 +823,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   for (int i = 0; i < FM; ++i) rsum[i] = 0;
 #pragma unroll
   for (int j = 0; j < FN; ++j) csum[j] = 0;
-  const bool want_rsum = SUMS && p.zB != 0 && wn == 0;
-  const bool want_csum = SUMS && p.zAp != 0 && wm == 0;
+  const bool want_rsum = (SUMS & SUM_ROWS) && p.zB != 0 && wn == 0;
+  const bool want_csum = (SUMS & SUM_COLS) && p.zAp != 0 && wm == 0;
 
   // Fragments, double-buffered in registers: lane l reads row l % MB of its
   // MB-row block, 16-byte chunk LPR * ks + l / MB (a k-step is 16 * LPR bytes
@@ -878,14 +880,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     }
 #pragma unroll
     for (int j = 1; j < FN; ++j) Mfma<KIND, MB>::run(acc[c][j], ac, b[j]);
-    if constexpr (SUMS) {
-      rsum[c] = sum_bytes(ac, rsum[c]);
+    if constexpr ((SUMS & SUM_ROWS) != 0) rsum[c] = sum_bytes(ac, rsum[c]);
+    if constexpr ((SUMS & SUM_COLS) != 0) {
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         if (j * FM / FN == c) csum[j] = sum_bytes(b[j], csum[j]);
     }
     // between the MFMAs: the reads first, then the vector ALU work
-    constexpr int NV = (INT8 ? 4 : 0) + (SUMS ? 8 : 0);
+    constexpr int NV = (INT8 ? 4 : 0) + ((SUMS & SUM_ROWS) ? 4 : 0) + ((SUMS & SUM_COLS) ? 4 * ((FN + FM - 1) / FM) : 0);
     int nv = 0;
 #pragma unroll
     for (int q = 1; q < FN; ++q) {
@@ -1024,7 +1026,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   };
 
   uint32_t kzz = 0;
-  if constexpr (SUMS) {
+  if constexpr (SUMS != 0) {
     // Complete the row / column sums (the K parts of one row live in lanes
     // l, l + MB, ...) and publish them through LDS.
     auto lane_total = [&](int v) {
@@ -1113,13 +1115,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           // C = acc' - zA'*colsum(B) - zB*rowsum(A') + K*zA'*zB in wrapping
           // 32-bit arithmetic; the true value fits in int32 (K <= 33025).
           uint32_t rcorr = 0;
-          if constexpr (SUMS) rcorr = p.zB != 0 ? (uint32_t)p.zB * (uint32_t)sums[lrow] : 0u;
+          if constexpr ((SUMS & SUM_ROWS) != 0) rcorr = p.zB != 0 ? (uint32_t)p.zB * (uint32_t)sums[lrow] : 0u;
           const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
           int32_t c[4];
   #pragma unroll
           for (int q = 0; q < 4; ++q) {
             uint32_t ccorr = 0;
-            if constexpr (SUMS)
+            if constexpr ((SUMS & SUM_COLS) != 0)
               ccorr = p.zAp != 0 ? (uint32_t)p.zAp * (uint32_t)sums[BM + min(lcol + q, BN - 1)] : 0u;
             c[q] = (int32_t)(vv[q] - ccorr - rcorr + kzz);
           }

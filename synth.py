@@ -17,6 +17,12 @@ to binary16 (round to nearest even).
       x ~ N(0, 1), w ~ N(0, 0.05^2)
   c5  u8 x i8 GEMM 8192^3, A ~ U{0..255} (zA=128), B ~ U{-127..127} (zB=0),
       per-channel scale ~ U[0.001, 0.01], bias ~ N(0, 1), int8 requantized out
+
+and one more, the quantized convolution (seed 104):
+
+  q4  u8 x i8 conv2d with the shape of c4 (NHWC 256x14x14x256, KRSC
+      512x3x3x256, stride 1, pad 1), x ~ U{0..255} (zA=100), w ~ U{-127..127}
+      (zB=0), per-channel scale ~ U[0.001, 0.01], bias ~ N(0, 1), int8 out
 """
 from __future__ import annotations
 
@@ -51,7 +57,7 @@ def i8_uniform(rng: np.random.Generator, shape, lo=-127, hi=127) -> np.ndarray:
 @dataclass
 class Workload:
     name: str
-    kind: str  # "gemm_f16", "gemm_u8i8", "conv_f16"
+    kind: str  # "gemm_f16", "gemm_u8i8", "conv_f16", "conv_u8i8"
     dims: dict
     arrays: dict = field(default_factory=dict)
     params: dict = field(default_factory=dict)
@@ -69,6 +75,8 @@ DESCRIPTIONS = {
     "c4": "conv2d_implicit_gemm NHWC 256x14x14x256 * KRSC 512x3x3x256, s1 p1, fp16 in, fp32 out "
           "(GEMM M=50176 N=512 K=2304)",
     "c5": "gemm_u8i8_zp M=N=K=8192, zA=128 zB=0, per-channel scale+bias, RNE int8 requant",
+    "q4": "conv2d_u8i8_zp NHWC 256x14x14x256 u8 (zA=100) * KRSC 512x3x3x256 i8 (zB=0), s1 p1, "
+          "per-channel scale+bias, RNE int8 requant (GEMM M=50176 N=512 K=2304)",
 }
 
 
@@ -79,7 +87,7 @@ def workload(name: str, *, scale_down: int = 1) -> Workload:
     factor while keeping the distribution; it is used only by tests that need
     a small member of the same family.
     """
-    seed = int(name[1:])
+    seed = int(name[1:]) + (100 if name[0] == "q" else 0)
     rng = np.random.default_rng(seed)
     if name == "c1":
         n = 256 // scale_down
@@ -113,7 +121,18 @@ def workload(name: str, *, scale_down: int = 1) -> Workload:
         bias = rng.standard_normal(size=n).astype(np.float32)
         return Workload(name, "gemm_u8i8", dict(M=n, N=n, K=n), dict(A=A, Bt=Bt, scale=scale, bias=bias),
                         dict(zA=128, zB=0, outputs=("Q_i8",)))
+    if name == "q4":
+        nb = 256 // scale_down
+        x = u8_uniform(rng, (nb, 14, 14, 256))
+        w = i8_uniform(rng, (512, 3, 3, 256))
+        scale = rng.uniform(0.001, 0.01, size=512).astype(np.float32)
+        bias = rng.standard_normal(size=512).astype(np.float32)
+        conv = dict(Nb=nb, H=14, W=14, C=256, Kout=512, R=3, S=3,
+                    stride_h=1, stride_w=1, pad_h=1, pad_w=1)
+        dims = dict(M=nb * 14 * 14, N=512, K=9 * 256, **conv)
+        return Workload(name, "conv_u8i8", dims, dict(x=x, w=w, scale=scale, bias=bias),
+                        dict(zA=100, zB=0, outputs=("Q_i8",)))
     raise KeyError(name)
 
 
-WORKLOADS = ("c1", "c2", "c3", "c4", "c5")
+WORKLOADS = ("c1", "c2", "c3", "c4", "c5", "q4")

@@ -138,3 +138,28 @@ def test_c4_sampled_pixels(igc, oracle, monkeypatch, variant, streamk):
     err = fp_rel_err(y, ref)
     print(f"c4 sampled pixels {len(pix)}: max rel err {err:.3e}")
     assert err <= FP_TOL
+
+
+def test_q4_sampled_pixels(igc, oracle):
+    """The quantized convolution at the 256x14x14 conv shape, requantized int8,
+    bit-exact on sampled output pixels (borders and interior of several images)."""
+    import torch
+
+    wl = synth.workload("q4")
+    d, pr = wl.dims, wl.params
+    x, w = wl.arrays["x"], wl.arrays["w"]
+    scale, bias = wl.arrays["scale"], wl.arrays["bias"]
+    M, N = d["M"], d["N"]
+    dQ = empty_dev((M, N), torch.int8)
+    dS, dBi = to_dev(scale), to_dev(bias)
+    dx, dw = to_dev(x), to_dev(w)
+    igc.conv2d_u8i8_zp(d["Nb"], d["H"], d["W"], d["C"], d["Kout"], d["R"], d["S"], d["stride_h"],
+                       d["stride_w"], d["pad_h"], d["pad_w"], dx, pr["zA"], dw, pr["zB"],
+                       Q_i8=dQ, ldq=N, scale_n=dS, bias_n=dBi)
+    rng = np.random.default_rng(45)
+    pix = {0, 13, 14, 195, 196, 223, 224, 255, 256, M - 1, M - 196, M - 224, 14 * 14 * 128 + 7 * 14 + 7}
+    pix |= set(rng.integers(0, M, 40).tolist())
+    pix = np.array(sorted(pix))
+    Q = to_host(dQ[pix.tolist()])
+    C = oracle.conv2d_u8i8_direct_at(x, pr["zA"], w, pr["zB"], pix, (1, 1), (1, 1))
+    assert np.array_equal(Q, oracle.requant(C, scale, bias))

@@ -32,8 +32,11 @@ def asm(tmp_path_factory):
     return kernels
 
 
+INT_KINDS = (2, 4)  # u8 x i8 GEMM and convolution
+
+
 def _params(demangled):
-    m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (true|false), (true|false), (\d+)>", demangled)
+    m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), (true|false), (\d+), (\d+)>", demangled)
     assert m, demangled
     kind, bm, bn, wm, wn = (int(m.group(i)) for i in range(1, 6))
     return kind, bm, bn, m.group(6) == "true"
@@ -44,7 +47,7 @@ def test_every_kernel_uses_mfma_of_its_dtype(asm):
         kind, bm, bn, fast = _params(name)
         # 16 x 16 output blocks: on MI355X they sustain a higher clock than the
         # 32 x 32 forms within the power limit
-        want = "v_mfma_i32_16x16x64_i8" if kind == 2 else "v_mfma_f32_16x16x32_f16"
+        want = "v_mfma_i32_16x16x64_i8" if kind in INT_KINDS else "v_mfma_f32_16x16x32_f16"
         assert want in body, name
         others = {"v_mfma_f32_16x16x32_f16", "v_mfma_i32_16x16x64_i8",
                   "v_mfma_f32_32x32x16_f16", "v_mfma_i32_32x32x32_i8"} - {want}
@@ -75,7 +78,7 @@ def test_no_packed_fp32_and_no_fma_in_epilogue_math(asm):
     for name, (body, _) in asm.items():
         assert "v_pk_add_f32" not in body and "v_pk_mul_f32" not in body and "v_pk_fma_f32" not in body
         kind, *_ = _params(name)
-        if kind == 2:  # requantize: two separately rounded operations
+        if kind in INT_KINDS:  # requantize: two separately rounded operations
             # (the epilogue follows the last MFMA; integer division lowering
             # elsewhere may use fused ops of its own)
             epi = body[body.rfind("v_mfma"):]
