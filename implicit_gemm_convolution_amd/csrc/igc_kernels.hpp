@@ -855,7 +855,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
                    auto issue) {
     __builtin_amdgcn_sched_barrier(0);
     const uint4 ac = INT8 ? ax : a[c];
-    Mfma<KIND, MB>::run(acc[c][0], ac, b[0]);
+    // B's fragment goes in the instruction's first operand slot and A's in
+    // the second: the block comes out transposed, so each lane holds 4
+    // consecutive columns of one row (see the epilogue).
+    Mfma<KIND, MB>::run(acc[c][0], b[0], ac);
     __builtin_amdgcn_sched_barrier(0);
     issue();
     __builtin_amdgcn_sched_barrier(0);
@@ -879,7 +882,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       axn.w ^= 0x80808080u;
     }
 #pragma unroll
-    for (int j = 1; j < FN; ++j) Mfma<KIND, MB>::run(acc[c][j], ac, b[j]);
+    for (int j = 1; j < FN; ++j) Mfma<KIND, MB>::run(acc[c][j], b[j], ac);
     if constexpr ((SUMS & SUM_ROWS) != 0) rsum[c] = sum_bytes(ac, rsum[c]);
     if constexpr ((SUMS & SUM_COLS) != 0) {
 #pragma unroll
@@ -995,19 +998,32 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   lds_barrier();
 
   // ------------------------------------------------------------------ epilogue
-  // The accumulators are staged through LDS one wave-row at a time (TM rows;
-  // rows 32i..32i+31 in stage array i, BN*4 bytes per row, 16-byte chunk q
-  // in slot q ^ (8 * ((row >> 2) & 1)) so that the two row groups written by
-  // one staging store land in different bank halves).  Then every thread
-  // takes 4 consecutive columns of a row: the int8 corrections and
-  // quantization run element-wise on them, and results leave in 16-byte
-  // (fp32/int32) or 4-byte (int8) stores.
+  // Accumulator layout of an output block (the MFMA computes it transposed,
+  // B x A): lane l holds row l % MB and, in register e, column
+  // acc_col(e) = 4*(l/16) + e of a 16 x 16 block, or 8*(e/4) + 4*(l/32) + e%4
+  // of a 32 x 32 block: every 4 registers are 4 consecutive columns, staged
+  // with one 16-byte LDS store.
   //
-  // Accumulator layout of an MFMA output block: lane l holds column l % MB
-  // and, in register e, row 4*(l/16) + e of a 16 x 16 block, or row
-  // 8*(e/4) + 4*(l/32) + e%4 of a 32 x 32 block.
-  const int ccol = lane % MB;
-  auto acc_row = [&](int e) { return MB == 16 ? 4 * (lane >> 4) + e : 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); };
+  // The accumulators are staged through LDS one wave-row at a time (TM rows;
+  // rows 32i..32i+31 in stage array i, BN*4 bytes per row, the 16-byte chunk
+  // q of row r in slot q ^ (r % 16), so the 16 rows of one staging store hit
+  // distinct banks).  Then every thread takes 4 consecutive columns of a
+  // row: the int8 corrections and quantization run element-wise on them, and
+  // a wave's stores cover whole rows, 16 bytes (fp32/int32) or 4 (int8) per
+  // thread.  (Storing straight from the registers instead -- 16 rows x 16-64
+  // bytes per store instruction -- measured slower on MI355X: 8192^2 int8
+  // requantize 449 -> 508 us.)
+  const int arow = lane % MB;
+  auto acc_col = [&](int e) { return MB == 16 ? 4 * (lane >> 4) + e : 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); };
+  // registers 4*g4 .. 4*g4+3 of block (i, j) as raw bits (each element is
+  // copied out first: bit-casting a vector-element lvalue directly reads
+  // element 0 with this compiler)
+  auto acc_quad = [&](int i, int j, int g4) {
+    const auto v0 = acc[i][j][4 * g4], v1 = acc[i][j][4 * g4 + 1];
+    const auto v2 = acc[i][j][4 * g4 + 2], v3 = acc[i][j][4 * g4 + 3];
+    return make_uint4(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                      __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3));
+  };
   // Staging arrays for 32-row blocks: the three A stages and the first B
   // stage (each holds 32 x BN x 4 bytes since BN <= BM); the zero-point sums
   // go to the second B stage.
@@ -1018,11 +1034,12 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
                 "staging and sums fit in the stages");
   int* const sums = reinterpret_cast<int*>(sb1);
   // rl: row within a 32-row array; c: column.  The 16-byte chunk index is
-  // XOR-ed with a function of the row so that the row groups written by one
-  // staging store (2 of 32 columns, or 4 of 16) land on disjoint banks.
+  // XOR-ed with rl % 16 (within its aligned group of 16 chunks, BN >= 64), so
+  // a staging store (16 rows, one chunk column each) is free of bank
+  // conflicts and a row read is a permutation of its chunks.
+  static_assert(BN >= 64, "chunk swizzle within groups of 16");
   auto stage_off = [](int rl, int c) {
-    const int x = MB == 16 ? 4 * ((rl >> 2) & 3) : 8 * ((rl >> 2) & 1);
-    return rl * (BN * 4) + (((c >> 2) ^ x) << 4) + (c & 3) * 4;
+    return rl * (BN * 4) + (((c >> 2) ^ (rl & 15)) << 4) + (c & 3) * 4;
   };
 
   uint32_t kzz = 0;
@@ -1185,12 +1202,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int e = 0; e < NE; ++e) {
-            // copy the element out first: bit-casting a vector-element lvalue
-            // directly reads element 0 with this compiler
-            const auto val = acc[i][j][e];
-            const int off = stage_off((i * MB) % 32 + acc_row(e), wn * TN + j * MB + ccol);
-            *reinterpret_cast<int32_t*>(arr + off) = __builtin_bit_cast(int32_t, val);
+          for (int g4 = 0; g4 < NE / 4; ++g4) {
+            const int off = stage_off((i * MB) % 32 + arow, wn * TN + j * MB + acc_col(4 * g4));
+            lds_write16(arr, off, acc_quad(i, j, g4));
           }
       }
     }
