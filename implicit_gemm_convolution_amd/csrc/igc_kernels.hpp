@@ -823,6 +823,31 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   for (int i = 0; i < FM; ++i) rsum[i] = 0;
 #pragma unroll
   for (int j = 0; j < FN; ++j) csum[j] = 0;
+  // With 16 x 16 blocks the sums run on the matrix cores instead: onehot[j]
+  // is a fragment of ones in row j (the lanes with l % 16 == j) and zeros
+  // elsewhere.  MFMA(B block j, onehot[j]) adds colsum(B block j) into
+  // column j of one shared 16 x 16 accumulator (cacc), MFMA(onehot[i],
+  // A' block i) adds rowsum(A' block i) into row i of another (racc); every
+  // other entry gets zeros, so one accumulator holds all the blocks' sums.
+  // One MFMA per block and k-step: 1/FN more matrix work per sum, where the
+  // v_dot4 form cost over a third of the main loop's time.  The two extra
+  // accumulators must fit beside the tile's in the 256 accumulator
+  // registers: at 256 x 256 (all 256 taken) the sums stay on v_dot4.
+  constexpr bool MSUMS = SUMS != 0 && MB == 16 && FM <= 16 && FN <= 16 && FM * FN * NE + 2 * NE <= 256;
+  acc_t racc, cacc;
+  uint4 onehot[MSUMS ? (FM > FN ? FM : FN) : 1];
+  if constexpr (MSUMS) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      racc[e] = 0;
+      cacc[e] = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < (FM > FN ? FM : FN); ++j) {
+      const uint32_t v = (lane & 15) == j ? 0x01010101u : 0u;
+      onehot[j] = make_uint4(v, v, v, v);
+    }
+  }
   const bool want_rsum = (SUMS & SUM_ROWS) && p.zB != 0 && wn == 0;
   const bool want_csum = (SUMS & SUM_COLS) && p.zAp != 0 && wm == 0;
 
@@ -883,14 +908,24 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     }
 #pragma unroll
     for (int j = 1; j < FN; ++j) Mfma<KIND, MB>::run(acc[c][j], b[j], ac);
-    if constexpr ((SUMS & SUM_ROWS) != 0) rsum[c] = sum_bytes(ac, rsum[c]);
-    if constexpr ((SUMS & SUM_COLS) != 0) {
+    if constexpr (MSUMS) {
+      if constexpr ((SUMS & SUM_ROWS) != 0) Mfma<KIND, MB>::run(racc, onehot[c], ac);
+      if constexpr ((SUMS & SUM_COLS) != 0) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        if (j * FM / FN == c) csum[j] = sum_bytes(b[j], csum[j]);
+        for (int j = 0; j < FN; ++j)
+          if (j * FM / FN == c) Mfma<KIND, MB>::run(cacc, b[j], onehot[j]);
+      }
+    } else {
+      if constexpr ((SUMS & SUM_ROWS) != 0) rsum[c] = sum_bytes(ac, rsum[c]);
+      if constexpr ((SUMS & SUM_COLS) != 0) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (j * FM / FN == c) csum[j] = sum_bytes(b[j], csum[j]);
+      }
     }
     // between the MFMAs: the reads first, then the vector ALU work
-    constexpr int NV = (INT8 ? 4 : 0) + ((SUMS & SUM_ROWS) ? 4 : 0) + ((SUMS & SUM_COLS) ? 4 * ((FN + FM - 1) / FM) : 0);
+    constexpr int NV = (INT8 ? 4 : 0) + ((!MSUMS && (SUMS & SUM_ROWS)) ? 4 : 0) +
+                       ((!MSUMS && (SUMS & SUM_COLS)) ? 4 * ((FN + FM - 1) / FM) : 0);
     int nv = 0;
 #pragma unroll
     for (int q = 1; q < FN; ++q) {
@@ -1051,21 +1086,42 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       if constexpr (MB == 16) v += __shfl_xor(v, 16);
       return v;
     };
-    if (want_rsum) {
-      // K-tail padding loads as byte 0 and is stored as A' = -128: add those
-      // terms back.
-      const int pad_fix = 128 * (nk * KT_BYTES - p.K);
+    // K-tail padding loads as byte 0 and is stored as A' = -128: add those
+    // terms back.
+    const int pad_fix = 128 * (nk * KT_BYTES - p.K);
+    if constexpr (MSUMS) {
+      // racc: lane l, register e holds the sum of row l % 16 of A' block
+      // 4*(l/16) + e; cacc: lane l (l % 16 = j < FN), register e holds the
+      // sum of column 4*(l/16) + e of B block j.
+      if (want_rsum) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int t = lane_total(rsum[i]) + pad_fix;
-        if (lane < MB) sums[wm * TM + i * MB + lane] = t;
+        for (int e = 0; e < NE; ++e) {
+          const int i = 4 * (lane >> 4) + e;
+          const int v = racc[e];
+          if (i < FM) sums[wm * TM + i * MB + (lane & 15)] = v + pad_fix;
+        }
       }
-    }
-    if (want_csum) {
+      if (want_csum && (lane & 15) < FN) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int t = lane_total(csum[j]);
-        if (lane < MB) sums[BM + wn * TN + j * MB + lane] = t;
+        for (int e = 0; e < NE; ++e) {
+          const int v = cacc[e];
+          sums[BM + wn * TN + (lane & 15) * MB + 4 * (lane >> 4) + e] = v;
+        }
+      }
+    } else {
+      if (want_rsum) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int t = lane_total(rsum[i]) + pad_fix;
+          if (lane < MB) sums[wm * TM + i * MB + lane] = t;
+        }
+      }
+      if (want_csum) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int t = lane_total(csum[j]);
+          if (lane < MB) sums[BM + wn * TN + j * MB + lane] = t;
+        }
       }
     }
   }
