@@ -83,3 +83,22 @@ def test_no_packed_fp32_and_no_fma_in_epilogue_math(asm):
             # elsewhere may use fused ops of its own)
             epi = body[body.rfind("v_mfma"):]
             assert "v_fma_f32" not in epi and "v_fmac_f32" not in epi and "v_fmamk_f32" not in epi, name
+
+
+def test_zero_point_sums_on_matrix_cores_where_accumulators_fit(asm):
+    # u8 x i8 kernels with zero-point sums: one extra MFMA per block and
+    # k-step (a fragment of ones), no v_dot4, except at 256x256 where the
+    # tile's accumulators fill all 256 accumulator registers.
+    seen = 0
+    for name, (body, _) in asm.items():
+        m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+), \d+, \d+, (true|false), (\d+), \d+>", name)
+        kind, bm, bn, sums = int(m.group(1)), int(m.group(2)), int(m.group(3)), int(m.group(5))
+        if kind not in INT_KINDS or sums == 0:
+            continue
+        dot4 = "v_dot4" in body
+        if bm == 256 and bn == 256:
+            assert dot4, name
+        else:
+            assert not dot4, name
+            seen += 1
+    assert seen > 0
