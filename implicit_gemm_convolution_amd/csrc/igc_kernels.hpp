@@ -1137,17 +1137,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // requantize scale and bias are loaded once, before the rows (loaded per
   // row, each pass waited for its own loads behind the previous pass's
   // stores, which may alias them).
+  // (loaded at the start of the staged path below)
   float q_scale[4] = {0.f, 0.f, 0.f, 0.f}, q_bias[4] = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (INT8) {
-    if (p.Qo) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int cc = min(col + q, p.N - 1);
-        q_scale[q] = p.scale[cc];
-        q_bias[q] = p.bias[cc];
-      }
-    }
-  }
 
   // Stream-K.  A segment that is only part of its tile first publishes the
   // tile's partial sums (mode 1: the staged tile, row-major, in this
@@ -1249,40 +1240,114 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
         }
       }
   };
+  // Requantized int8 as the only output of a whole tile: requantize in the
+  // registers (a lane's 4 accumulators of a block are 4 consecutive columns
+  // of one row), stage the packed int8 tile once (BM x BN bytes, the 16-byte
+  // chunk q of row r in slot q ^ (r % (BN/16)), so a staging store of 16
+  // rows and a row read are free of bank conflicts), and write it out in
+  // 16-byte rows.  Other tiles and outputs take the staged int32 path below.
+  bool qonly = false;
+  if constexpr (INT8) qonly = mode == 0 && p.Qo && !p.Ci && !p.D && p.vec_q && m0 + BM <= p.M && n0 + BN <= p.N;
+  if (qonly) {
+    if constexpr (INT8) {
+      static_assert(BM * BN <= RA * SA_ALLOC, "the int8 tile fits in the A stages");
+      constexpr int CQ = BN / 16;  // 16-byte chunks per int8 row
+      uint8_t* const qs = sa0;     // the A stage arrays are contiguous
+      auto qoff = [](int r, int c) { return r * BN + ((((c >> 4) ^ (r & (CQ - 1)))) << 4) + (c & 15); };
+      if constexpr (SUMS != 0) __syncthreads();  // the published row / column sums
 #pragma unroll
-  for (int h = 0; h < WM; ++h) {
-    if (wm == h) {
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        uint8_t* arr = stage_rt((i * MB) / 32);
+        for (int g4 = 0; g4 < NE / 4; ++g4) {
+          // (a scheduling fence per block column keeps its scale / bias loads
+          // here; hoisted for all columns at once they spill registers)
+          __builtin_amdgcn_sched_barrier(0);
+          const int lc = wn * TN + j * MB + acc_col(4 * g4);  // tile column of the first of the 4
+          uint32_t ccorr[4];
+          float sc[4], bi[4];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int g4 = 0; g4 < NE / 4; ++g4) {
-            const int off = stage_off((i * MB) % 32 + arow, wn * TN + j * MB + acc_col(4 * g4));
-            lds_write16(arr, off, acc_quad(i, j, g4));
+          for (int q = 0; q < 4; ++q) {
+            ccorr[q] = ((SUMS & SUM_COLS) != 0 && p.zAp != 0) ? (uint32_t)p.zAp * (uint32_t)sums[BM + lc + q] : 0u;
+            sc[q] = p.scale[n0 + lc + q];
+            bi[q] = p.bias[n0 + lc + q];
           }
-      }
-    }
-    __syncthreads();
 #pragma unroll
-    for (int pass = 0; pass < TM / RPP; ++pass) {
-      const int rr = rr0 + pass * RPP;         // row within the wave-row
-      const uint8_t* arr = stage_rt((pass * RPP) / 32);
-      const int lrow = h * TM + rr;
-      const int row = m0 + lrow;
-      uint4 v = *reinterpret_cast<const uint4*>(arr + stage_off(rr & 31, lcol));
-      const int voff = (lrow * BN + lcol) * 4;
-      if constexpr (SK) {
-        if (mode == 1) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), wsr, voff,
-                                                 (2 * g + (first_seg ? 0 : 1)) * SLOT, CPOL_DEV);
-          continue;
+          for (int i = 0; i < FM; ++i) {
+            const uint4 v = acc_quad(i, j, g4);
+            const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+            const uint32_t rcorr =
+                ((SUMS & SUM_ROWS) != 0 && p.zB != 0) ? (uint32_t)p.zB * (uint32_t)sums[wm * TM + i * MB + arow] : 0u;
+            int qi[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              // C = acc' - zA'*colsum(B) - zB*rowsum(A') + K*zA'*zB (wrapping;
+              // the true value fits in int32), then the requantize steps
+              const int32_t c = (int32_t)(vv[q] - ccorr[q] - rcorr + kzz);
+              const float t = (float)c * sc[q];  // separately rounded: built with -ffp-contract=off
+              const float y = t + bi[q];
+              float r = __builtin_rintf(y);      // half to even
+              r = fminf(fmaxf(r, -128.f), 127.f);
+              qi[q] = (int)r;
+            }
+            const uint32_t lo = __builtin_amdgcn_perm((uint32_t)qi[1], (uint32_t)qi[0], 0x0c0c0400u);
+            const uint32_t hi = __builtin_amdgcn_perm((uint32_t)qi[3], (uint32_t)qi[2], 0x04000c0cu);
+            *reinterpret_cast<uint32_t*>(qs + qoff(wm * TM + i * MB + arow, lc)) = lo | hi;
+          }
+        }
+      __syncthreads();
+      constexpr int RPQ = NT / CQ;  // rows per pass
+      static_assert(NT % CQ == 0 && BM % RPQ == 0, "int8 passes cover whole rows");
+      const int qc = (tid % CQ) * 16;
+#pragma unroll 4
+      for (int r = tid / CQ; r < BM; r += RPQ)
+        store16_nt(p.Qo + (long long)(m0 + r) * p.ldq + n0 + qc, lds_read16(qs, qoff(r, qc)));
+    }
+  } else {
+    if constexpr (INT8) {
+      if (p.Qo) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cc = min(col + q, p.N - 1);
+          q_scale[q] = p.scale[cc];
+          q_bias[q] = p.bias[cc];
         }
       }
-      if (mode == 0) emit(v, lrow);
     }
-    __syncthreads();
+  #pragma unroll
+    for (int h = 0; h < WM; ++h) {
+      if (wm == h) {
+  #pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          uint8_t* arr = stage_rt((i * MB) / 32);
+  #pragma unroll
+          for (int j = 0; j < FN; ++j)
+  #pragma unroll
+            for (int g4 = 0; g4 < NE / 4; ++g4) {
+              const int off = stage_off((i * MB) % 32 + arow, wn * TN + j * MB + acc_col(4 * g4));
+              lds_write16(arr, off, acc_quad(i, j, g4));
+            }
+        }
+      }
+      __syncthreads();
+  #pragma unroll
+      for (int pass = 0; pass < TM / RPP; ++pass) {
+        const int rr = rr0 + pass * RPP;         // row within the wave-row
+        const uint8_t* arr = stage_rt((pass * RPP) / 32);
+        const int lrow = h * TM + rr;
+        const int row = m0 + lrow;
+        uint4 v = *reinterpret_cast<const uint4*>(arr + stage_off(rr & 31, lcol));
+        const int voff = (lrow * BN + lcol) * 4;
+        if constexpr (SK) {
+          if (mode == 1) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), wsr, voff,
+                                                   (2 * g + (first_seg ? 0 : 1)) * SLOT, CPOL_DEV);
+            continue;
+          }
+        }
+        if (mode == 0) emit(v, lrow);
+      }
+      __syncthreads();
+    }
   }
   if constexpr (SK) if (mode == 1) {
     // the partial is out (its device-coherent stores acknowledged): count
