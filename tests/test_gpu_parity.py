@@ -235,6 +235,24 @@ def test_u8i8_output_subsets(igc, oracle, outputs):
     check_u8i8(oracle, got, A, 128, Bt, 3, scale, bias)
 
 
+# Requantized int8 as the only output: whole tiles requantize in registers and
+# stage packed int8, edge tiles take the staged int32 path; 520 x 520 mixes
+# both for every tile size, and the zero points select each sums mask.
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("zA,zB", [(128, 0), (128, 3), (37, 0), (37, -5)])
+def test_u8i8_requant_only_whole_and_edge_tiles(igc, oracle, variant, zA, zB):
+    M, N, K = 520, 520, 384
+    rng = np.random.default_rng(zA * 7 + zB + 1000)
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = synth.i8_uniform(rng, (N, K))
+    scale, bias = q_params(rng, N, K)
+    got = run_u8i8(igc, A, zA, Bt, zB, outputs=("Q",), scale=scale, bias=bias)
+    C = oracle.gemm_u8i8_naive(A, zA, Bt, zB)
+    ref = oracle.requant(C, scale, bias)
+    assert np.count_nonzero((ref > -128) & (ref < 127)) > ref.size // 2  # mostly unsaturated
+    assert np.array_equal(got["Q"], ref)
+
+
 @pytest.mark.parametrize("K", [33024, 33025])
 def test_u8i8_extreme_values_at_overflow_bound(igc, oracle, K):
     # |C| = 255 * 255 * K reaches 2,147,450,625 at K = 33025 (just below 2^31).
@@ -440,4 +458,20 @@ def test_qconv_dequant_and_requant_bit_exact(igc, oracle, case):
     Cref = oracle.conv2d_u8i8_direct_at(x, zA, w, zB, np.arange(Nb * P * Q), st, pd)
     assert np.array_equal(got["C"].astype(np.int64), Cref)
     assert np.array_equal(got["D"], oracle.dequant(Cref, 0.02, 0.01))
+    assert np.array_equal(got["Q"], oracle.requant(Cref, scale, bias))
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("case", [QCONV_CASES[0], QCONV_CASES[2], QCONV_CASES[4]])
+def test_qconv_requant_only(igc, oracle, variant, case):
+    Nb, H, W, C, Kout, R, S, st, pd, zA, zB = case
+    rng = np.random.default_rng(7 * sum(case[:7]) + zA)
+    x = synth.u8_uniform(rng, (Nb, H, W, C))
+    w = synth.i8_uniform(rng, (Kout, R, S, C))
+    scale = (rng.uniform(0.5, 2.0, Kout) * 40.0 / (74.0 * 74.0 * np.sqrt(R * S * C))).astype(np.float32)
+    bias = rng.standard_normal(Kout).astype(np.float32)
+    got = run_qconv(igc, x, zA, w, zB, st, pd, outputs=("Q",), scale=scale, bias=bias)
+    P = (H + 2 * pd[0] - R) // st[0] + 1
+    Q = (W + 2 * pd[1] - S) // st[1] + 1
+    Cref = oracle.conv2d_u8i8_direct_at(x, zA, w, zB, np.arange(Nb * P * Q), st, pd)
     assert np.array_equal(got["Q"], oracle.requant(Cref, scale, bias))
