@@ -204,6 +204,7 @@ int gemm_f16f32(int M, int N, int K, const void* A, int lda, const void* B, int 
   p.A = static_cast<const uint8_t*>(A); p.lda = lda;
   p.B = static_cast<const uint8_t*>(B); p.ldb = ldb;
   p.Cf = C; p.ldcf = ldc;
+  p.vec_c = aligned16(C) && ldc % 4 == 0;  // 16-byte stores of 4 consecutive columns
   // Buffer descriptors of the fast path cover one tile of rows and must stay below 2^31 bytes.
   const bool fast = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 &&
                     256LL * lda * 2 < (1LL << 31) && 256LL * ldb * 2 < (1LL << 31);
