@@ -30,7 +30,16 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // Tile variants.  The large tile keeps the most MFMA work per LDS byte; the
 // smaller ones exist so that small problems still spread over the 256 CUs
 // (the multi-kernel-per-shape dispatch of [GEMM-TVM] §4.3, done at run time).
-enum Variant { V_AUTO = -1, V_256x256 = 0, V_128x128 = 1, V_64x64 = 2, V_256x128 = 3, V_224x256 = 4, V_COUNT = 5 };
+enum Variant {
+  V_AUTO = -1,
+  V_256x256 = 0,
+  V_128x128 = 1,
+  V_64x64 = 2,
+  V_256x128 = 3,
+  V_224x256 = 4,
+  V_BYPASS = 5,  // fp16 GEMM, aligned operands: 32x32 tiles, one wave each, no LDS
+  V_COUNT = 6
+};
 
 inline int forced_variant() {
   const char* s = std::getenv("IGC_FORCE_VARIANT");
@@ -134,10 +143,31 @@ int launch_variant(int v, const igc::Params& p, hipStream_t stream) {
   }
 }
 
+inline int launch_bypass(igc::Params p, hipStream_t stream) {
+  p.tiles_m = (int)ceil_div(p.M, 32);
+  p.tiles_n = (int)ceil_div(p.N, 32);
+  const long long grid = (long long)p.tiles_m * p.tiles_n;
+  if (grid > 0x7fffffffLL) return fail(IGC_EUNSUPPORTED, "too many tiles (%lld)", grid);
+  hipLaunchKernelGGL((igc::gemm_f16_bypass_kernel<8>), dim3((unsigned)grid), dim3(64), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return IGC_OK;
+}
+
 template <int KIND, int SUMS>
 int launch(const igc::Params& p, bool fast, hipStream_t stream, int dev) {
+  if constexpr (KIND == igc::KIND_F16_GEMM) {
+    // The LDS-bypass kernel wins only where the whole problem is one short
+    // round: measured on MI355X, 256^3 3.6 us against 4.1 (64x64 tiles), 512^3
+    // 4.8 against 4.9, but 1024^3 16.4 against 6.6 and 256x256x4096 23.5
+    // against 14.2 (a single wave then walks a long K loop alone).
+    const int fv = forced_variant();
+    const bool small = ceil_div(p.M, 32) * ceil_div(p.N, 32) <= device_cus(dev) && p.K <= 512;
+    if (fast && (fv == V_BYPASS || (fv == V_AUTO && small))) return launch_bypass(p, stream);
+  }
   const int cus = device_cus(dev);
   int v = choose_variant(p.M, p.N, cus);
+  if (v == V_BYPASS) v = V_64x64;  // (forced, for a kind or shape without the bypass kernel)
   // The element-wise (unaligned) loaders need more registers; they stop at 128x128.
   if (!fast && (v == V_256x256 || v == V_256x128 || v == V_224x256)) v = V_128x128;
   if constexpr (KIND == igc::KIND_F16_CONV_C64) {

@@ -1405,4 +1405,83 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   }  // segments
 }
 
+// ---------------------------------------------------------------------------
+// LDS-bypass fp16 GEMM for small, latency-bound problems ([GEMM-TVM] §3.4:
+// operands loaded from global memory straight into the tensor-core operand
+// registers, no shared-memory staging).  One wave per 32 x 32 output tile;
+// lane l loads, for each 16-row block of A and of B, row l % 16 and the
+// 16-byte chunk l / 16 of each 64-byte k-step, i.e. exactly its MFMA operand.
+// KC k-steps of loads are issued before the first MFMA that needs them.  No
+// LDS, no barriers.  Needs the aligned operands of the fast path (rows
+// 16-byte aligned, K % 8 == 0).  The MFMA takes B first (transposed block:
+// lane l holds row l % 16, columns 4*(l/16) .. +3), so each block leaves in
+// one 16-byte store per lane.
+// ---------------------------------------------------------------------------
+template <int KC>
+__global__ void __launch_bounds__(64, 1) gemm_f16_bypass_kernel(const Params p) {
+  const int lane = threadIdx.x & 63;
+  const int tm = (int)blockIdx.x / p.tiles_n;
+  const int tn = (int)blockIdx.x - tm * p.tiles_n;
+  const int m0 = tm * 32, n0 = tn * 32;
+  const long long lda2 = p.lda * 2, ldb2 = p.ldb * 2;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.A + m0 * lda2), (short)0, (int)(min(32, p.M - m0) * lda2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.B + n0 * ldb2), (short)0, (int)(min(32, p.N - n0) * ldb2), 0x00020000);
+  const int frow = lane & 15;
+  const uint32_t chunk = (uint32_t)(lane >> 4) * 16u;
+  const uint32_t oa0 = (uint32_t)(frow * lda2) + chunk, oa1 = (uint32_t)((frow + 16) * lda2) + chunk;
+  const uint32_t ob0 = (uint32_t)(frow * ldb2) + chunk, ob1 = (uint32_t)((frow + 16) * ldb2) + chunk;
+  const uint32_t kbytes = (uint32_t)p.K * 2u;
+  const int nks = (p.K + 31) / 32;  // 64-byte k-steps
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto ld = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off, uint32_t kb) {
+    // k past K reads out of range (zeros): K % 8 == 0, so a chunk is all in or all out
+    const uint32_t o = kb + chunk < kbytes ? off + kb : OOB;
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)o, 0, 0));
+  };
+  for (int kb = 0; kb < nks; kb += KC) {
+    uint4 a0[KC], a1[KC], b0[KC], b1[KC];
+#pragma unroll
+    for (int s = 0; s < KC; ++s) {
+      const uint32_t k = (uint32_t)(kb + s) * 64u;
+      a0[s] = ld(ra, oa0, k);
+      a1[s] = ld(ra, oa1, k);
+      b0[s] = ld(rb, ob0, k);
+      b1[s] = ld(rb, ob1, k);
+    }
+#pragma unroll
+    for (int s = 0; s < KC; ++s) {
+      Mfma<KIND_F16_GEMM, 16>::run(acc[0][0], b0[s], a0[s]);
+      Mfma<KIND_F16_GEMM, 16>::run(acc[0][1], b1[s], a0[s]);
+      Mfma<KIND_F16_GEMM, 16>::run(acc[1][0], b0[s], a1[s]);
+      Mfma<KIND_F16_GEMM, 16>::run(acc[1][1], b1[s], a1[s]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = m0 + i * 16 + frow;
+    if (row >= p.M) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = n0 + j * 16 + (lane >> 4) * 4;
+      float* dst = p.Cf + (long long)row * p.ldcf + col;
+      const float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
+      if (col + 3 < p.N && p.vec_c) {
+        store16_nt(dst, make_uint4(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                                   __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)));
+      } else {
+        const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (col + q < p.N) dst[q] = vv[q];
+      }
+    }
+  }
+}
+
 }  // namespace igc

@@ -74,6 +74,28 @@ def test_f16_integer_valued_bit_exact(igc, oracle, variant, M, N, K):
     assert np.array_equal(C.astype(np.float64), ref)
 
 
+# The LDS-bypass fp16 kernel (forced): 32x32 tiles, one wave each, operands
+# loaded straight into the MFMA registers.
+@pytest.mark.parametrize("M,N,K", F16_EXACT_SHAPES + [(256, 256, 1024), (70, 33, 520)])
+def test_f16_bypass_integer_valued_bit_exact(igc, oracle, monkeypatch, M, N, K):
+    monkeypatch.setenv("IGC_FORCE_VARIANT", "5")
+    rng = np.random.default_rng(M * 131 + N * 7 + K)
+    A = synth.f16_small_ints(rng, (M, K))
+    Bt = synth.f16_small_ints(rng, (N, K))
+    C = run_f16(igc, A, Bt)
+    assert np.array_equal(C.astype(np.float64), oracle.gemm_f16(A, Bt))
+
+
+@pytest.mark.parametrize("M,N,K,ldc", [(256, 256, 256, 256), (200, 300, 1000, 301), (64, 48, 4096, 48)])
+def test_f16_bypass_random_tolerance(igc, oracle, monkeypatch, M, N, K, ldc):
+    monkeypatch.setenv("IGC_FORCE_VARIANT", "5")
+    rng = np.random.default_rng(M + N + K + 5)
+    A = synth.f16_uniform(rng, (M, K))
+    Bt = synth.f16_uniform(rng, (N, K))
+    C = run_f16(igc, A, Bt, ldc=ldc)
+    assert fp_rel_err(C, oracle.gemm_f16(A, Bt)) <= FP_TOL
+
+
 # Small tiles in grids of one round of 256 compute units or less (ragged
 # edges, long K loops) and of several rounds (289-1156 tiles).
 @pytest.mark.parametrize("variant,M,N,K", [("2", 1088, 1088, 264), ("1", 2176, 2176, 136),

@@ -21,7 +21,7 @@ def asm(tmp_path_factory):
     path = build.assembly(str(out))
     text = open(path).read()
     kernels = {}
-    for name in re.findall(r"^\s+\.amdhsa_kernel (\S+)", text, re.M):
+    for name in sorted(set(re.findall(r"^\s+\.amdhsa_kernel (\S+)", text, re.M))):
         start = re.search(r"^" + re.escape(name) + r":", text, re.M)
         assert start, name
         body = text[start.end():].split(".Lfunc_end", 1)[0]
@@ -30,6 +30,12 @@ def asm(tmp_path_factory):
         kernels[demangled] = (body, meta)
     assert kernels
     return kernels
+
+
+@pytest.fixture(scope="module")
+def tiled(asm):
+    """The tiled LDS kernels (igc::gemm_kernel<...>)."""
+    return {k: v for k, v in asm.items() if "gemm_kernel<" in k}
 
 
 INT_KINDS = (2, 4)  # u8 x i8 GEMM and convolution
@@ -42,8 +48,8 @@ def _params(demangled):
     return kind, bm, bn, m.group(6) == "true"
 
 
-def test_every_kernel_uses_mfma_of_its_dtype(asm):
-    for name, (body, _) in asm.items():
+def test_every_kernel_uses_mfma_of_its_dtype(tiled):
+    for name, (body, _) in tiled.items():
         kind, bm, bn, fast = _params(name)
         # 16 x 16 output blocks: on MI355X they sustain a higher clock than the
         # 32 x 32 forms within the power limit
@@ -55,8 +61,8 @@ def test_every_kernel_uses_mfma_of_its_dtype(asm):
             assert other not in body, (name, other)
 
 
-def test_no_scratch_in_main_loops_and_lds_within_limit(asm):
-    for name, (body, meta) in asm.items():
+def test_no_scratch_in_main_loops_and_lds_within_limit(tiled):
+    for name, (body, meta) in tiled.items():
         kind, bm, bn, fast = _params(name)
         lds = int(re.search(r"\.amdhsa_group_segment_fixed_size (\d+)", meta).group(1))
         assert lds <= 160 * 1024, name
@@ -73,8 +79,8 @@ def test_no_scratch_in_main_loops_and_lds_within_limit(asm):
             assert scratch <= (256 if bm == 256 else 0), (name, scratch)
 
 
-def test_fast_kernels_load_straight_into_lds_and_stream_outputs(asm):
-    for name, (body, _) in asm.items():
+def test_fast_kernels_load_straight_into_lds_and_stream_outputs(tiled):
+    for name, (body, _) in tiled.items():
         kind, bm, bn, fast = _params(name)
         if not fast:
             continue
@@ -82,8 +88,8 @@ def test_fast_kernels_load_straight_into_lds_and_stream_outputs(asm):
         assert re.search(r"global_store_dword(x4)? .* nt", body), name
 
 
-def test_no_packed_fp32_and_no_fma_in_epilogue_math(asm):
-    for name, (body, _) in asm.items():
+def test_no_packed_fp32_and_no_fma_in_epilogue_math(tiled):
+    for name, (body, _) in tiled.items():
         assert "v_pk_add_f32" not in body and "v_pk_mul_f32" not in body and "v_pk_fma_f32" not in body
         kind, *_ = _params(name)
         if kind in INT_KINDS:  # requantize: two separately rounded operations
@@ -93,12 +99,12 @@ def test_no_packed_fp32_and_no_fma_in_epilogue_math(asm):
             assert "v_fma_f32" not in epi and "v_fmac_f32" not in epi and "v_fmamk_f32" not in epi, name
 
 
-def test_zero_point_sums_on_matrix_cores_where_accumulators_fit(asm):
+def test_zero_point_sums_on_matrix_cores_where_accumulators_fit(tiled):
     # u8 x i8 kernels with zero-point sums: one extra MFMA per block and
     # k-step (a fragment of ones), no v_dot4, except at 256x256 where the
     # tile's accumulators fill all 256 accumulator registers.
     seen = 0
-    for name, (body, _) in asm.items():
+    for name, (body, _) in tiled.items():
         m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+), \d+, \d+, (true|false), (\d+), \d+>", name)
         kind, bm, bn, sums = int(m.group(1)), int(m.group(2)), int(m.group(3)), int(m.group(5))
         if kind not in INT_KINDS or sums == 0:
@@ -110,3 +116,17 @@ def test_zero_point_sums_on_matrix_cores_where_accumulators_fit(asm):
             assert not dot4, name
             seen += 1
     assert seen > 0
+
+
+def test_bypass_kernel_uses_no_lds(asm):
+    # the LDS-bypass fp16 kernel: MFMA operands loaded straight into
+    # registers, no LDS, no barrier, no scratch; 16-byte streaming stores
+    found = [k for k in asm if "gemm_f16_bypass_kernel" in k]
+    assert found
+    for name in found:
+        body, meta = asm[name]
+        assert "v_mfma_f32_16x16x32_f16" in body
+        assert int(re.search(r"\.amdhsa_group_segment_fixed_size (\d+)", meta).group(1)) == 0
+        assert int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", meta).group(1)) == 0
+        assert "ds_read" not in body and "ds_write" not in body and "s_barrier" not in body
+        assert re.search(r"global_store_dwordx4 .* nt", body), name
