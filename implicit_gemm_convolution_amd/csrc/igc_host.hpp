@@ -92,6 +92,11 @@ int launch_one(igc::Params p, hipStream_t stream) {
   long long grid = (long long)p.tiles_m * p.tiles_n;
   if (grid > 0x7fffffffLL) return fail(IGC_EUNSUPPORTED, "too many tiles (%lld)", grid);
   p.dp_tiles = (int)grid;
+  {
+    int d = 0;
+    const long long cus = (hipGetDevice(&d) == hipSuccess && d >= 0 && d < kMaxDevices) ? device_cus(d) : 256;
+    p.xcd_regroup = grid > cus;  // several rounds of workgroups per compute unit
+  }
   p.sk_wgs = 0;
   p.sk_iters = 0;
   if constexpr (BM == 256 && BN == 256 && FAST && SUMS == 0 && KIND != igc::KIND_U8I8_GEMM && KIND != igc::KIND_U8I8_CONV) {
