@@ -954,9 +954,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     lb.load(stB(D), k0 + decltype(D)::value);
   });
   wait_vmcnt_lgkm0<(DEPTH - 1) * (NLA + NLB)>();
+  // (zA = 0: the zeros of the out-of-range loads already are the zero point)
+  const bool padfix = PADFIX && p.zAp != -128;
   if constexpr (PADFIX) {
-    la.fix_pad(stA(std::integral_constant<int, 0>()));
-    wait_vmcnt_lgkm0<(DEPTH - 1) * (NLA + NLB)>();
+    if (padfix) {
+      la.fix_pad(stA(std::integral_constant<int, 0>()));
+      wait_vmcnt_lgkm0<(DEPTH - 1) * (NLA + NLB)>();
+    }
   }
   lds_barrier();
 #pragma unroll
@@ -1008,8 +1012,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt_lgkm0<(DEPTH - 2) * (NLA + NLB) + NLA>();
     if constexpr (PADFIX) {
-      la.fix_pad(stA(std::integral_constant<int, u + 1>()));
-      wait_vmcnt_lgkm0<(DEPTH - 2) * (NLA + NLB) + NLA>();
+      if (padfix) {
+        la.fix_pad(stA(std::integral_constant<int, u + 1>()));
+        wait_vmcnt_lgkm0<(DEPTH - 2) * (NLA + NLB) + NLA>();
+      }
     }
     lds_barrier();
     const uint8_t* As1 = stA(std::integral_constant<int, u + 1>());

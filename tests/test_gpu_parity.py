@@ -447,6 +447,8 @@ QCONV_CASES = [
     (2, 9, 11, 64, 96, 3, 3, (1, 1), (1, 1), 90, 2),        # C % 128 != 0: element-wise
     (1, 7, 9, 3, 13, 3, 3, (1, 2), (1, 0), 200, -1),
     (1, 9, 9, 128, 32, 7, 7, (1, 1), (3, 3), 17, 4),        # R*S = 49: element-wise
+    (2, 9, 11, 128, 96, 3, 3, (1, 1), (1, 1), 0, 5),        # zA = 0: padding needs no rewrite
+    (1, 7, 9, 16, 13, 3, 3, (1, 2), (1, 1), 0, 0),          # zA = 0, element-wise
 ]
 
 
