@@ -1,7 +1,8 @@
 /*
  * igc.h -- C ABI of libigc.so: tiled dense GEMM (fp16 -> fp32 and u8 x i8 ->
  * int32 with zero points and a fused quantization epilogue) and conv2d lowered
- * to an implicit GEMM, for AMD Instinct MI355X (gfx950).
+ * to an implicit GEMM (fp16, and u8 x i8 with zero points), for AMD Instinct
+ * MI355X (gfx950).
  *
  * Sources (cited by page title and section):
  *  [GEMM-TVM]  CSDN article "TVM在CUDA GPU上跑GEMM的全套张量化实现：WMMA/DP4A/IMMA
@@ -11,8 +12,14 @@
  *
  * Conventions shared by every entry point
  *  - All buffers are device memory owned by the caller (inputs, outputs and
- *    per-channel vectors).  The library never allocates, frees or copies
- *    device memory and keeps no state besides a per-device architecture cache.
+ *    per-channel vectors).  The library never copies device memory.  Its only
+ *    state is a per-device cache of the architecture and compute-unit count
+ *    and, for fp16 launches whose last round of 256x256 tiles is split
+ *    between workgroups (stream-K), a workspace per (device, stream) that it
+ *    allocates on first use, grows when needed and keeps until the process
+ *    ends.
+ *  - Environment (tests, tuning): IGC_FORCE_VARIANT=0..5 pins a kernel
+ *    variant, IGC_STREAMK=0 / 2 disables / forces the stream-K split.
  *  - Argument validation is synchronous and happens before any HIP call; a
  *    rejected call has no side effects.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
