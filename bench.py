@@ -6,20 +6,25 @@
 One step is one call of the workload's entry point over its synthetic inputs,
 which are resident in HBM before the timed region starts.  W untimed steps,
 then exactly K steps between two synchronizations; rank 0 prints one JSON
-line.  The headline workload is the 4096^3 fp16 GEMM (TFLOPS); the other four
-workloads are measured in the same run the same way and reported under
-"workloads" (the u8 x i8 GEMMs in TOPS).
+line.  The headline workload is the 4096^3 fp16 GEMM (TFLOPS); the other
+workloads (c1, c2, c4, c5 and the quantized convolution q4) are measured in
+the same run the same way, before the headline, and reported under
+"workloads" (the u8 x i8 ones in TOPS).
 
-`roofline` describes the workload's kernel: algorithmic operations per launch
-(2*M*N*K) divided by its mean launch duration, taken from HIP events recorded
-around every launch of the timed region on the stream the kernel runs on,
-against the MI355X dense MFMA peak of its dtype.  `traffic` (HBM bytes per
-launch) comes from the committed rocprofv3 counter summary in profiles/ when
-that summary was taken on the current kernel sources, else null.
+`value` and `roofline.achieved` are algorithmic operations per launch
+(2*M*N*K) divided by the mean launch duration of K back-to-back launches
+between two HIP events on the stream the kernel runs on, against the MI355X
+dense MFMA peak of its dtype.  After that timed region, untimed for `value`:
+each launch alone between two events (median, min, max), for c1 and c2 also
+with the caches flushed before every launch (cold), and the shader clock read
+from the driver while the launches run.  `traffic` (HBM bytes per launch)
+comes from the committed rocprofv3 counter summary in profiles/ when that
+summary was taken on the current kernel sources, else null.
 
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload
 (whole output rows, or whole output pixels for the convolution) on the host's
-cores.
+cores, with the OpenMP thread count it used, the CPUs available to the
+process and the CPU model.
 """
 from __future__ import annotations
 
@@ -88,10 +93,11 @@ class Runner:
         if wl.kind == "gemm_f16":
             A, B = t(wl.arrays["A"]), t(wl.arrays["Bt"])
             C = torch.empty((d["M"], d["N"]), dtype=torch.float32, device=dev)
-            self.keep = [A, B, C]
             M, N, K = d["M"], d["N"], d["K"]
+            ws, nws = self._workspace(igc.gemm_f16f32_workspace_size(M, N, K), torch, dev)
+            self.keep = [A, B, C, ws]
             self.call = self._direct("gemm_f16f32", M, N, K, A.data_ptr(), K, B.data_ptr(), K,
-                                     C.data_ptr(), N, self.stream)
+                                     C.data_ptr(), N, ws.data_ptr() if nws else None, nws, self.stream)
             self.dtype, self.peak, self.unit = "f16", PEAK_F16_TFLOPS, "TFLOPS"
         elif wl.kind == "gemm_u8i8":
             pr = wl.params
@@ -109,12 +115,13 @@ class Runner:
                 Q = torch.empty((M, N), dtype=torch.int8, device=dev)
                 S, Bi = t(wl.arrays["scale"]), t(wl.arrays["bias"])
                 kw.update(Q_i8=Q, ldq=N, scale_n=S, bias_n=Bi)
-            self.keep = [A, B] + [v for v in kw.values() if hasattr(v, "data_ptr")]
+            ws, nws = self._workspace(igc.gemm_u8i8_zp_workspace_size(M, N, K), torch, dev)
+            self.keep = [A, B, ws] + [v for v in kw.values() if hasattr(v, "data_ptr")]
             zA, zB = pr["zA"], pr["zB"]
             a = lambda k: kw[k].data_ptr() if k in kw else None  # noqa: E731
             self.ep = igc.Epilogue(a("C_i32"), kw.get("ldc", 0), a("D_f32"), kw.get("ldd", 0),
                                    kw.get("dq_scale", 0.0), a("Q_i8"), kw.get("ldq", 0),
-                                   a("scale_n"), a("bias_n"))
+                                   a("scale_n"), a("bias_n"), ws.data_ptr() if nws else None, nws)
             self.call = self._direct("gemm_u8i8_zp", M, N, K, A.data_ptr(), K, zA, B.data_ptr(), K, zB,
                                      ctypes.byref(self.ep), self.stream)
             self.dtype, self.peak, self.unit = "i8", PEAK_I8_TOPS, "TOPS"
@@ -123,10 +130,12 @@ class Runner:
             x, w = t(wl.arrays["x"]), t(wl.arrays["w"])
             S, Bi = t(wl.arrays["scale"]), t(wl.arrays["bias"])
             Q = torch.empty((d["M"], d["N"]), dtype=torch.int8, device=dev)
-            self.keep = [x, w, S, Bi, Q]
-            self.ep = igc.Epilogue(None, 0, None, 0, 0.0, Q.data_ptr(), d["N"], S.data_ptr(), Bi.data_ptr())
             args = (d["Nb"], d["H"], d["W"], d["C"], d["Kout"], d["R"], d["S"], d["stride_h"],
                     d["stride_w"], d["pad_h"], d["pad_w"])
+            ws, nws = self._workspace(igc.conv2d_u8i8_zp_workspace_size(*args), torch, dev)
+            self.keep = [x, w, S, Bi, Q, ws]
+            self.ep = igc.Epilogue(None, 0, None, 0, 0.0, Q.data_ptr(), d["N"], S.data_ptr(), Bi.data_ptr(),
+                                   ws.data_ptr() if nws else None, nws)
             self.call = self._direct("conv2d_u8i8_zp", *args, x.data_ptr(), pr["zA"], w.data_ptr(), pr["zB"],
                                      ctypes.byref(self.ep), self.stream)
             self.dtype, self.peak, self.unit = "i8", PEAK_I8_TOPS, "TOPS"
@@ -135,12 +144,18 @@ class Runner:
             P = (d["H"] + 2 * d["pad_h"] - d["R"]) // d["stride_h"] + 1
             Q = (d["W"] + 2 * d["pad_w"] - d["S"]) // d["stride_w"] + 1
             y = torch.empty((d["Nb"], P, Q, d["Kout"]), dtype=torch.float32, device=dev)
-            self.keep = [x, w, y]
             args = (d["Nb"], d["H"], d["W"], d["C"], d["Kout"], d["R"], d["S"], d["stride_h"],
                     d["stride_w"], d["pad_h"], d["pad_w"])
+            ws, nws = self._workspace(igc.conv2d_implicit_gemm_workspace_size(*args), torch, dev)
+            self.keep = [x, w, y, ws]
             self.call = self._direct("conv2d_implicit_gemm", *args, x.data_ptr(), w.data_ptr(),
-                                     y.data_ptr(), self.stream)
+                                     y.data_ptr(), ws.data_ptr() if nws else None, nws, self.stream)
             self.dtype, self.peak, self.unit = "f16", PEAK_F16_TFLOPS, "TFLOPS"
+
+    @staticmethod
+    def _workspace(nbytes, torch, dev):
+        """The caller-owned workspace the library asks for (zero-filled once)."""
+        return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev), nbytes
 
     def _direct(self, name, *args):
         """The C-ABI entry point with its arguments converted once: the timed
@@ -153,10 +168,14 @@ class Runner:
                 raise RuntimeError(f"{name}: status {st}")
         return call
 
-    def measure(self, torch, steps: int, warmup: int) -> dict:
+    def measure(self, torch, steps: int, warmup: int, cold: bool = False) -> dict:
         """Time `steps` back-to-back launches on the current stream between two
         HIP events: the average launch duration is the elapsed time / steps
-        (no event commands between the launches, as a caller would run them)."""
+        (no event commands between the launches, as a caller would run them).
+        Then, untimed for the headline value: each launch alone between two
+        events (median, min, max), the same with the caches flushed before
+        every launch when `cold`, and the shader clock read while the launches
+        run."""
         if warmup is None:
             # until 0.25 s of work has run (at least 10 launches)
             warmup, t0 = 0, time.perf_counter()
@@ -182,7 +201,7 @@ class Runner:
         total = t_all0.elapsed_time(t_all1) * 1e-3
         ops = self.wl.ops()
         step_s = total / steps
-        return dict(
+        res = dict(
             steps=steps, warmup=warmup, ms_per_step=step_s * 1e3, wall_s=wall,
             value=ops / step_s / 1e12, unit=self.unit, dtype=self.dtype,
             launch_us_mean=step_s * 1e6,
@@ -190,6 +209,93 @@ class Runner:
             frac_of_peak=ops / step_s / 1e12 / self.peak,
             alg_gbps=algorithmic_bytes(self.wl) / step_s / 1e9,
         )
+        res.update(self._per_launch(torch, steps, "launch_us"))
+        if cold:
+            # a 512 MiB write between launches evicts the operands from the
+            # 256 MiB last-level cache (MALL) and the L2s
+            flush = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
+            res.update(self._per_launch(torch, steps, "cold_launch_us", before=lambda: flush.fill_(1.0)))
+            res["cold_alg_gbps"] = algorithmic_bytes(self.wl) / (res["cold_launch_us_median"] * 1e-6) / 1e9
+            del flush
+        res["sclk_mhz"] = self._sclk_while_running(torch)
+        return res
+
+    def _per_launch(self, torch, steps, key, before=None) -> dict:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in ev:
+            if before is not None:
+                before()
+            e0.record()
+            self.call()
+            e1.record()
+        torch.cuda.synchronize()
+        us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+        return {f"{key}_median": us[len(us) // 2], f"{key}_min": us[0], f"{key}_max": us[-1],
+                f"{key}_mean": sum(us) / len(us)}
+
+    def _sclk_while_running(self, torch, seconds=0.3):
+        """Shader clock (MHz) read while back-to-back launches run, or None."""
+        import threading
+
+        samples, stop = [], threading.Event()
+
+        def poll():
+            while not stop.is_set():
+                v = read_sclk_mhz()
+                if v is None:
+                    return
+                samples.append(v)
+                time.sleep(0.01)
+
+        th = threading.Thread(target=poll, daemon=True)
+        th.start()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                self.call()
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        if not samples:
+            return None
+        samples.sort()
+        return {"median": samples[len(samples) // 2], "min": samples[0], "max": samples[-1],
+                "samples": len(samples)}
+
+
+def read_sclk_mhz():
+    """Current shader clock of GPU 0 from the driver's DPM table (the level
+    marked '*'), or None where the file is not readable."""
+    import glob
+
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        tok = [t for t in line.split() if t.lower().endswith("mhz")]
+                        if tok:
+                            return float(tok[0][:-3])
+        except OSError:
+            continue
+    return None
+
+
+def host_info() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "cpus_available": avail}
 
 
 def cpu_baseline(wl, budget_s: float) -> dict:
@@ -232,9 +338,11 @@ def cpu_baseline(wl, budget_s: float) -> dict:
     ops = 2.0 * n * d["N"] * d["K"]
     unit = "TOPS" if wl.kind in ("gemm_u8i8", "conv_u8i8") else "TFLOPS"
     what = "output pixels" if wl.kind.startswith("conv") else "output rows"
+    info = host_info()
     return dict(value=ops / t / 1e12, unit=unit, cores=cores, kind="oracle",
                 sample=f"first {n} of {d['M']} {what} of {wl.name} (all {d['N']} columns, "
-                       f"K={d['K']}), {t:.1f} s on {cores} threads",
+                       f"K={d['K']}), {t:.1f} s on {cores} OpenMP threads",
+                cpu_model=info["cpu_model"], cpus_available=info["cpus_available"],
                 seconds=t)
 
 
@@ -302,13 +410,17 @@ def main(argv=None) -> int:
         print(f"device check failed: {igc.last_error()}", file=sys.stderr)
         return 1
 
-    names = [args.workload] + ([] if args.only else [w for w in synth.WORKLOADS if w != args.workload])
+    # The headline workload runs last: after the others, the GPU is at the
+    # steady clock it holds under sustained load (it needs ~20 ms of load to
+    # leave its idle clock), whatever --warmup says.
+    names = ([] if args.only else [w for w in synth.WORKLOADS if w != args.workload]) + [args.workload]
     results = {}
     head_wl = None
     for name in names:
         wl = synth.workload(name)
         r = Runner(wl, igc, torch)
-        res = r.measure(torch, args.steps, args.warmup)
+        res = r.measure(torch, args.steps, args.warmup, cold=name in ("c1", "c2"))
+        res["roofline_traffic_bytes"] = traffic_for(name)
         res["config"] = synth.DESCRIPTIONS[name]
         results[name] = res
         if name == args.workload:
@@ -316,7 +428,10 @@ def main(argv=None) -> int:
         del r
         torch.cuda.empty_cache()
         print(f"# {name}: {res['value']:.1f} {res['unit']} ({100 * res['frac_of_peak']:.1f}% of peak), "
-              f"{res['launch_us_mean']:.1f} us/launch", file=sys.stderr, flush=True)
+              f"{res['launch_us_mean']:.1f} us/launch back to back, {res['launch_us_median']:.1f} us median alone"
+              + (f", {res['cold_launch_us_median']:.1f} us cold" if "cold_launch_us_median" in res else "")
+              + (f", sclk {res['sclk_mhz']['median']:.0f} MHz" if res.get("sclk_mhz") else ""),
+              file=sys.stderr, flush=True)
 
     head = results[args.workload]
     cpu = None
@@ -348,6 +463,10 @@ def main(argv=None) -> int:
             "frac": round(head["frac_of_peak"], 4),
             "traffic": traffic_for(args.workload),
             "launch_us_mean": round(head["launch_us_mean"], 2),
+            "launch_us_median": round(head["launch_us_median"], 2),
+            "launch_us_min": round(head["launch_us_min"], 2),
+            "launch_us_max": round(head["launch_us_max"], 2),
+            "sclk_mhz": head.get("sclk_mhz"),
             "kernel_source_hash": kernel_source_hash(),
         },
         "cpu_baseline": cpu,

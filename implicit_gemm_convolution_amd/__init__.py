@@ -15,11 +15,16 @@ from .binding import (  # noqa: F401
     Epilogue,
     IGCError,
     conv2d_implicit_gemm,
+    conv2d_implicit_gemm_workspace_size,
     conv2d_u8i8_zp,
+    conv2d_u8i8_zp_workspace_size,
     device_check,
     gemm_f16f32,
+    gemm_f16f32_workspace_size,
     gemm_u8i8_zp,
+    gemm_u8i8_zp_workspace_size,
     last_error,
     load,
+    set_tuning,
     status_string,
 )

@@ -29,7 +29,9 @@ IGC_ENODEV = -5
 
 # Every symbol include/igc.h declares.
 EXPORTED = ("gemm_f16f32", "gemm_u8i8_zp", "conv2d_implicit_gemm", "conv2d_u8i8_zp",
-            "igc_status_string", "igc_last_error", "igc_device_check")
+            "gemm_f16f32_workspace_size", "gemm_u8i8_zp_workspace_size",
+            "conv2d_implicit_gemm_workspace_size", "conv2d_u8i8_zp_workspace_size",
+            "igc_status_string", "igc_last_error", "igc_device_check", "igc_set_tuning")
 
 
 class IGCError(RuntimeError):
@@ -50,6 +52,8 @@ class Epilogue(ctypes.Structure):
         ("ldq", ctypes.c_int),
         ("scale_n", ctypes.c_void_p),
         ("bias_n", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("ws_bytes", ctypes.c_size_t),
     ]
 
 
@@ -70,15 +74,24 @@ def load() -> ctypes.CDLL:
     except ImportError:
         pass
     L = ctypes.CDLL(LIB_PATH)
-    i, p = ctypes.c_int, ctypes.c_void_p
-    L.gemm_f16f32.argtypes = [i, i, i, p, i, p, i, p, i, p]
+    i, p, z = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    pz = ctypes.POINTER(ctypes.c_size_t)
+    L.gemm_f16f32.argtypes = [i, i, i, p, i, p, i, p, i, p, z, p]
     L.gemm_f16f32.restype = i
     L.gemm_u8i8_zp.argtypes = [i, i, i, p, i, i, p, i, i, ctypes.POINTER(Epilogue), p]
     L.gemm_u8i8_zp.restype = i
-    L.conv2d_implicit_gemm.argtypes = [i] * 11 + [p, p, p, p]
+    L.conv2d_implicit_gemm.argtypes = [i] * 11 + [p, p, p, p, z, p]
     L.conv2d_implicit_gemm.restype = i
     L.conv2d_u8i8_zp.argtypes = [i] * 11 + [p, i, p, i, ctypes.POINTER(Epilogue), p]
     L.conv2d_u8i8_zp.restype = i
+    for name in ("gemm_f16f32_workspace_size", "gemm_u8i8_zp_workspace_size"):
+        getattr(L, name).argtypes = [i, i, i, pz]
+        getattr(L, name).restype = i
+    for name in ("conv2d_implicit_gemm_workspace_size", "conv2d_u8i8_zp_workspace_size"):
+        getattr(L, name).argtypes = [i] * 11 + [pz]
+        getattr(L, name).restype = i
+    L.igc_set_tuning.argtypes = [i, i]
+    L.igc_set_tuning.restype = i
     L.igc_status_string.argtypes = [i]
     L.igc_status_string.restype = ctypes.c_char_p
     L.igc_last_error.argtypes = []
@@ -133,33 +146,74 @@ def device_check(raise_on_error: bool = False) -> int:
     return _check(st, "igc_device_check") if raise_on_error else st
 
 
-def gemm_f16f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None, *, check=True) -> int:
-    st = load().gemm_f16f32(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _stream(stream))
+def set_tuning(force_variant: int = -1, streamk_mode: int = 1, *, check=True) -> int:
+    """Process-wide overrides (tests, sweeps): a forced tile variant (-1 = by
+    shape) and the stream-K mode (0 off, 1 where it pays, 2 always)."""
+    st = load().igc_set_tuning(int(force_variant), int(streamk_mode))
+    return _check(st, "igc_set_tuning") if check else st
+
+
+def _ws_query(name, *args) -> int:
+    out = ctypes.c_size_t(0)
+    _check(getattr(load(), name)(*args, ctypes.byref(out)), name)
+    return int(out.value)
+
+
+def gemm_f16f32_workspace_size(M, N, K) -> int:
+    return _ws_query("gemm_f16f32_workspace_size", M, N, K)
+
+
+def gemm_u8i8_zp_workspace_size(M, N, K) -> int:
+    return _ws_query("gemm_u8i8_zp_workspace_size", M, N, K)
+
+
+def conv2d_implicit_gemm_workspace_size(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w) -> int:
+    return _ws_query("conv2d_implicit_gemm_workspace_size", Nb, H, W, C, Kout, R, S, stride_h, stride_w,
+                     pad_h, pad_w)
+
+
+def conv2d_u8i8_zp_workspace_size(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w) -> int:
+    return _ws_query("conv2d_u8i8_zp_workspace_size", Nb, H, W, C, Kout, R, S, stride_h, stride_w,
+                     pad_h, pad_w)
+
+
+def _ws_bytes(workspace, ws_bytes):
+    if ws_bytes is None:
+        ws_bytes = int(workspace.numel() * workspace.element_size()) if hasattr(workspace, "numel") else 0
+    return ws_bytes
+
+
+def gemm_f16f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None, *, workspace=None, ws_bytes=None,
+                check=True) -> int:
+    st = load().gemm_f16f32(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _addr(workspace),
+                            _ws_bytes(workspace, ws_bytes), _stream(stream))
     return _check(st, "gemm_f16f32") if check else st
 
 
 def gemm_u8i8_zp(M, N, K, A, lda, zA, B, ldb, zB, *, C_i32=None, ldc=0, D_f32=None, ldd=0,
                  dq_scale=0.0, Q_i8=None, ldq=0, scale_n=None, bias_n=None, stream=None,
-                 check=True) -> int:
+                 workspace=None, ws_bytes=None, check=True) -> int:
     ep = Epilogue(_addr(C_i32), ldc, _addr(D_f32), ldd, float(dq_scale), _addr(Q_i8), ldq,
-                  _addr(scale_n), _addr(bias_n))
+                  _addr(scale_n), _addr(bias_n), _addr(workspace), _ws_bytes(workspace, ws_bytes))
     st = load().gemm_u8i8_zp(M, N, K, _addr(A), lda, zA, _addr(B), ldb, zB, ctypes.byref(ep),
                              _stream(stream))
     return _check(st, "gemm_u8i8_zp") if check else st
 
 
 def conv2d_implicit_gemm(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, x, w, y,
-                         stream=None, *, check=True) -> int:
+                         stream=None, *, workspace=None, ws_bytes=None, check=True) -> int:
     st = load().conv2d_implicit_gemm(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w,
-                                     _addr(x), _addr(w), _addr(y), _stream(stream))
+                                     _addr(x), _addr(w), _addr(y), _addr(workspace),
+                                     _ws_bytes(workspace, ws_bytes), _stream(stream))
     return _check(st, "conv2d_implicit_gemm") if check else st
 
 
 def conv2d_u8i8_zp(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, x, zA, w, zB, *,
                    C_i32=None, ldc=0, D_f32=None, ldd=0, dq_scale=0.0, Q_i8=None, ldq=0,
-                   scale_n=None, bias_n=None, stream=None, check=True) -> int:
+                   scale_n=None, bias_n=None, stream=None, workspace=None, ws_bytes=None,
+                   check=True) -> int:
     ep = Epilogue(_addr(C_i32), ldc, _addr(D_f32), ldd, float(dq_scale), _addr(Q_i8), ldq,
-                  _addr(scale_n), _addr(bias_n))
+                  _addr(scale_n), _addr(bias_n), _addr(workspace), _ws_bytes(workspace, ws_bytes))
     st = load().conv2d_u8i8_zp(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, _addr(x), zA,
                                _addr(w), zB, ctypes.byref(ep), _stream(stream))
     return _check(st, "conv2d_u8i8_zp") if check else st

@@ -1,16 +1,14 @@
 // igc.hip -- the C ABI of libigc.so (declared in include/igc.h): argument
-// validation, device check, and the host state of the launches (error
-// detail, compute-unit counts, stream-K workspaces).  Variant choice and the
-// launches themselves are in igc_host.hpp, instantiated in igc_launch.hip;
-// all arithmetic happens in the kernels of igc_kernels.hpp.
+// validation, device check, workspace checks and the library's host state
+// (error detail, per-device architecture and compute-unit counts, tuning
+// overrides).  The launch plan and the launches themselves are in
+// igc_host.hpp, instantiated in igc_launch.hip; all arithmetic happens in the
+// kernels of igc_kernels.hpp.  The library allocates no device memory.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <atomic>
 #include <cstdarg>
-#include <map>
-#include <mutex>
-#include <utility>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -73,47 +71,15 @@ int device_cus(int dev) {
   return n;
 }
 
-// Stream-K workspace, one per (device, stream) so that launches on different
-// streams never share it: partial tiles and per-tile arrival counters (zeroed
-// once when allocated; the kernel leaves them at zero).  It grows on demand
-// and is kept until the process ends.
-struct SkWorkspace {
-  void* ws = nullptr;
-  size_t ws_bytes = 0;
-  int* cnt = nullptr;
-  size_t cnt_n = 0;
-};
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, SkWorkspace> g_ws;
+std::atomic<int> g_force_variant{V_AUTO};
+std::atomic<int> g_streamk_mode{1};
 
-int sk_workspace(int dev, hipStream_t stream, size_t ws_bytes, size_t cnt_n, float** ws, int** cnt) {
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  SkWorkspace& w = g_ws[std::make_pair(dev, stream)];
-  if (w.ws_bytes < ws_bytes || w.cnt_n < cnt_n) {
-    if (w.ws || w.cnt) {
-      // earlier launches on this stream may still use the old buffers
-      if (hipStreamSynchronize(stream) != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(IGC_EHIP, "hipStreamSynchronize failed before growing the stream-K workspace");
-      }
-      (void)hipFree(w.ws);
-      (void)hipFree(w.cnt);
-      w = SkWorkspace();
-    }
-    const size_t nb = std::max(ws_bytes, w.ws_bytes), nc = std::max(cnt_n, w.cnt_n);
-    if (hipMalloc(&w.ws, nb) != hipSuccess || hipMalloc(reinterpret_cast<void**>(&w.cnt), nc * sizeof(int)) != hipSuccess ||
-        hipMemsetAsync(w.cnt, 0, nc * sizeof(int), stream) != hipSuccess) {
-      (void)hipGetLastError();
-      if (w.ws) (void)hipFree(w.ws);
-      if (w.cnt) (void)hipFree(w.cnt);
-      w = SkWorkspace();
-      return fail(IGC_EHIP, "cannot allocate the stream-K workspace (%zu bytes)", nb);
-    }
-    w.ws_bytes = nb;
-    w.cnt_n = nc;
-  }
-  *ws = static_cast<float*>(w.ws);
-  *cnt = w.cnt;
+// The caller's workspace against the plan: none needed, or one large enough.
+int check_workspace(const Plan& pl, const void* ws, size_t ws_bytes) {
+  if (!pl.ws_bytes) return IGC_OK;
+  if (ws_bytes < pl.ws_bytes)
+    return fail(IGC_EINVAL, "workspace of %zu bytes < the %zu bytes this call needs", ws_bytes, pl.ws_bytes);
+  if (!aligned16(ws)) return fail(IGC_EINVAL, "workspace not 16-byte aligned");
   return IGC_OK;
 }
 
@@ -124,6 +90,9 @@ igc::Params zero_params() {
 }
 
 // Validation shared by the two convolutions; fills the im2col part of p.
+// The im2col loaders keep a row's top-left input coordinate in two signed
+// 16-bit halves of one register, so H, W, R, S and the paddings must stay
+// below 2^15.
 int conv_params(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h, int stride_w,
                 int pad_h, int pad_w, igc::Params& p, long long* nx_out) {
   if (Nb <= 0 || H <= 0 || W <= 0 || C <= 0 || Kout <= 0 || R <= 0 || S <= 0)
@@ -134,6 +103,8 @@ int conv_params(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_
   const long long Q = ((long long)W + 2LL * pad_w - S) / stride_w + 1;
   if ((long long)H + 2LL * pad_h < R || (long long)W + 2LL * pad_w < S || P < 1 || Q < 1)
     return fail(IGC_EINVAL, "filter larger than the padded input");
+  if (H >= 32768 || W >= 32768 || R >= 32768 || S >= 32768 || pad_h >= 32768 || pad_w >= 32768)
+    return fail(IGC_EUNSUPPORTED, "H, W, R, S, pad_h and pad_w must be below 32768");
   const long long M = (long long)Nb * P * Q;
   const long long K = (long long)R * S * C;
   const long long nx = (long long)Nb * H * W * C;
@@ -148,17 +119,64 @@ int conv_params(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_
   return IGC_OK;
 }
 
+// Validation of a u8 x i8 output descriptor for an M x N product.
+int check_epilogue(const igc_u8i8_epilogue* ep, int N, int K) {
+  if (!ep) return fail(IGC_EINVAL, "epilogue descriptor is NULL");
+  if (!ep->C_i32 && !ep->D_f32 && !ep->Q_i8) return fail(IGC_EINVAL, "no output requested");
+  if (K > 33025) return fail(IGC_EOVERFLOW, "K=%d > 33025 can overflow int32", K);
+  if (ep->C_i32 && ep->ldc < N) return fail(IGC_EINVAL, "ldc=%d < N=%d", ep->ldc, N);
+  if (ep->D_f32 && ep->ldd < N) return fail(IGC_EINVAL, "ldd=%d < N=%d", ep->ldd, N);
+  if (ep->Q_i8) {
+    if (ep->ldq < N) return fail(IGC_EINVAL, "ldq=%d < N=%d", ep->ldq, N);
+    if (!ep->scale_n || !ep->bias_n) return fail(IGC_EINVAL, "Q_i8 needs scale_n and bias_n");
+  }
+  return IGC_OK;
+}
+
+void epilogue_params(igc::Params& p, const igc_u8i8_epilogue* ep) {
+  p.Ci = ep->C_i32; p.ldci = ep->ldc;
+  p.D = ep->D_f32; p.ldd = ep->ldd; p.dq = ep->dq_scale;
+  p.Qo = ep->Q_i8; p.ldq = ep->ldq; p.scale = ep->scale_n; p.bias = ep->bias_n;
+  p.vec_c = aligned16(ep->C_i32) && ep->ldc % 4 == 0;
+  p.vec_d = aligned16(ep->D_f32) && ep->ldd % 4 == 0;
+  p.vec_q = (reinterpret_cast<uintptr_t>(ep->Q_i8) & 3u) == 0 && ep->ldq % 4 == 0;
+}
+
+// Plans a launch on the current device, checks the caller's workspace
+// against it and launches.
+template <int KIND, int SUMS>
+int plan_and_launch(igc::Params& p, bool fast, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int dev;
+  if (int s = check_device(&dev)) return s;
+  const Plan pl = make_plan(KIND, p.M, p.N, p.K, fast, device_cus(dev), ws != nullptr);
+  if (int s = check_workspace(pl, ws, ws_bytes)) return s;
+  apply_plan(p, pl, ws);
+  return launch<KIND, SUMS>(p, pl, fast, stream);
+}
+
 // The zero-point sums are compiled only into the kernels that need them:
 // rowsum(A') when zB != 0, colsum(B) when zA != 128.
 template <int KIND>
-int launch_u8i8(const igc::Params& p, bool fast, hipStream_t stream, int dev) {
+int launch_u8i8(igc::Params& p, bool fast, void* ws, size_t ws_bytes, hipStream_t stream) {
   const int sums = (p.zB != 0 ? igc::SUM_ROWS : 0) | (p.zAp != 0 ? igc::SUM_COLS : 0);
   switch (sums) {
-    case 0: return launch<KIND, 0>(p, fast, stream, dev);
-    case 1: return launch<KIND, 1>(p, fast, stream, dev);
-    case 2: return launch<KIND, 2>(p, fast, stream, dev);
-    default: return launch<KIND, 3>(p, fast, stream, dev);
+    case 0: return plan_and_launch<KIND, 0>(p, fast, ws, ws_bytes, stream);
+    case 1: return plan_and_launch<KIND, 1>(p, fast, ws, ws_bytes, stream);
+    case 2: return plan_and_launch<KIND, 2>(p, fast, ws, ws_bytes, stream);
+    default: return plan_and_launch<KIND, 3>(p, fast, ws, ws_bytes, stream);
   }
+}
+
+// Workspace bytes of the plan for an M x N x K problem of this kind on the
+// current device, with the aligned operand path (the one that may split).
+int query_workspace(int kind, int M, int N, int K, size_t* bytes) {
+  if (!bytes) return fail(IGC_EINVAL, "bytes is NULL");
+  *bytes = 0;
+  if (M == 0 || N == 0) return IGC_OK;
+  int dev;
+  if (int s = check_device(&dev)) return s;
+  *bytes = make_plan(kind, M, N, K, true, device_cus(dev), true).ws_bytes;
+  return IGC_OK;
 }
 
 }  // namespace igc_host
@@ -186,8 +204,24 @@ int igc_device_check(void) {
   return check_device(&dev);
 }
 
+int igc_set_tuning(int force_variant, int streamk_mode) {
+  g_last_error[0] = 0;
+  if (force_variant < V_AUTO || force_variant >= V_COUNT)
+    return fail(IGC_EINVAL, "force_variant=%d outside [-1, %d]", force_variant, V_COUNT - 1);
+  if (streamk_mode < 0 || streamk_mode > 2) return fail(IGC_EINVAL, "streamk_mode=%d outside [0, 2]", streamk_mode);
+  g_force_variant.store(force_variant, std::memory_order_relaxed);
+  g_streamk_mode.store(streamk_mode, std::memory_order_relaxed);
+  return IGC_OK;
+}
+
+int gemm_f16f32_workspace_size(int M, int N, int K, size_t* bytes) {
+  g_last_error[0] = 0;
+  if (M < 0 || N < 0 || K < 0) return fail(IGC_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
+  return query_workspace(igc::KIND_F16_GEMM, M, N, K, bytes);
+}
+
 int gemm_f16f32(int M, int N, int K, const void* A, int lda, const void* B, int ldb, float* C,
-                int ldc, void* stream) {
+                int ldc, void* workspace, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
   if (M < 0 || N < 0 || K < 0) return fail(IGC_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
   if (M == 0 || N == 0) return IGC_OK;
@@ -197,8 +231,6 @@ int gemm_f16f32(int M, int N, int K, const void* A, int lda, const void* B, int 
     if (!A || !B) return fail(IGC_EINVAL, "A or B is NULL");
     if (lda < K || ldb < K) return fail(IGC_EINVAL, "lda=%d / ldb=%d < K=%d", lda, ldb, K);
   }
-  int dev;
-  if (int s = check_device(&dev)) return s;
   igc::Params p = zero_params();
   p.M = M; p.N = N; p.K = K;
   p.A = static_cast<const uint8_t*>(A); p.lda = lda;
@@ -208,7 +240,13 @@ int gemm_f16f32(int M, int N, int K, const void* A, int lda, const void* B, int 
   // Buffer descriptors of the fast path cover one tile of rows and must stay below 2^31 bytes.
   const bool fast = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 &&
                     256LL * lda * 2 < (1LL << 31) && 256LL * ldb * 2 < (1LL << 31);
-  return launch<igc::KIND_F16_GEMM, 0>(p, fast, static_cast<hipStream_t>(stream), dev);
+  return plan_and_launch<igc::KIND_F16_GEMM, 0>(p, fast, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int gemm_u8i8_zp_workspace_size(int M, int N, int K, size_t* bytes) {
+  g_last_error[0] = 0;
+  if (M < 0 || N < 0 || K < 0) return fail(IGC_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
+  return query_workspace(igc::KIND_U8I8_GEMM, M, N, K, bytes);
 }
 
 int gemm_u8i8_zp(int M, int N, int K, const uint8_t* A, int lda, int zA, const int8_t* B, int ldb,
@@ -217,36 +255,30 @@ int gemm_u8i8_zp(int M, int N, int K, const uint8_t* A, int lda, int zA, const i
   if (M < 0 || N < 0 || K < 0) return fail(IGC_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
   if (zA < 0 || zA > 255) return fail(IGC_EINVAL, "zA=%d outside [0, 255]", zA);
   if (zB < -128 || zB > 127) return fail(IGC_EINVAL, "zB=%d outside [-128, 127]", zB);
-  if (!ep) return fail(IGC_EINVAL, "epilogue descriptor is NULL");
-  if (!ep->C_i32 && !ep->D_f32 && !ep->Q_i8) return fail(IGC_EINVAL, "no output requested");
-  if (K > 33025) return fail(IGC_EOVERFLOW, "K=%d > 33025 can overflow int32", K);
+  if (int s = check_epilogue(ep, N, K)) return s;
   if (M == 0 || N == 0) return IGC_OK;
-  if (ep->C_i32 && ep->ldc < N) return fail(IGC_EINVAL, "ldc=%d < N=%d", ep->ldc, N);
-  if (ep->D_f32 && ep->ldd < N) return fail(IGC_EINVAL, "ldd=%d < N=%d", ep->ldd, N);
-  if (ep->Q_i8) {
-    if (ep->ldq < N) return fail(IGC_EINVAL, "ldq=%d < N=%d", ep->ldq, N);
-    if (!ep->scale_n || !ep->bias_n) return fail(IGC_EINVAL, "Q_i8 needs scale_n and bias_n");
-  }
   if (K > 0) {
     if (!A || !B) return fail(IGC_EINVAL, "A or B is NULL");
     if (lda < K || ldb < K) return fail(IGC_EINVAL, "lda=%d / ldb=%d < K=%d", lda, ldb, K);
   }
-  int dev;
-  if (int s = check_device(&dev)) return s;
   igc::Params p = zero_params();
   p.M = M; p.N = N; p.K = K;
   p.A = A; p.lda = lda;
   p.B = reinterpret_cast<const uint8_t*>(B); p.ldb = ldb;
   p.zAp = zA - 128; p.zB = zB;
-  p.Ci = ep->C_i32; p.ldci = ep->ldc;
-  p.D = ep->D_f32; p.ldd = ep->ldd; p.dq = ep->dq_scale;
-  p.Qo = ep->Q_i8; p.ldq = ep->ldq; p.scale = ep->scale_n; p.bias = ep->bias_n;
-  p.vec_c = aligned16(ep->C_i32) && ep->ldc % 4 == 0;
-  p.vec_d = aligned16(ep->D_f32) && ep->ldd % 4 == 0;
-  p.vec_q = (reinterpret_cast<uintptr_t>(ep->Q_i8) & 3u) == 0 && ep->ldq % 4 == 0;
+  epilogue_params(p, ep);
   const bool fast = aligned16(A) && aligned16(B) && lda % 16 == 0 && ldb % 16 == 0 &&
                     K % 16 == 0 && 256LL * lda < (1LL << 31) && 256LL * ldb < (1LL << 31);
-  return launch_u8i8<igc::KIND_U8I8_GEMM>(p, fast, static_cast<hipStream_t>(stream), dev);
+  return launch_u8i8<igc::KIND_U8I8_GEMM>(p, fast, ep->workspace, ep->ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int conv2d_u8i8_zp_workspace_size(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h,
+                                  int stride_w, int pad_h, int pad_w, size_t* bytes) {
+  g_last_error[0] = 0;
+  igc::Params p = zero_params();
+  long long nx = 0;
+  if (int st = conv_params(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, p, &nx)) return st;
+  return query_workspace(igc::KIND_U8I8_CONV, p.M, p.N, p.K, bytes);
 }
 
 int conv2d_u8i8_zp(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h, int stride_w,
@@ -259,54 +291,45 @@ int conv2d_u8i8_zp(int Nb, int H, int W, int C, int Kout, int R, int S, int stri
   if (!x || !w) return fail(IGC_EINVAL, "x or w is NULL");
   if (zA < 0 || zA > 255) return fail(IGC_EINVAL, "zA=%d outside [0, 255]", zA);
   if (zB < -128 || zB > 127) return fail(IGC_EINVAL, "zB=%d outside [-128, 127]", zB);
-  if (!ep) return fail(IGC_EINVAL, "epilogue descriptor is NULL");
-  if (!ep->C_i32 && !ep->D_f32 && !ep->Q_i8) return fail(IGC_EINVAL, "no output requested");
-  if (p.K > 33025) return fail(IGC_EOVERFLOW, "K=R*S*C=%d > 33025 can overflow int32", p.K);
-  const int N = Kout;
-  if (ep->C_i32 && ep->ldc < N) return fail(IGC_EINVAL, "ldc=%d < Kout=%d", ep->ldc, N);
-  if (ep->D_f32 && ep->ldd < N) return fail(IGC_EINVAL, "ldd=%d < Kout=%d", ep->ldd, N);
-  if (ep->Q_i8) {
-    if (ep->ldq < N) return fail(IGC_EINVAL, "ldq=%d < Kout=%d", ep->ldq, N);
-    if (!ep->scale_n || !ep->bias_n) return fail(IGC_EINVAL, "Q_i8 needs scale_n and bias_n");
-  }
-  int dev;
-  if (int s = check_device(&dev)) return s;
+  if (int s = check_epilogue(ep, Kout, p.K)) return s;
   p.A = x; p.lda = 0;
   p.B = reinterpret_cast<const uint8_t*>(w); p.ldb = p.K;
   p.zAp = zA - 128; p.zB = zB;
-  p.Ci = ep->C_i32; p.ldci = ep->ldc;
-  p.D = ep->D_f32; p.ldd = ep->ldd; p.dq = ep->dq_scale;
-  p.Qo = ep->Q_i8; p.ldq = ep->ldq; p.scale = ep->scale_n; p.bias = ep->bias_n;
-  p.vec_c = aligned16(ep->C_i32) && ep->ldc % 4 == 0;
-  p.vec_d = aligned16(ep->D_f32) && ep->ldd % 4 == 0;
-  p.vec_q = (reinterpret_cast<uintptr_t>(ep->Q_i8) & 3u) == 0 && ep->ldq % 4 == 0;
+  epilogue_params(p, ep);
   // whole 128-channel K tiles within one tap: the uniform-tap loader
   const bool fast = aligned16(x) && aligned16(w) && C % 128 == 0 && (long long)R * S <= 31 &&
                     nx < (1LL << 31) && 256LL * p.K < (1LL << 31);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  return launch_u8i8<igc::KIND_U8I8_CONV>(p, fast, st, dev);
+  return launch_u8i8<igc::KIND_U8I8_CONV>(p, fast, ep->workspace, ep->ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int conv2d_implicit_gemm_workspace_size(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h,
+                                        int stride_w, int pad_h, int pad_w, size_t* bytes) {
+  g_last_error[0] = 0;
+  igc::Params p = zero_params();
+  long long nx = 0;
+  if (int st = conv_params(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, p, &nx)) return st;
+  return query_workspace(igc::KIND_F16_CONV, p.M, p.N, p.K, bytes);
 }
 
 int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h,
                          int stride_w, int pad_h, int pad_w, const void* x, const void* w, float* y,
-                         void* stream) {
+                         void* workspace, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
   igc::Params p = zero_params();
   long long nx = 0;
   if (int st = conv_params(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, p, &nx)) return st;
   if (!x || !w || !y) return fail(IGC_EINVAL, "x, w or y is NULL");
-  int dev;
-  if (int s = check_device(&dev)) return s;
   p.A = static_cast<const uint8_t*>(x); p.lda = 0;
   p.B = static_cast<const uint8_t*>(w); p.ldb = p.K;
   p.Cf = y; p.ldcf = Kout;
   p.vec_c = aligned16(y) && Kout % 4 == 0;
   const bool fast = aligned16(x) && aligned16(w) && C % 8 == 0 && nx * 2 < (1LL << 31) &&
                     256LL * p.K * 2 < (1LL << 31);
+  hipStream_t st = static_cast<hipStream_t>(stream);
   // whole 64-channel K tiles within one tap: the uniform-tap loader
   if (fast && C % 64 == 0 && (long long)R * S <= 31)
-    return launch<igc::KIND_F16_CONV_C64, 0>(p, true, static_cast<hipStream_t>(stream), dev);
-  return launch<igc::KIND_F16_CONV, 0>(p, fast, static_cast<hipStream_t>(stream), dev);
+    return plan_and_launch<igc::KIND_F16_CONV_C64, 0>(p, true, workspace, ws_bytes, st);
+  return plan_and_launch<igc::KIND_F16_CONV, 0>(p, fast, workspace, ws_bytes, st);
 }
 
 }  // extern "C"

@@ -1,16 +1,16 @@
 // igc_host.hpp -- host side of a launch, shared by the C ABI (igc.hip) and
-// the launch units (igc_launch.hip): tile-variant choice, the stream-K split
-// and the kernel launch on the caller's stream.  launch<KIND, SUMS> is
-// instantiated in igc_launch.hip, once per kernel kind, so that the kinds
-// compile in parallel; igc.hip only calls it.
+// the launch units (igc_launch.hip): the launch plan (tile variant, stream-K
+// split, workspace bytes) and the kernel launch on the caller's stream.
+// launch<KIND, SUMS> is instantiated in igc_launch.hip, once per kernel kind,
+// so that the kinds compile in parallel; igc.hip plans and calls it.
 #pragma once
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstddef>
 #include <cstdint>
-#include <cstdlib>
 
 #include "../../include/igc.h"
 #include "igc_kernels.hpp"
@@ -19,11 +19,8 @@ namespace igc_host {
 
 constexpr int kMaxDevices = 64;
 
-// Defined in igc.hip: the thread's error detail, the per-device compute-unit
-// count and the per-(device, stream) stream-K workspace.
+// Defined in igc.hip: the thread's error detail.
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
-int device_cus(int dev);
-int sk_workspace(int dev, hipStream_t stream, size_t ws_bytes, size_t cnt_n, float** ws, int** cnt);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -41,14 +38,24 @@ enum Variant {
   V_COUNT = 6
 };
 
-inline int forced_variant() {
-  const char* s = std::getenv("IGC_FORCE_VARIANT");
-  if (!s || !*s) return V_AUTO;
-  int v = std::atoi(s);
-  return (v >= 0 && v < V_COUNT) ? v : V_AUTO;
-}
+// Process-wide tuning overrides set by igc_set_tuning (tests and sweeps):
+// a forced variant (V_AUTO: the shape decides) and the stream-K mode
+// (0 never split, 1 split where it pays, 2 split whenever a round is partial).
+extern std::atomic<int> g_force_variant;
+extern std::atomic<int> g_streamk_mode;
 
 inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+inline void variant_tile(int v, int& bm, int& bn) {
+  switch (v) {
+    case V_256x256: bm = 256; bn = 256; return;
+    case V_224x256: bm = 224; bn = 256; return;
+    case V_256x128: bm = 256; bn = 128; return;
+    case V_128x128: bm = 128; bn = 128; return;
+    case V_BYPASS: bm = 32; bn = 32; return;
+    default: bm = 64; bn = 64; return;
+  }
+}
 
 // Large problems run on one workgroup per compute unit, in rounds of `cus`
 // tiles, so their time goes as (rounds) x (tile area).  224 x 256 tiles are
@@ -56,8 +63,6 @@ inline long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 // (the 256 x 14 x 14 conv) needs 392 tiles of 256 rows, two rounds with the
 // second 53% full, but 448 tiles of 224 rows, two rounds of 7/8 the work.
 inline int choose_variant(int M, int N, int cus) {
-  int f = forced_variant();
-  if (f != V_AUTO) return f;
   const long long t256 = ceil_div(M, 256) * ceil_div(N, 256);
   if (t256 >= 192) {
     const long long t224 = ceil_div(M, 224) * ceil_div(N, 256);
@@ -75,56 +80,96 @@ inline int choose_variant(int M, int N, int cus) {
 // It pays only when the idle part of the last round is worth more than the
 // cost of publishing and summing the partial tiles, measured on MI355X at
 // about 26 K-tile iterations (4096^2 conv tiles: 392 tiles on 256 CUs, 36
-// iterations each, ran 12% slower split).  IGC_STREAMK=0 never splits,
-// IGC_STREAMK=2 splits whenever the last round is partial (tests).
-inline int streamk_mode() {
-  const char* s = std::getenv("IGC_STREAMK");
-  if (s && s[0] == '0') return 0;
-  if (s && s[0] == '2') return 2;
-  return 1;
-}
+// iterations each, ran 12% slower split).
 constexpr long long kStreamKFixupIters = 26;
 
-template <int KIND, int BM, int BN, int WM, int WN, bool FAST, int SUMS, int DEPTH = 2>
-int launch_one(igc::Params p, hipStream_t stream) {
-  p.tiles_m = (int)ceil_div(p.M, BM);
-  p.tiles_n = (int)ceil_div(p.N, BN);
-  long long grid = (long long)p.tiles_m * p.tiles_n;
-  if (grid > 0x7fffffffLL) return fail(IGC_EUNSUPPORTED, "too many tiles (%lld)", grid);
-  p.dp_tiles = (int)grid;
-  {
-    int d = 0;
-    const long long cus = (hipGetDevice(&d) == hipSuccess && d >= 0 && d < kMaxDevices) ? device_cus(d) : 256;
-    p.xcd_regroup = grid > cus;  // several rounds of workgroups per compute unit
+// Everything a launch needs to know before it enqueues anything; a pure
+// function of the problem, the device's compute-unit count and the tuning
+// overrides, so the workspace-size queries and the launches agree.
+struct Plan {
+  int variant = V_64x64;
+  int bm = 64, bn = 64;
+  int tiles_m = 0, tiles_n = 0;
+  long long grid = 0;     // workgroups launched
+  int dp_tiles = 0;       // whole-tile workgroups
+  int sk_wgs = 0;         // stream-K workgroups after them
+  long long sk_iters = 0; // K-tile iterations they share
+  int xcd_regroup = 0;
+  size_t cnt_bytes = 0;   // arrival counters at the start of the workspace (256-byte multiple)
+  size_t ws_bytes = 0;    // total workspace the launch uses (0: none)
+};
+
+// kind: igc::Kind; fast: the aligned (direct-to-LDS) loaders apply; ws_ok:
+// a workspace may be used (the caller passed one).  EB = bytes per element.
+inline Plan make_plan(int kind, int M, int N, int K, bool fast, int cus, bool ws_ok) {
+  Plan pl;
+  const int fv = g_force_variant.load(std::memory_order_relaxed);
+  const bool int8 = kind == igc::KIND_U8I8_GEMM || kind == igc::KIND_U8I8_CONV;
+  int v;
+  if (kind == igc::KIND_F16_GEMM && fast &&
+      (fv == V_BYPASS ||
+       (fv == V_AUTO && ceil_div(M, 32) * ceil_div(N, 32) <= cus && K <= 512))) {
+    // The LDS-bypass kernel wins only where the whole problem is one short
+    // round: measured on MI355X, 256^3 3.6 us against 4.1 (64x64 tiles),
+    // 512^3 4.8 against 4.9, but 1024^3 16.4 against 6.6 and 256x256x4096
+    // 23.5 against 14.2 (a single wave then walks a long K loop alone).
+    v = V_BYPASS;
+  } else {
+    v = fv == V_AUTO ? choose_variant(M, N, cus) : fv;
+    if (v == V_BYPASS) v = V_64x64;  // (forced, for a kind or shape without the bypass kernel)
+    // The element-wise (unaligned) loaders need more registers; they stop at 128x128.
+    if (!fast && (v == V_256x256 || v == V_256x128 || v == V_224x256)) v = V_128x128;
   }
-  p.sk_wgs = 0;
-  p.sk_iters = 0;
-  if constexpr (BM == 256 && BN == 256 && FAST && SUMS == 0 && KIND != igc::KIND_U8I8_GEMM && KIND != igc::KIND_U8I8_CONV) {
-    int dev = 0;
-    const int mode = streamk_mode();
-    if (mode && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) {
-      const long long cus = device_cus(dev);
-      const long long nk = ceil_div((long long)p.K * 2, igc::KT_BYTES);
-      // iterations the last round leaves idle, per compute unit
-      const long long idle = (cus - grid % cus) * nk / cus;
-      if (grid > cus && grid % cus != 0 && nk >= 4 && (mode == 2 || idle > kStreamKFixupIters)) {
-        const long long dp = grid / cus * cus;
-        const long long iters = (grid - dp) * nk;
-        const long long wgs = std::min(cus, std::max(1LL, iters / 4));
-        float* ws = nullptr;
-        int* cnt = nullptr;
-        if (int st = sk_workspace(dev, stream, (size_t)(2 * wgs * BM * BN * 4), (size_t)(grid - dp), &ws, &cnt))
-          return st;
-        p.dp_tiles = (int)dp;
-        p.sk_wgs = (int)wgs;
-        p.sk_iters = iters;
-        p.ws = ws;
-        p.cnt = cnt;
-        grid = dp + wgs;
-      }
+  pl.variant = v;
+  variant_tile(v, pl.bm, pl.bn);
+  pl.tiles_m = (int)ceil_div(M, pl.bm);
+  pl.tiles_n = (int)ceil_div(N, pl.bn);
+  const long long grid = (long long)pl.tiles_m * pl.tiles_n;
+  pl.grid = grid;
+  pl.dp_tiles = (int)std::min(grid, 0x7fffffffLL);
+  pl.xcd_regroup = grid > cus;  // several rounds of workgroups per compute unit
+  const int mode = g_streamk_mode.load(std::memory_order_relaxed);
+  if (v == V_256x256 && fast && !int8 && ws_ok && mode != 0) {
+    const long long nk = ceil_div((long long)K * 2, igc::KT_BYTES);
+    // iterations the last round leaves idle, per compute unit
+    const long long idle = (cus - grid % cus) * nk / cus;
+    if (grid > cus && grid % cus != 0 && nk >= 4 && (mode == 2 || idle > kStreamKFixupIters)) {
+      const long long dp = grid / cus * cus;
+      const long long iters = (grid - dp) * nk;
+      const long long wgs = std::min((long long)cus, std::max(1LL, iters / 4));
+      pl.dp_tiles = (int)dp;
+      pl.sk_wgs = (int)wgs;
+      pl.sk_iters = iters;
+      pl.grid = dp + wgs;
+      pl.cnt_bytes = (size_t)ceil_div((grid - dp) * 4, 256) * 256;
+      pl.ws_bytes = pl.cnt_bytes + (size_t)(2 * wgs) * (size_t)(pl.bm * pl.bn * 4);
     }
   }
-  hipLaunchKernelGGL((igc::gemm_kernel<KIND, BM, BN, WM, WN, FAST, SUMS, DEPTH>), dim3((unsigned)grid),
+  return pl;
+}
+
+// Fills the split and workspace fields of p from the plan; ws is the
+// caller's workspace (used only when the plan needs one).
+inline void apply_plan(igc::Params& p, const Plan& pl, void* ws) {
+  p.tiles_m = pl.tiles_m;
+  p.tiles_n = pl.tiles_n;
+  p.dp_tiles = pl.dp_tiles;
+  p.xcd_regroup = pl.xcd_regroup;
+  p.sk_wgs = pl.sk_wgs;
+  p.sk_iters = pl.sk_iters;
+  if (pl.ws_bytes) {
+    p.cnt = static_cast<int*>(ws);
+    p.ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.cnt_bytes);
+  } else {
+    p.cnt = nullptr;
+    p.ws = nullptr;
+  }
+}
+
+template <int KIND, int BM, int BN, int WM, int WN, bool FAST, int SUMS, int DEPTH = 2>
+int launch_one(const igc::Params& p, const Plan& pl, hipStream_t stream) {
+  if (pl.grid > 0x7fffffffLL) return fail(IGC_EUNSUPPORTED, "too many tiles (%lld)", pl.grid);
+  hipLaunchKernelGGL((igc::gemm_kernel<KIND, BM, BN, WM, WN, FAST, SUMS, DEPTH>), dim3((unsigned)pl.grid),
                      dim3(64 * WM * WN), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -132,54 +177,43 @@ int launch_one(igc::Params p, hipStream_t stream) {
 }
 
 template <int KIND, bool FAST, int SUMS>
-int launch_variant(int v, const igc::Params& p, hipStream_t stream) {
-  switch (v) {
+int launch_variant(const igc::Params& p, const Plan& pl, hipStream_t stream) {
+  switch (pl.variant) {
     case V_224x256:
-      if constexpr (FAST) return launch_one<KIND, 224, 256, 2, 2, FAST, SUMS>(p, stream);
-      [[fallthrough]];
+      if constexpr (FAST) return launch_one<KIND, 224, 256, 2, 2, FAST, SUMS>(p, pl, stream);
+      break;
     case V_256x256:
-      if constexpr (FAST) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, stream);
-      [[fallthrough]];
+      if constexpr (FAST) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, pl, stream);
+      break;
     case V_256x128:
-      if constexpr (FAST) return launch_one<KIND, 256, 128, 2, 2, FAST, SUMS>(p, stream);
-      [[fallthrough]];
-    case V_128x128: return launch_one<KIND, 128, 128, 2, 2, FAST, SUMS>(p, stream);
-    default: return launch_one<KIND, 64, 64, 2, 2, FAST, SUMS>(p, stream);
+      if constexpr (FAST) return launch_one<KIND, 256, 128, 2, 2, FAST, SUMS>(p, pl, stream);
+      break;
+    case V_128x128: return launch_one<KIND, 128, 128, 2, 2, FAST, SUMS>(p, pl, stream);
+    case V_64x64: return launch_one<KIND, 64, 64, 2, 2, FAST, SUMS>(p, pl, stream);
+    default: break;
   }
+  return fail(IGC_EUNSUPPORTED, "internal: variant %d not compiled for this operand form", pl.variant);
 }
 
-inline int launch_bypass(igc::Params p, hipStream_t stream) {
-  p.tiles_m = (int)ceil_div(p.M, 32);
-  p.tiles_n = (int)ceil_div(p.N, 32);
-  const long long grid = (long long)p.tiles_m * p.tiles_n;
-  if (grid > 0x7fffffffLL) return fail(IGC_EUNSUPPORTED, "too many tiles (%lld)", grid);
-  hipLaunchKernelGGL((igc::gemm_f16_bypass_kernel<8>), dim3((unsigned)grid), dim3(64), 0, stream, p);
+inline int launch_bypass(const igc::Params& p, const Plan& pl, hipStream_t stream) {
+  if (pl.grid > 0x7fffffffLL) return fail(IGC_EUNSUPPORTED, "too many tiles (%lld)", pl.grid);
+  hipLaunchKernelGGL((igc::gemm_f16_bypass_kernel<8>), dim3((unsigned)pl.grid), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return IGC_OK;
 }
 
+// p carries the problem, its outputs and the plan's split (apply_plan).
 template <int KIND, int SUMS>
-int launch(const igc::Params& p, bool fast, hipStream_t stream, int dev) {
+int launch(const igc::Params& p, const Plan& pl, bool fast, hipStream_t stream) {
   if constexpr (KIND == igc::KIND_F16_GEMM) {
-    // The LDS-bypass kernel wins only where the whole problem is one short
-    // round: measured on MI355X, 256^3 3.6 us against 4.1 (64x64 tiles), 512^3
-    // 4.8 against 4.9, but 1024^3 16.4 against 6.6 and 256x256x4096 23.5
-    // against 14.2 (a single wave then walks a long K loop alone).
-    const int fv = forced_variant();
-    const bool small = ceil_div(p.M, 32) * ceil_div(p.N, 32) <= device_cus(dev) && p.K <= 512;
-    if (fast && (fv == V_BYPASS || (fv == V_AUTO && small))) return launch_bypass(p, stream);
+    if (pl.variant == V_BYPASS) return launch_bypass(p, pl, stream);
   }
-  const int cus = device_cus(dev);
-  int v = choose_variant(p.M, p.N, cus);
-  if (v == V_BYPASS) v = V_64x64;  // (forced, for a kind or shape without the bypass kernel)
-  // The element-wise (unaligned) loaders need more registers; they stop at 128x128.
-  if (!fast && (v == V_256x256 || v == V_256x128 || v == V_224x256)) v = V_128x128;
   if constexpr (KIND == igc::KIND_F16_CONV_C64) {
-    return launch_variant<KIND, true, SUMS>(v, p, stream);  // dispatched only with aligned operands
+    return launch_variant<KIND, true, SUMS>(p, pl, stream);  // dispatched only with aligned operands
   } else {
-    return fast ? launch_variant<KIND, true, SUMS>(v, p, stream)
-                : launch_variant<KIND, false, SUMS>(v, p, stream);
+    return fast ? launch_variant<KIND, true, SUMS>(p, pl, stream)
+                : launch_variant<KIND, false, SUMS>(p, pl, stream);
   }
 }
 
@@ -199,7 +233,7 @@ int launch(const igc::Params& p, bool fast, hipStream_t stream, int dev) {
   X(10, igc::KIND_U8I8_CONV, 3)
 
 #define IGC_EXTERN_LAUNCH(n, K, S) \
-  extern template int launch<K, S>(const igc::Params&, bool, hipStream_t, int);
+  extern template int launch<K, S>(const igc::Params&, const Plan&, bool, hipStream_t);
 IGC_LAUNCH_KINDS(IGC_EXTERN_LAUNCH)
 #undef IGC_EXTERN_LAUNCH
 

@@ -7,37 +7,37 @@
 namespace igc_host {
 
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 0
-template int launch<igc::KIND_F16_GEMM, 0>(const igc::Params&, bool, hipStream_t, int);
+template int launch<igc::KIND_F16_GEMM, 0>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 1
-template int launch<igc::KIND_F16_CONV, 0>(const igc::Params&, bool, hipStream_t, int);
+template int launch<igc::KIND_F16_CONV, 0>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 2
-template int launch<igc::KIND_F16_CONV_C64, 0>(const igc::Params&, bool, hipStream_t, int);
+template int launch<igc::KIND_F16_CONV_C64, 0>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 3
-template int launch<igc::KIND_U8I8_GEMM, 0>(const igc::Params&, bool, hipStream_t, int);
+template int launch<igc::KIND_U8I8_GEMM, 0>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 4
-template int launch<igc::KIND_U8I8_GEMM, 1>(const igc::Params&, bool, hipStream_t, int);
+template int launch<igc::KIND_U8I8_GEMM, 1>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 5
-template int launch<igc::KIND_U8I8_GEMM, 2>(const igc::Params&, bool, hipStream_t, int);
+template int launch<igc::KIND_U8I8_GEMM, 2>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 6
-template int launch<igc::KIND_U8I8_GEMM, 3>(const igc::Params&, bool, hipStream_t, int);
+template int launch<igc::KIND_U8I8_GEMM, 3>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 7
-template int launch<igc::KIND_U8I8_CONV, 0>(const igc::Params&, bool, hipStream_t, int);
+template int launch<igc::KIND_U8I8_CONV, 0>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 8
-template int launch<igc::KIND_U8I8_CONV, 1>(const igc::Params&, bool, hipStream_t, int);
+template int launch<igc::KIND_U8I8_CONV, 1>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 9
-template int launch<igc::KIND_U8I8_CONV, 2>(const igc::Params&, bool, hipStream_t, int);
+template int launch<igc::KIND_U8I8_CONV, 2>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 10
-template int launch<igc::KIND_U8I8_CONV, 3>(const igc::Params&, bool, hipStream_t, int);
+template int launch<igc::KIND_U8I8_CONV, 3>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 
 }  // namespace igc_host

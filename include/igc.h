@@ -11,17 +11,24 @@
  *              with TensorCores.
  *
  * Conventions shared by every entry point
- *  - All buffers are device memory owned by the caller (inputs, outputs and
- *    per-channel vectors).  The library never copies device memory.  Its only
- *    state is a per-device cache of the architecture and compute-unit count
- *    and, for fp16 launches whose last round of 256x256 tiles is split
- *    between workgroups (stream-K), a workspace per (device, stream) that it
- *    allocates on first use, grows when needed and keeps until the process
- *    ends.
- *  - Environment (tests, tuning): IGC_FORCE_VARIANT=0..5 pins a kernel
- *    variant, IGC_STREAMK=0 / 2 disables / forces the stream-K split.
- *  - Argument validation is synchronous and happens before any HIP call; a
- *    rejected call has no side effects.
+ *  - All buffers are device memory owned by the caller: inputs, outputs,
+ *    per-channel vectors and the optional workspace.  The library never
+ *    allocates, frees or copies device memory.  Its only state is a
+ *    per-device cache of the architecture and compute-unit count and the
+ *    process-wide tuning overrides of igc_set_tuning.
+ *  - Workspace.  A call may split the K loop of some output tiles between
+ *    workgroups (stream-K) and sum their partial tiles through a caller-owned
+ *    workspace.  <entry>_workspace_size() returns the bytes a call of that
+ *    shape needs on the current device (0: none).  Pass a 16-byte aligned
+ *    device buffer of at least that size, zero-filled before its first use;
+ *    every call leaves it zero-filled again in the part that must start at
+ *    zero.  With workspace == NULL the call runs without the split (same
+ *    results, possibly slower).  A non-NULL workspace smaller than needed is
+ *    rejected with IGC_EINVAL.  Calls that overlap in time (different
+ *    streams) must not share a workspace.
+ *  - Argument validation is synchronous and happens before any HIP call,
+ *    except the workspace-size check, which needs the device's compute-unit
+ *    count; a rejected call has no side effects.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns without waiting.  The caller synchronizes.
  *  - Outputs must not alias inputs.  Calls on different streams that write the
@@ -62,15 +69,26 @@ extern "C" {
  * Every product of two fp16 values is exact in fp32; the K-sum is accumulated
  * in fp32 (summation order is unspecified).  Any alignment and any lda/ldb is
  * accepted; 16-byte aligned A/B with lda, ldb and K multiples of 8 take the
- * fast path.
+ * fast path.  workspace / ws_bytes: the optional caller-owned workspace of
+ * the conventions above (NULL / 0 for none).
  * Errors: IGC_EINVAL (negative size, NULL pointer with a non-empty operand,
- * lda < K, ldb < K, ldc < N), IGC_ENODEV, IGC_EHIP.
+ * lda < K, ldb < K, ldc < N, workspace too small or misaligned), IGC_ENODEV,
+ * IGC_EHIP.
  */
 int gemm_f16f32(int M, int N, int K,
                 const void* A, int lda,
                 const void* B, int ldb,
                 float* C, int ldc,
+                void* workspace, size_t ws_bytes,
                 void* stream);
+
+/*
+ * gemm_f16f32_workspace_size -- *bytes = the workspace gemm_f16f32 needs for
+ * an M x N x K problem on the current device (0 when it never splits a tile;
+ * an upper bound: a call whose operands take the element-wise path needs
+ * none).  Errors: IGC_EINVAL (negative size, bytes NULL), IGC_ENODEV.
+ */
+int gemm_f16f32_workspace_size(int M, int N, int K, size_t* bytes);
 
 /*
  * Outputs of gemm_u8i8_zp.  Any non-empty subset may be requested in one call;
@@ -87,6 +105,9 @@ int gemm_f16f32(int M, int N, int K,
  *                   scale_n and bias_n are fp32 device vectors of length N and
  *                   are required when Q_i8 is requested.
  *
+ *   workspace,      optional caller-owned workspace (see the conventions above
+ *   ws_bytes        and gemm_u8i8_zp_workspace_size); NULL / 0 for none.
+ *
  * Int -> fp32 conversions round to nearest even; the two fp32 operations of
  * the requantize step are separately rounded (no fused multiply-add).
  */
@@ -100,6 +121,8 @@ typedef struct igc_u8i8_epilogue {
   int ldq;
   const float* scale_n;
   const float* bias_n;
+  void* workspace;
+  size_t ws_bytes;
 } igc_u8i8_epilogue;
 
 /*
@@ -119,7 +142,7 @@ typedef struct igc_u8i8_epilogue {
  *
  * Errors: IGC_EINVAL (negative size, NULL pointer with a non-empty operand,
  * ld too small, zero point out of range, ep NULL or requesting no output,
- * Q_i8 without scale_n/bias_n), IGC_EOVERFLOW (K > 33025, where
+ * Q_i8 without scale_n/bias_n, workspace too small), IGC_EOVERFLOW (K > 33025, where
  * 255*255*K can exceed the int32 range), IGC_ENODEV, IGC_EHIP.
  */
 int gemm_u8i8_zp(int M, int N, int K,
@@ -127,6 +150,9 @@ int gemm_u8i8_zp(int M, int N, int K,
                  const int8_t* B, int ldb, int zB,
                  const igc_u8i8_epilogue* ep,
                  void* stream);
+
+/* gemm_u8i8_zp_workspace_size -- as gemm_f16f32_workspace_size, for gemm_u8i8_zp. */
+int gemm_u8i8_zp_workspace_size(int M, int N, int K, size_t* bytes);
 
 /*
  * conv2d_implicit_gemm -- 2-D convolution (cross-correlation, no filter flip),
@@ -146,14 +172,23 @@ int gemm_u8i8_zp(int M, int N, int K,
  * GEMM view: M = Nb*P*Q rows (n,p,q), N = Kout, K = R*S*C with
  * k = (r*S + s)*C + c; the weight tensor is the column-major B operand.
  * 16-byte aligned x/w with C a multiple of 8 take the fast path.
+ * workspace / ws_bytes: optional, as for gemm_f16f32.
  * Errors: IGC_EINVAL (non-positive dimension or stride, negative padding,
- * NULL pointer, P or Q < 1), IGC_EUNSUPPORTED (an index of x, w or y that
- * does not fit in 32 bits), IGC_ENODEV, IGC_EHIP.
+ * NULL pointer, P or Q < 1, workspace too small), IGC_EUNSUPPORTED (an index
+ * of x, w or y that does not fit in 32 bits; H, W, R, S, pad_h or pad_w of
+ * 32768 or more), IGC_ENODEV, IGC_EHIP.
  */
 int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S,
                          int stride_h, int stride_w, int pad_h, int pad_w,
                          const void* x, const void* w, float* y,
+                         void* workspace, size_t ws_bytes,
                          void* stream);
+
+/* conv2d_implicit_gemm_workspace_size -- as gemm_f16f32_workspace_size, for
+ * conv2d_implicit_gemm (the convolution's arguments are validated as there). */
+int conv2d_implicit_gemm_workspace_size(int Nb, int H, int W, int C, int Kout, int R, int S,
+                                        int stride_h, int stride_w, int pad_h, int pad_w,
+                                        size_t* bytes);
 
 /*
  * conv2d_u8i8_zp -- quantized 2-D convolution: u8 activations x i8 weights
@@ -185,10 +220,30 @@ int conv2d_u8i8_zp(int Nb, int H, int W, int C, int Kout, int R, int S,
                    const uint8_t* x, int zA, const int8_t* w, int zB,
                    const igc_u8i8_epilogue* ep, void* stream);
 
+/* conv2d_u8i8_zp_workspace_size -- as gemm_f16f32_workspace_size, for
+ * conv2d_u8i8_zp. */
+int conv2d_u8i8_zp_workspace_size(int Nb, int H, int W, int C, int Kout, int R, int S,
+                                  int stride_h, int stride_w, int pad_h, int pad_w,
+                                  size_t* bytes);
+
 /* Diagnostics. */
 const char* igc_status_string(int status); /* static string for a status code              */
 const char* igc_last_error(void);          /* detail of this thread's last failure, or ""  */
 int igc_device_check(void);                /* IGC_OK if the current device is gfx950       */
+
+/*
+ * igc_set_tuning -- process-wide overrides for tests and tuning sweeps (not
+ * needed for normal use; the defaults are -1 and 1).  They apply to calls
+ * made after it returns.
+ *   force_variant  -1: the shape chooses the tile; 0: 256x256, 1: 128x128,
+ *                  2: 64x64, 3: 256x128, 4: 224x256, 5: the fp16 LDS-bypass
+ *                  kernel (32x32 tiles).  A tile the operands' path does not
+ *                  have falls back to the nearest smaller one.
+ *   streamk_mode   0: never split tiles; 1: split where it pays; 2: split
+ *                  whenever the last round of tiles is partial.
+ * Errors: IGC_EINVAL (value out of range).
+ */
+int igc_set_tuning(int force_variant, int streamk_mode);
 
 #ifdef __cplusplus
 }

@@ -20,6 +20,23 @@ def fp_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref) / den))
 
 
+def fp_errors(got: np.ndarray, ref: np.ndarray):
+    """(gated error, unfloored element-wise max |x-r|/|r| over r != 0,
+    normwise max|x-r| / max|r|)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0, 0.0, 0.0
+    diff = np.abs(got - ref)
+    nz = ref != 0
+    unfloored = float(np.max(diff[nz] / np.abs(ref[nz]))) if np.any(nz) else 0.0
+    if np.any(~nz & (diff > 0)):
+        unfloored = float("inf")
+    mx = float(np.max(np.abs(ref)))
+    normwise = float(np.max(diff)) / mx if mx > 0 else float(np.max(diff))
+    return fp_rel_err(got, ref), unfloored, normwise
+
+
 def torch_dev():
     import torch
 
@@ -34,6 +51,14 @@ def to_dev(a: np.ndarray):
 def empty_dev(shape, dtype):
     torch, dev = torch_dev()
     return torch.empty(shape, dtype=dtype, device=dev)
+
+
+def workspace_for(nbytes: int):
+    """A zero-filled device workspace of nbytes (None when no workspace is needed)."""
+    if nbytes == 0:
+        return None
+    torch, dev = torch_dev()
+    return torch.zeros(nbytes, dtype=torch.uint8, device=dev)
 
 
 def sync():

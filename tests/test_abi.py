@@ -36,6 +36,19 @@ def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("gemm_f16f32", "gemm_u8i8_zp", "conv2d_implicit_gemm", "conv2d_u8i8_zp"):
         assert name in fns
+        assert name + "_workspace_size" in fns
+
+
+def test_library_allocates_no_device_memory():
+    """The caller owns every device buffer: no HIP allocation, free, memset,
+    copy or synchronization appears in the library's sources."""
+    csrc = os.path.join(ROOT, "implicit_gemm_convolution_amd", "csrc")
+    banned = re.compile(r"\bhip(Malloc\w*|Free\w*|Memset\w*|Memcpy\w*|StreamSynchronize|DeviceSynchronize"
+                        r"|HostMalloc|MallocManaged|ExtMallocWithFlags)\s*\(")
+    for name in os.listdir(csrc):
+        text = open(os.path.join(csrc, name)).read()
+        text = re.sub(r"//[^\n]*", "", text)
+        assert not banned.search(text), (name, banned.search(text).group(0))
 
 
 def test_library_exports_every_declared_symbol(igc):
@@ -110,6 +123,13 @@ def test_conv_validation(igc):
     assert f(x=None) == E
     assert f(R=7, ph=1) == E                           # filter larger than the padded input
     assert f(Nb=1 << 20, H=1 << 10, W=1 << 10, C=8) == igc.IGC_EUNSUPPORTED
+    # coordinates of 2^15 or more do not fit the loaders' 16-bit halves
+    U = igc.IGC_EUNSUPPORTED
+    assert f(H=1, W=40000, C=8, R=1, S=3, ph=0, pw=1) == U
+    assert f(H=32768, W=1, C=8, R=3, S=1, ph=1, pw=0) == U
+    assert f(H=4, W=4, ph=32768, pw=0, R=3, S=3) == U
+    assert f(H=4, W=4, ph=0, pw=40000, R=3, S=3) == U
+    assert "32768" in igc.last_error()
 
 
 def test_qconv_validation(igc):
@@ -132,8 +152,38 @@ def test_qconv_validation(igc):
     assert f(C_i32=None, Q_i8=1, ldq=8) == E           # Q without scale/bias
     assert f(C=3670, R=3, S=3) == igc.IGC_EOVERFLOW    # K = 33030
     assert f(Nb=1 << 20, H=1 << 10, W=1 << 10, C=8) == igc.IGC_EUNSUPPORTED
+    assert f(H=1, W=40000, C=8, R=1, S=3, ph=0, pw=1) == igc.IGC_EUNSUPPORTED
     st = igc.load().conv2d_u8i8_zp(1, 4, 4, 128, 8, 3, 3, 1, 1, 1, 1, 1, 128, 1, 0, None, None)
     assert st == E                                     # NULL epilogue descriptor
+
+
+def test_set_tuning_validation(igc):
+    E = igc.IGC_EINVAL
+    assert igc.set_tuning(-2, 1, check=False) == E
+    assert igc.set_tuning(6, 1, check=False) == E
+    assert igc.set_tuning(-1, 3, check=False) == E
+    assert igc.set_tuning(-1, -1, check=False) == E
+    for v in range(-1, 6):
+        for sk in range(3):
+            assert igc.set_tuning(v, sk, check=False) == igc.IGC_OK
+    assert igc.set_tuning(-1, 1, check=False) == igc.IGC_OK
+
+
+def test_workspace_size_validation(igc):
+    L = igc.load()
+    out = ctypes.c_size_t(7)
+    E = igc.IGC_EINVAL
+    assert L.gemm_f16f32_workspace_size(-1, 4, 4, ctypes.byref(out)) == E
+    assert L.gemm_u8i8_zp_workspace_size(4, 4, -4, ctypes.byref(out)) == E
+    assert L.gemm_f16f32_workspace_size(4, 4, 4, None) == E
+    # an empty problem needs nothing and no device
+    assert L.gemm_f16f32_workspace_size(0, 4, 4, ctypes.byref(out)) == igc.IGC_OK
+    assert out.value == 0
+    conv = (1, 4, 4, 8, 8, 3, 3, 1, 1, 1, 1)
+    bad = (1, 4, 4, 8, 8, 7, 3, 1, 1, 1, 1)  # filter larger than the padded input
+    assert L.conv2d_implicit_gemm_workspace_size(*bad, ctypes.byref(out)) == E
+    assert L.conv2d_u8i8_zp_workspace_size(*bad, ctypes.byref(out)) == E
+    assert L.conv2d_u8i8_zp_workspace_size(*conv, None) == E
 
 
 def test_valid_call_without_gpu_reports_nodev(igc):
@@ -146,3 +196,5 @@ def test_valid_call_without_gpu_reports_nodev(igc):
         pass
     assert igc.gemm_f16f32(4, 4, 8, 16, 8, 16, 8, 16, 4, check=False) == igc.IGC_ENODEV
     assert igc.device_check() == igc.IGC_ENODEV
+    out = ctypes.c_size_t(0)
+    assert igc.load().gemm_f16f32_workspace_size(4096, 4096, 4096, ctypes.byref(out)) == igc.IGC_ENODEV

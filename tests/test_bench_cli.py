@@ -20,3 +20,14 @@ def test_traffic_summary_matches_hash_or_is_ignored():
     t = bench.traffic_for("c3")
     assert t is None or t > 0
     assert bench.traffic_for("no-such-workload") is None
+
+
+def test_host_record_fields():
+    sys.path.insert(0, ROOT)
+    import bench
+
+    info = bench.host_info()
+    assert info["cpus_available"] >= 1
+    assert info["cpu_model"] is None or isinstance(info["cpu_model"], str)
+    v = bench.read_sclk_mhz()
+    assert v is None or v > 0

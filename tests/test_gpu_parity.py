@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_util import FP_TOL, empty_dev, fp_rel_err, strided, to_dev, to_host
+from gpu_util import FP_TOL, empty_dev, fp_rel_err, strided, to_dev, to_host, workspace_for
 
 pytestmark = pytest.mark.gpu
 
@@ -29,13 +29,18 @@ def igc():
     return m
 
 
+@pytest.fixture(autouse=True)
+def _default_tuning(igc):
+    """Every test starts and ends with the library's default tuning."""
+    igc.set_tuning(-1, 1)
+    yield
+    igc.set_tuning(-1, 1)
+
+
 @pytest.fixture
-def variant(request, monkeypatch):
+def variant(request, igc):
     v = getattr(request, "param", None)
-    if v is None:
-        monkeypatch.delenv("IGC_FORCE_VARIANT", raising=False)
-    else:
-        monkeypatch.setenv("IGC_FORCE_VARIANT", v)
+    igc.set_tuning(-1 if v is None else int(v), 1)
     return v
 
 
@@ -50,7 +55,7 @@ def run_f16(igc, A, Bt, lda=None, ldb=None, ldc=None, sentinel=np.nan):
     dA = to_dev(strided(A, lda)) if M else empty_dev((0,), torch.float16)
     dB = to_dev(strided(Bt, ldb)) if N else empty_dev((0,), torch.float16)
     dC = to_dev(np.full((M, ldc), sentinel, np.float32))
-    igc.gemm_f16f32(M, N, K, dA, lda, dB, ldb, dC, ldc)
+    igc.gemm_f16f32(M, N, K, dA, lda, dB, ldb, dC, ldc, workspace=workspace_for(igc.gemm_f16f32_workspace_size(M, N, K)))
     C = to_host(dC)
     if ldc > N:  # columns past N are never written
         pad = C[:, N:]
@@ -77,8 +82,8 @@ def test_f16_integer_valued_bit_exact(igc, oracle, variant, M, N, K):
 # The LDS-bypass fp16 kernel (forced): 32x32 tiles, one wave each, operands
 # loaded straight into the MFMA registers.
 @pytest.mark.parametrize("M,N,K", F16_EXACT_SHAPES + [(256, 256, 1024), (70, 33, 520)])
-def test_f16_bypass_integer_valued_bit_exact(igc, oracle, monkeypatch, M, N, K):
-    monkeypatch.setenv("IGC_FORCE_VARIANT", "5")
+def test_f16_bypass_integer_valued_bit_exact(igc, oracle, M, N, K):
+    igc.set_tuning(5, 1)
     rng = np.random.default_rng(M * 131 + N * 7 + K)
     A = synth.f16_small_ints(rng, (M, K))
     Bt = synth.f16_small_ints(rng, (N, K))
@@ -87,8 +92,8 @@ def test_f16_bypass_integer_valued_bit_exact(igc, oracle, monkeypatch, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,ldc", [(256, 256, 256, 256), (200, 300, 1000, 301), (64, 48, 4096, 48)])
-def test_f16_bypass_random_tolerance(igc, oracle, monkeypatch, M, N, K, ldc):
-    monkeypatch.setenv("IGC_FORCE_VARIANT", "5")
+def test_f16_bypass_random_tolerance(igc, oracle, M, N, K, ldc):
+    igc.set_tuning(5, 1)
     rng = np.random.default_rng(M + N + K + 5)
     A = synth.f16_uniform(rng, (M, K))
     Bt = synth.f16_uniform(rng, (N, K))
@@ -100,8 +105,8 @@ def test_f16_bypass_random_tolerance(igc, oracle, monkeypatch, M, N, K, ldc):
 # edges, long K loops) and of several rounds (289-1156 tiles).
 @pytest.mark.parametrize("variant,M,N,K", [("2", 1088, 1088, 264), ("1", 2176, 2176, 136),
                                            ("2", 200, 136, 2056), ("1", 300, 260, 1160)])
-def test_f16_small_tiles_one_and_several_rounds(igc, oracle, monkeypatch, variant, M, N, K):
-    monkeypatch.setenv("IGC_FORCE_VARIANT", variant)
+def test_f16_small_tiles_one_and_several_rounds(igc, oracle, variant, M, N, K):
+    igc.set_tuning(int(variant), 1)
     rng = np.random.default_rng(M + N + K + 1)
     A = synth.f16_small_ints(rng, (M, K))
     Bt = synth.f16_small_ints(rng, (N, K))
@@ -111,8 +116,8 @@ def test_f16_small_tiles_one_and_several_rounds(igc, oracle, monkeypatch, varian
 
 @pytest.mark.parametrize("variant,M,N,K", [("2", 1088, 1088, 400), ("1", 2176, 2176, 144),
                                            ("2", 130, 70, 3000), ("1", 300, 260, 2064)])
-def test_u8i8_small_tiles_one_and_several_rounds(igc, oracle, monkeypatch, variant, M, N, K):
-    monkeypatch.setenv("IGC_FORCE_VARIANT", variant)
+def test_u8i8_small_tiles_one_and_several_rounds(igc, oracle, variant, M, N, K):
+    igc.set_tuning(int(variant), 1)
     rng = np.random.default_rng(M + N + K + 2)
     A = synth.u8_uniform(rng, (M, K))
     Bt = synth.i8_uniform(rng, (N, K))
@@ -195,7 +200,8 @@ def run_u8i8(igc, A, zA, Bt, zB, outputs=("C", "D", "Q"), scale=None, bias=None,
         dBi = to_dev(bias.astype(np.float32))
         out["_keep"] = (dS, dBi)
         kw.update(Q_i8=out["Q"], ldq=N, scale_n=dS, bias_n=dBi)
-    igc.gemm_u8i8_zp(M, N, K, dA, lda, zA, dB, ldb, zB, **kw)
+    igc.gemm_u8i8_zp(M, N, K, dA, lda, zA, dB, ldb, zB,
+                     workspace=workspace_for(igc.gemm_u8i8_zp_workspace_size(M, N, K)), **kw)
     return {k: to_host(v) for k, v in out.items() if not k.startswith("_")}
 
 
@@ -308,7 +314,9 @@ def run_conv(igc, x, w, stride, pad):
     dx = to_dev(x)
     dw = to_dev(w)
     dy = empty_dev((Nb, P, Q, Kout), torch.float32)
-    igc.conv2d_implicit_gemm(Nb, H, W, C, Kout, R, S, stride[0], stride[1], pad[0], pad[1], dx, dw, dy)
+    dims = (Nb, H, W, C, Kout, R, S, stride[0], stride[1], pad[0], pad[1])
+    igc.conv2d_implicit_gemm(*dims, dx, dw, dy,
+                             workspace=workspace_for(igc.conv2d_implicit_gemm_workspace_size(*dims)))
     return to_host(dy)
 
 
@@ -374,11 +382,13 @@ def test_conv_impulse(igc):
 # rounds: the last tiles are shared between workgroups and summed through the
 # workspace.  The shared tiles are the last ones in the tile order, i.e. the
 # last tile rows here.
-def _sk_run(igc, A, Bt, monkeypatch, on):
+def _sk_run(igc, A, Bt, on):
     # (stream-K runs on the 256x256 tiles; at these shapes the default choice
     # would be 224x256 tiles)
-    monkeypatch.setenv("IGC_FORCE_VARIANT", "0")
-    monkeypatch.setenv("IGC_STREAMK", "2" if on else "0")
+    igc.set_tuning(0, 2 if on else 0)
+    if on:
+        M, K = A.shape
+        assert igc.gemm_f16f32_workspace_size(M, Bt.shape[0], K) > 0
     return run_f16(igc, A, Bt)
 
 
@@ -387,28 +397,58 @@ def _sk_run(igc, A, Bt, monkeypatch, on):
     (4352, 4096, 1024),  # 272 tiles: 16 shared, four workgroups each
     (4352, 4096, 648),   # partial K tile first, 11 K tiles
 ])
-def test_streamk_integer_valued_exact(igc, oracle, monkeypatch, M, N, K):
+def test_streamk_integer_valued_exact(igc, oracle, M, N, K):
     rng = np.random.default_rng(M + N + K)
     A = synth.f16_small_ints(rng, (M, K))
     Bt = synth.f16_small_ints(rng, (N, K))
-    C = _sk_run(igc, A, Bt, monkeypatch, True)
-    C0 = _sk_run(igc, A, Bt, monkeypatch, False)
+    C = _sk_run(igc, A, Bt, True)
+    C0 = _sk_run(igc, A, Bt, False)
     assert np.array_equal(C, C0)
     rows = np.array(sorted({4095, 4096, 4097, M - 1} | set(rng.integers(4096, M, 24).tolist())
                            | set(rng.integers(0, 4096, 8).tolist())))
     assert np.array_equal(C[rows].astype(np.float64), oracle.gemm_f16(A[rows], Bt))
 
 
-def test_streamk_random_tolerance_and_deterministic(igc, oracle, monkeypatch):
+def test_streamk_random_tolerance_and_deterministic(igc, oracle):
     M, N, K = 6144, 4096, 1024
     rng = np.random.default_rng(17)
     A = synth.f16_normal(rng, (M, K))
     Bt = synth.f16_normal(rng, (N, K))
-    C1 = _sk_run(igc, A, Bt, monkeypatch, True)
-    C2 = _sk_run(igc, A, Bt, monkeypatch, True)
+    C1 = _sk_run(igc, A, Bt, True)
+    C2 = _sk_run(igc, A, Bt, True)
     assert np.array_equal(C1, C2)
     rows = np.array(sorted({4096, M - 1} | set(rng.integers(4096, M, 16).tolist())))
     assert fp_rel_err(C1[rows], oracle.gemm_f16(A[rows], Bt)) <= FP_TOL
+
+
+def test_streamk_workspace_contract(igc, oracle):
+    """The split needs the caller's workspace: a workspace smaller than the
+    query's size is rejected before anything is launched, no workspace runs
+    the whole-tile path (same results), and one zero-filled workspace serves
+    consecutive calls (the kernel leaves its counters at zero)."""
+    import torch
+
+    M, N, K = 4352, 4096, 1024
+    rng = np.random.default_rng(23)
+    A = synth.f16_small_ints(rng, (M, K))
+    Bt = synth.f16_small_ints(rng, (N, K))
+    igc.set_tuning(0, 2)
+    need = igc.gemm_f16f32_workspace_size(M, N, K)
+    assert need > 0
+    dA, dB = to_dev(A), to_dev(Bt)
+    dC = empty_dev((M, N), torch.float32)
+    small = workspace_for(need - 16)
+    st = igc.gemm_f16f32(M, N, K, dA, K, dB, K, dC, N, workspace=small, check=False)
+    assert st == igc.IGC_EINVAL and "workspace" in igc.last_error()
+    igc.gemm_f16f32(M, N, K, dA, K, dB, K, dC, N)  # no workspace: whole tiles
+    C0 = to_host(dC).copy()
+    ws = workspace_for(need)
+    for _ in range(3):
+        dC.fill_(float("nan"))
+        igc.gemm_f16f32(M, N, K, dA, K, dB, K, dC, N, workspace=ws)
+        assert np.array_equal(to_host(dC), C0)
+    rows = np.array(sorted({4095, 4096, M - 1} | set(rng.integers(4096, M, 12).tolist())))
+    assert np.array_equal(C0[rows].astype(np.float64), oracle.gemm_f16(A[rows], Bt))
 
 
 # ----------------------------------------------------------------- quantized conv
@@ -433,7 +473,9 @@ def run_qconv(igc, x, zA, w, zB, stride, pad, outputs=("C",), scale=None, bias=N
         dS, dBi = to_dev(scale.astype(np.float32)), to_dev(bias.astype(np.float32))
         out["_keep"] = (dS, dBi)
         kw.update(Q_i8=out["Q"], ldq=Kout, scale_n=dS, bias_n=dBi)
-    igc.conv2d_u8i8_zp(Nb, H, W, C, Kout, R, S, stride[0], stride[1], pad[0], pad[1], dx, zA, dw, zB, **kw)
+    dims = (Nb, H, W, C, Kout, R, S, stride[0], stride[1], pad[0], pad[1])
+    igc.conv2d_u8i8_zp(*dims, dx, zA, dw, zB, workspace=workspace_for(igc.conv2d_u8i8_zp_workspace_size(*dims)),
+                       **kw)
     return {k: to_host(v) for k, v in out.items() if not k.startswith("_")}
 
 

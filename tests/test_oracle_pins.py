@@ -195,6 +195,24 @@ def test_dequant_large_ints_round_once(oracle):
     assert D.tolist() == [[16777216.0, 16777220.0, -16777216.0]]
 
 
+def test_dequant_hand_cases(oracle):
+    """Hand-worked binary32 cases, two of them where the reading taken,
+    fl32(fl32(C) * fl32(sA*sB)), differs from multiplying by sA and sB in
+    turn."""
+    with open(os.path.join(GOLDEN, "dequant_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    differing = 0
+    for c in cases:
+        sA, sB = float.fromhex(c["sA"]), float.fromhex(c["sB"])
+        assert np.float32(sA) == sA and np.float32(sB) == sB, c  # the scales are binary32 values
+        D = oracle.dequant(np.array([[c["C"]]], np.int64), sA, sB)
+        assert float(D[0, 0]) == float.fromhex(c["D"]), c
+        if "other_order" in c:
+            assert float.fromhex(c["other_order"]) != float.fromhex(c["D"])
+            differing += 1
+    assert differing >= 2
+
+
 def test_requant_hand_cases(oracle):
     with open(os.path.join(GOLDEN, "requant_cases.json")) as f:
         cases = json.load(f)["cases"]
