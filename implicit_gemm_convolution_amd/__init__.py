@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     conv2d_u8i8_zp_workspace_size,
     device_check,
     gemm_f16f32,
+    gemm_f16f32_noalloc,
     gemm_f16f32_workspace_size,
     gemm_u8i8_zp,
     gemm_u8i8_zp_workspace_size,

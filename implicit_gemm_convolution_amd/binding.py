@@ -31,6 +31,7 @@ IGC_ENODEV = -5
 EXPORTED = ("gemm_f16f32", "gemm_u8i8_zp", "conv2d_implicit_gemm", "conv2d_u8i8_zp",
             "gemm_f16f32_workspace_size", "gemm_u8i8_zp_workspace_size",
             "conv2d_implicit_gemm_workspace_size", "conv2d_u8i8_zp_workspace_size",
+            "gemm_f16f32_noalloc",
             "igc_status_string", "igc_last_error", "igc_device_check", "igc_set_tuning")
 
 
@@ -78,6 +79,8 @@ def load() -> ctypes.CDLL:
     pz = ctypes.POINTER(ctypes.c_size_t)
     L.gemm_f16f32.argtypes = [i, i, i, p, i, p, i, p, i, p, z, p]
     L.gemm_f16f32.restype = i
+    L.gemm_f16f32_noalloc.argtypes = [i, i, i, p, i, p, i, p, i, p]
+    L.gemm_f16f32_noalloc.restype = i
     L.gemm_u8i8_zp.argtypes = [i, i, i, p, i, i, p, i, i, ctypes.POINTER(Epilogue), p]
     L.gemm_u8i8_zp.restype = i
     L.conv2d_implicit_gemm.argtypes = [i] * 11 + [p, p, p, p, z, p]
@@ -188,6 +191,13 @@ def gemm_f16f32(M, N, K, A, lda, B, ldb, C, ldc, stream=None, *, workspace=None,
     st = load().gemm_f16f32(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _addr(workspace),
                             _ws_bytes(workspace, ws_bytes), _stream(stream))
     return _check(st, "gemm_f16f32") if check else st
+
+
+def gemm_f16f32_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream=None, *, check=True) -> int:
+    """gemm_f16f32 with its workspace in the library's static device array
+    (allocates nothing; calls that overlap on one GPU race)."""
+    st = load().gemm_f16f32_noalloc(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, _stream(stream))
+    return _check(st, "gemm_f16f32_noalloc") if check else st
 
 
 def gemm_u8i8_zp(M, N, K, A, lda, zA, B, ldb, zB, *, C_i32=None, ldc=0, D_f32=None, ldd=0,

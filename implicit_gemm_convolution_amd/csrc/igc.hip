@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -167,6 +168,38 @@ int launch_u8i8(igc::Params& p, bool fast, void* ws, size_t ws_bytes, hipStream_
   }
 }
 
+// Scratch of gemm_f16f32_noalloc: the stream-K workspace as a static device
+// array, one per GPU, held until the process ends.  In host code `scratch`
+// only names the symbol; its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current and kept in
+// g_scratch_ptr.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(int dev, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return fail(IGC_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return IGC_OK;
+}
+
+// Zero-fills n 32-bit words (a kernel, not a memset, so that a caller's HIP
+// graph capture records an ordinary kernel node).
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, int n) {
+  const int i = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
 // Workspace bytes of the plan for an M x N x K problem of this kind on the
 // current device, with the aligned operand path (the one that may split).
 int query_workspace(int kind, int M, int N, int K, size_t* bytes) {
@@ -241,6 +274,46 @@ int gemm_f16f32(int M, int N, int K, const void* A, int lda, const void* B, int 
   const bool fast = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 &&
                     256LL * lda * 2 < (1LL << 31) && 256LL * ldb * 2 < (1LL << 31);
   return plan_and_launch<igc::KIND_F16_GEMM, 0>(p, fast, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int gemm_f16f32_noalloc(int M, int N, int K, const void* A, int lda, const void* B, int ldb, float* C,
+                        int ldc, void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0 || N < 0 || K < 0) return fail(IGC_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
+  if (M == 0 || N == 0) return IGC_OK;
+  if (!C) return fail(IGC_EINVAL, "C is NULL");
+  if (ldc < N) return fail(IGC_EINVAL, "ldc=%d < N=%d", ldc, N);
+  if (K > 0) {
+    if (!A || !B) return fail(IGC_EINVAL, "A or B is NULL");
+    if (lda < K || ldb < K) return fail(IGC_EINVAL, "lda=%d / ldb=%d < K=%d", lda, ldb, K);
+  }
+  int dev;
+  if (int s = check_device(&dev)) return s;
+  igc::Params p = zero_params();
+  p.M = M; p.N = N; p.K = K;
+  p.A = static_cast<const uint8_t*>(A); p.lda = lda;
+  p.B = static_cast<const uint8_t*>(B); p.ldb = ldb;
+  p.Cf = C; p.ldcf = ldc;
+  p.vec_c = aligned16(C) && ldc % 4 == 0;
+  const bool fast = aligned16(A) && aligned16(B) && lda % 8 == 0 && ldb % 8 == 0 && K % 8 == 0 &&
+                    256LL * lda * 2 < (1LL << 31) && 256LL * ldb * 2 < (1LL << 31);
+  const Plan pl = make_plan(igc::KIND_F16_GEMM, M, N, K, fast, device_cus(dev), true);
+  void* ws = nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (pl.ws_bytes) {
+    if (pl.ws_bytes > kNoallocScratchBytes)
+      return fail(IGC_EUNSUPPORTED, "this call needs %zu bytes of stream-K workspace; the static scratch holds %zu",
+                  pl.ws_bytes, kNoallocScratchBytes);
+    if (int s = scratch_address(dev, &ws)) return s;
+    // the arrival counters must start at zero whatever an earlier call left
+    const int words = (int)(pl.cnt_bytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
+                       static_cast<uint32_t*>(ws), words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  apply_plan(p, pl, ws);
+  return launch<igc::KIND_F16_GEMM, 0>(p, pl, fast, st);
 }
 
 int gemm_u8i8_zp_workspace_size(int M, int N, int K, size_t* bytes) {

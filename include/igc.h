@@ -91,6 +91,27 @@ int gemm_f16f32(int M, int N, int K,
 int gemm_f16f32_workspace_size(int M, int N, int K, size_t* bytes);
 
 /*
+ * gemm_f16f32_noalloc -- gemm_f16f32 for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, layouts and results as gemm_f16f32
+ * without the workspace: where the call splits tiles between workgroups its
+ * workspace is a static device array of 32 MiB (33554432 bytes) per GPU,
+ * which each GPU the library runs on holds until the process ends.  The call
+ * allocates nothing and clears the array's counters with a kernel on
+ * `stream` before using it.  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (different streams) race.
+ * Errors: as gemm_f16f32, plus IGC_EUNSUPPORTED when the split this call
+ * makes needs more workspace than the 32 MiB the array holds (512 KiB per
+ * workgroup sharing tiles; gemm_f16f32_workspace_size gives the amount, and
+ * a shape for which it returns 0 never fails this way).
+ */
+int gemm_f16f32_noalloc(int M, int N, int K,
+                        const void* A, int lda,
+                        const void* B, int ldb,
+                        float* C, int ldc,
+                        void* stream);
+
+/*
  * Outputs of gemm_u8i8_zp.  Any non-empty subset may be requested in one call;
  * a NULL pointer means "not requested".
  *
