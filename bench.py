@@ -168,7 +168,7 @@ class Runner:
                 raise RuntimeError(f"{name}: status {st}")
         return call
 
-    def measure(self, torch, steps: int, warmup: int, cold: bool = False) -> dict:
+    def measure(self, torch, steps: int, warmup: int, cold: bool = False, extras: bool = True) -> dict:
         """Time `steps` back-to-back launches on the current stream between two
         HIP events: the average launch duration is the elapsed time / steps
         (no event commands between the launches, as a caller would run them).
@@ -209,6 +209,8 @@ class Runner:
             frac_of_peak=ops / step_s / 1e12 / self.peak,
             alg_gbps=algorithmic_bytes(self.wl) / step_s / 1e9,
         )
+        if not extras:
+            return res
         res.update(self._per_launch(torch, steps, "launch_us"))
         if cold:
             # a 512 MiB write between launches evicts the operands from the
@@ -376,6 +378,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="c3", choices=synth.WORKLOADS)
     ap.add_argument("--only", action="store_true", help="measure the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time the back-to-back launches only: no per-launch, cold-cache or clock passes "
+                         "(for profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
@@ -419,7 +424,7 @@ def main(argv=None) -> int:
     for name in names:
         wl = synth.workload(name)
         r = Runner(wl, igc, torch)
-        res = r.measure(torch, args.steps, args.warmup, cold=name in ("c1", "c2"))
+        res = r.measure(torch, args.steps, args.warmup, cold=name in ("c1", "c2"), extras=not args.no_extras)
         res["roofline_traffic_bytes"] = traffic_for(name)
         res["config"] = synth.DESCRIPTIONS[name]
         results[name] = res
@@ -428,7 +433,8 @@ def main(argv=None) -> int:
         del r
         torch.cuda.empty_cache()
         print(f"# {name}: {res['value']:.1f} {res['unit']} ({100 * res['frac_of_peak']:.1f}% of peak), "
-              f"{res['launch_us_mean']:.1f} us/launch back to back, {res['launch_us_median']:.1f} us median alone"
+              f"{res['launch_us_mean']:.1f} us/launch back to back"
+              + (f", {res['launch_us_median']:.1f} us median alone" if "launch_us_median" in res else "")
               + (f", {res['cold_launch_us_median']:.1f} us cold" if "cold_launch_us_median" in res else "")
               + (f", sclk {res['sclk_mhz']['median']:.0f} MHz" if res.get("sclk_mhz") else ""),
               file=sys.stderr, flush=True)
@@ -463,9 +469,9 @@ def main(argv=None) -> int:
             "frac": round(head["frac_of_peak"], 4),
             "traffic": traffic_for(args.workload),
             "launch_us_mean": round(head["launch_us_mean"], 2),
-            "launch_us_median": round(head["launch_us_median"], 2),
-            "launch_us_min": round(head["launch_us_min"], 2),
-            "launch_us_max": round(head["launch_us_max"], 2),
+            "launch_us_median": round(head["launch_us_median"], 2) if "launch_us_median" in head else None,
+            "launch_us_min": round(head["launch_us_min"], 2) if "launch_us_min" in head else None,
+            "launch_us_max": round(head["launch_us_max"], 2) if "launch_us_max" in head else None,
             "sclk_mhz": head.get("sclk_mhz"),
             "kernel_source_hash": kernel_source_hash(),
         },
