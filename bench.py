@@ -382,6 +382,10 @@ def main(argv=None) -> int:
                     help="time the back-to-back launches only: no per-launch, cold-cache or clock passes "
                          "(for profiler runs)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--variant", type=int, default=-1,
+                    help="force a tile variant through igc_set_tuning (-1: by shape; 0 256x256, 1 128x128, "
+                         "2 64x64, 3 256x128, 4 224x256, 5 fp16 LDS bypass) -- for A/B runs, not the headline")
+    ap.add_argument("--streamk", type=int, default=1, help="stream-K mode for igc_set_tuning (0, 1, 2)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args(argv)
@@ -414,6 +418,7 @@ def main(argv=None) -> int:
     if st != igc.IGC_OK:
         print(f"device check failed: {igc.last_error()}", file=sys.stderr)
         return 1
+    igc.set_tuning(args.variant, args.streamk)
 
     # The headline workload runs last: after the others, the GPU is at the
     # steady clock it holds under sustained load (it needs ~20 ms of load to
@@ -448,6 +453,8 @@ def main(argv=None) -> int:
     d = head_wl.dims
     line = {
         "metric": METRIC,
+        **({"tuning": {"variant": args.variant, "streamk": args.streamk}}
+           if (args.variant, args.streamk) != (-1, 1) else {}),
         "value": round(head["value"], 2),
         "unit": head["unit"],
         "n_gpus": 1,
