@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
         L.oracle_im2col_f16.argtypes = [_i64] * 10 + [_p, _p]
         L.oracle_conv2d_u8i8_direct_at.argtypes = conv_args + [_p, _i64, _p, _i64, _p, _i64, _p]
         L.oracle_im2col_u8.argtypes = [_i64] * 10 + [_p, _i64, _p]
+        L.oracle_conv2d_nhwcnc_direct.argtypes = conv_args + [_p, _p, _p]
         L.oracle_conv_out_dim.argtypes = [_i64] * 4
         L.oracle_conv_out_dim.restype = _i64
         L.oracle_num_threads.restype = ctypes.c_int
@@ -279,3 +280,22 @@ def im2col_u8(x: np.ndarray, zA: int, R: int, S: int, stride=(1, 1), pad=(0, 0))
     col = np.empty((Nb * P * Q, R * S * C), np.uint8)
     lib().oracle_im2col_u8(Nb, H, W, C, R, S, sh, sw, ph, pw, _ptr(x), int(zA), _ptr(col))
     return col
+
+
+def conv2d_nhwcnc_direct(x: np.ndarray, w: np.ndarray, stride=(1, 1), pad=(0, 0)) -> np.ndarray:
+    """O9: direct convolution in the blocked NHWCnc layout (block size 16).
+    x fp16 [Nb/16][H][W][C/16][16][16], w fp16 [R][S][C/16][Kout/16][16][16];
+    returns float64 [Nb/16][P][Q][Kout/16][16][16]."""
+    x = np.ascontiguousarray(x)
+    w = np.ascontiguousarray(w)
+    assert x.ndim == 6 and w.ndim == 6 and x.shape[4:] == (16, 16) and w.shape[4:] == (16, 16)
+    NB, H, W, CB = x.shape[:4]
+    R, S, CB2, OB = w.shape[:4]
+    assert CB == CB2
+    P = conv_out_dim(H, R, stride[0], pad[0])
+    Q = conv_out_dim(W, S, stride[1], pad[1])
+    y = np.empty((NB, P, Q, OB, 16, 16), np.float64)
+    xb, wb = x.view(np.uint16), w.view(np.uint16)
+    lib().oracle_conv2d_nhwcnc_direct(16 * NB, H, W, 16 * CB, 16 * OB, R, S, stride[0], stride[1], pad[0], pad[1],
+                                      _ptr(xb), _ptr(wb), _ptr(y))
+    return y

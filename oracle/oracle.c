@@ -401,6 +401,57 @@ void oracle_im2col_u8(int64_t Nb, int64_t H, int64_t W, int64_t C,
       }
 }
 
+/* ------------------------------------------------------------------------ */
+/* O9. Direct convolution in the blocked NHWCnc layout of [CONV-TC]            */
+/* "Preparation and algorithm" (block size 16):                               */
+/*   input   A[n/16][h][w][c/16][n%16][c%16]      (data_shape)                */
+/*   weights W[kh][kw][c/16][o/16][c%16][o%16]    (kernel_shape)              */
+/*   output  Conv[n/16][p][q][o/16][n%16][o%16]   (output_shape)              */
+/* and Conv[nb,p,q,ob,nn,oo] = sum over (kh, kw, ic, ii) of                   */
+/*   Apad[nb, p*sh+kh, q*sw+kw, ic, nn, ii] * W[kh, kw, ic, ob, ii, oo]        */
+/* with Apad = A inside the input and 0 in the padding, both factors widened  */
+/* before the multiply.  The sum runs over (kh, kw, ic, ii), i.e. the same    */
+/* (r, s, c) order as O6, so the two agree bit for bit on the same logical    */
+/* tensors.  Nb, C and Kout must be multiples of 16.  fp16 in, double out.     */
+/* ------------------------------------------------------------------------ */
+void oracle_conv2d_nhwcnc_direct(int64_t Nb, int64_t H, int64_t W, int64_t C, int64_t Kout,
+                                 int64_t R, int64_t S, int64_t sh, int64_t sw,
+                                 int64_t ph, int64_t pw,
+                                 const uint16_t* x16, const uint16_t* w16, double* y) {
+  int64_t P = oracle_conv_out_dim(H, R, sh, ph);
+  int64_t Q = oracle_conv_out_dim(W, S, sw, pw);
+  int64_t NB = Nb / 16, CB = C / 16, OB = Kout / 16;
+  int64_t nx = Nb * H * W * C, nw = Kout * R * S * C;
+  double* x = (double*)malloc(sizeof(double) * (size_t)(nx > 0 ? nx : 1));
+  double* w = (double*)malloc(sizeof(double) * (size_t)(nw > 0 ? nw : 1));
+  oracle_f16_decode(x16, x, nx);
+  oracle_f16_decode(w16, w, nw);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int64_t nb = 0; nb < NB; ++nb)
+    for (int64_t p = 0; p < P; ++p)
+      for (int64_t q = 0; q < Q; ++q)
+        for (int64_t ob = 0; ob < OB; ++ob)
+          for (int64_t nn = 0; nn < 16; ++nn)
+            for (int64_t oo = 0; oo < 16; ++oo) {
+              double acc = 0.0;
+              for (int64_t kh = 0; kh < R; ++kh)
+                for (int64_t kw = 0; kw < S; ++kw) {
+                  int64_t h = p * sh + kh - ph;
+                  int64_t ww = q * sw + kw - pw;
+                  int inside = h >= 0 && h < H && ww >= 0 && ww < W;
+                  for (int64_t ic = 0; ic < CB; ++ic)
+                    for (int64_t ii = 0; ii < 16; ++ii) {
+                      double a = 0.0; /* padding */
+                      if (inside) a = x[((((nb * H + h) * W + ww) * CB + ic) * 16 + nn) * 16 + ii];
+                      acc += a * w[((((kh * S + kw) * CB + ic) * OB + ob) * 16 + ii) * 16 + oo];
+                    }
+                }
+              y[((((nb * P + p) * Q + q) * OB + ob) * 16 + nn) * 16 + oo] = acc;
+            }
+  free(x);
+  free(w);
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -77,6 +77,8 @@ DESCRIPTIONS = {
     "c5": "gemm_u8i8_zp M=N=K=8192, zA=128 zB=0, per-channel scale+bias, RNE int8 requant",
     "q4": "conv2d_u8i8_zp NHWC 256x14x14x256 u8 (zA=100) * KRSC 512x3x3x256 i8 (zB=0), s1 p1, "
           "per-channel scale+bias, RNE int8 requant (GEMM M=50176 N=512 K=2304)",
+    "b4": "conv2d_implicit_gemm_nhwcnc blocked NHWCnc x (16,14,14,16,16,16) * w (3,3,16,32,16,16), s1 p1, "
+          "fp16 in, fp32 out (the 256x14x14 conv in the tutorial's layout; GEMM M=50176 N=512 K=2304)",
 }
 
 
@@ -87,7 +89,7 @@ def workload(name: str, *, scale_down: int = 1) -> Workload:
     factor while keeping the distribution; it is used only by tests that need
     a small member of the same family.
     """
-    seed = int(name[1:]) + (100 if name[0] == "q" else 0)
+    seed = int(name[1:]) + {"c": 0, "q": 100, "b": 200}[name[0]]
     rng = np.random.default_rng(seed)
     if name == "c1":
         n = 256 // scale_down
@@ -132,6 +134,18 @@ def workload(name: str, *, scale_down: int = 1) -> Workload:
         dims = dict(M=nb * 14 * 14, N=512, K=9 * 256, **conv)
         return Workload(name, "conv_u8i8", dims, dict(x=x, w=w, scale=scale, bias=bias),
                         dict(zA=100, zB=0, outputs=("Q_i8",)))
+    if name == "b4":
+        # c4's problem and distributions, drawn directly in the blocked NHWCnc
+        # layout of the conv tutorial (block size 16): x [N/16][H][W][C/16][16n][16c],
+        # w [R][S][C/16][K/16][16c][16k]
+        nb = 256 // scale_down
+        assert nb % 16 == 0
+        x = f16_normal(rng, (nb // 16, 14, 14, 16, 16, 16))
+        w = f16_normal(rng, (3, 3, 16, 32, 16, 16), std=0.05)
+        conv = dict(Nb=nb, H=14, W=14, C=256, Kout=512, R=3, S=3,
+                    stride_h=1, stride_w=1, pad_h=1, pad_w=1)
+        dims = dict(M=nb * 14 * 14, N=512, K=9 * 256, **conv)
+        return Workload(name, "conv_f16_blk", dims, dict(x=x, w=w))
     raise KeyError(name)
 
 

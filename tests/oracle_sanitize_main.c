@@ -41,6 +41,9 @@ void oracle_conv2d_u8i8_direct_at(int64_t Nb, int64_t H, int64_t W, int64_t C, i
                                   const int64_t* pix, int64_t npix, int64_t* y);
 void oracle_im2col_u8(int64_t Nb, int64_t H, int64_t W, int64_t C, int64_t R, int64_t S, int64_t sh,
                       int64_t sw, int64_t ph, int64_t pw, const uint8_t* x, int64_t zA, uint8_t* col);
+void oracle_conv2d_nhwcnc_direct(int64_t Nb, int64_t H, int64_t W, int64_t C, int64_t Kout, int64_t R,
+                                 int64_t S, int64_t sh, int64_t sw, int64_t ph, int64_t pw,
+                                 const uint16_t* x16, const uint16_t* w16, double* y);
 int oracle_num_threads(void);
 
 static uint32_t state = 12345u;
@@ -155,6 +158,40 @@ static void conv_cases(void) {
   }
 }
 
+/* the blocked layout against the plain one on the same logical tensors */
+static void blocked_case(void) {
+  const int64_t Nb = 16, H = 3, W = 4, C = 32, Kout = 16, R = 3, S = 2, sh = 1, sw = 2, ph = 1, pw = 1;
+  const int64_t P = oracle_conv_out_dim(H, R, sh, ph), Qo = oracle_conv_out_dim(W, S, sw, pw);
+  const int64_t nx = Nb * H * W * C, nw = Kout * R * S * C, ny = Nb * P * Qo * Kout;
+  uint16_t* xb = malloc(sizeof(uint16_t) * (size_t)nx);
+  uint16_t* wb = malloc(sizeof(uint16_t) * (size_t)nw);
+  uint16_t* x = malloc(sizeof(uint16_t) * (size_t)nx);
+  uint16_t* w = malloc(sizeof(uint16_t) * (size_t)nw);
+  double* yb = malloc(sizeof(double) * (size_t)ny);
+  double* y = malloc(sizeof(double) * (size_t)ny);
+  for (int64_t i = 0; i < nx; ++i) xb[i] = small_f16();
+  for (int64_t i = 0; i < nw; ++i) wb[i] = small_f16();
+  for (int64_t n = 0; n < Nb; ++n)
+    for (int64_t h = 0; h < H; ++h)
+      for (int64_t ww = 0; ww < W; ++ww)
+        for (int64_t c = 0; c < C; ++c)
+          x[((n * H + h) * W + ww) * C + c] = xb[((((n / 16) * H + h) * W + ww) * (C / 16) + c / 16) * 256 + (n % 16) * 16 + c % 16];
+  for (int64_t k = 0; k < Kout; ++k)
+    for (int64_t r = 0; r < R; ++r)
+      for (int64_t s = 0; s < S; ++s)
+        for (int64_t c = 0; c < C; ++c)
+          w[((k * R + r) * S + s) * C + c] = wb[(((r * S + s) * (C / 16) + c / 16) * (Kout / 16) + k / 16) * 256 + (c % 16) * 16 + k % 16];
+  oracle_conv2d_nhwcnc_direct(Nb, H, W, C, Kout, R, S, sh, sw, ph, pw, xb, wb, yb);
+  oracle_conv2d_direct(Nb, H, W, C, Kout, R, S, sh, sw, ph, pw, x, w, y);
+  for (int64_t n = 0; n < Nb; ++n)
+    for (int64_t p = 0; p < P; ++p)
+      for (int64_t q = 0; q < Qo; ++q)
+        for (int64_t k = 0; k < Kout; ++k)
+          CHECK(y[((n * P + p) * Qo + q) * Kout + k] ==
+                yb[((((n / 16) * P + p) * Qo + q) * (Kout / 16) + k / 16) * 256 + (n % 16) * 16 + k % 16]);
+  free(xb); free(wb); free(x); free(w); free(yb); free(y);
+}
+
 int main(void) {
   for (uint32_t h = 0; h < 65536; ++h) (void)oracle_f16_to_f64((uint16_t)h);
   uint16_t bits[4] = {0x0001, 0x7bff, 0xfc00, 0x3c00};
@@ -163,6 +200,7 @@ int main(void) {
   CHECK(out[3] == 1.0);
   gemm_cases();
   conv_cases();
+  blocked_case();
   CHECK(oracle_num_threads() >= 1);
   if (fails) {
     fprintf(stderr, "%d checks failed\n", fails);

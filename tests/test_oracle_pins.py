@@ -454,3 +454,103 @@ def test_qconv_special_cases(oracle):
     pix = np.array([0, 7, 19, Nb * H * W - 1])
     at = oracle.conv2d_u8i8_direct_at(x, 13, w, 5, pix, (1, 1), (1, 1))
     assert np.array_equal(at, oracle.conv2d_u8i8_direct(x, 13, w, 5, (1, 1), (1, 1)).reshape(-1, Kout)[pix])
+
+
+# ----------------------------------------------------------------- O9: blocked NHWCnc layout
+def blk_x_to_nhwc(xb):
+    """[Nb/16][H][W][C/16][16n][16c] -> [Nb][H][W][C] (numpy permutation only)."""
+    NB, H, W, CB = xb.shape[:4]
+    return xb.transpose(0, 4, 1, 2, 3, 5).reshape(NB * 16, H, W, CB * 16)
+
+
+def blk_w_to_krsc(wb):
+    """[R][S][C/16][K/16][16c][16k] -> [K][R][S][C]."""
+    R, S, CB, OB = wb.shape[:4]
+    return wb.transpose(3, 5, 0, 1, 2, 4).reshape(OB * 16, R, S, CB * 16)
+
+
+def blk_y_to_nhwc(yb):
+    """[Nb/16][P][Q][K/16][16n][16k] -> [Nb][P][Q][K]."""
+    NB, P, Q, OB = yb.shape[:4]
+    return yb.transpose(0, 4, 1, 2, 3, 5).reshape(NB * 16, P, Q, OB * 16)
+
+
+@pytest.mark.parametrize("NB,H,W,CB,OB,R,S,stride,pad", [
+    (1, 5, 4, 2, 1, 3, 3, (1, 1), (1, 1)),
+    (2, 3, 6, 1, 2, 2, 3, (2, 1), (0, 2)),
+    (1, 4, 4, 3, 1, 1, 1, (1, 1), (0, 0)),
+])
+def test_conv_nhwcnc_equals_direct_nhwc(oracle, NB, H, W, CB, OB, R, S, stride, pad):
+    """O9 on blocked tensors is O6 on the same logical tensors, bit for bit
+    (same (r, s, c) summation order; the layouts differ only by a
+    permutation of axes)."""
+    rng = np.random.default_rng(NB * 100 + H * 10 + W)
+    xb = synth.f16_normal(rng, (NB, H, W, CB, 16, 16))
+    wb = synth.f16_normal(rng, (R, S, CB, OB, 16, 16), std=0.1)
+    yb = oracle.conv2d_nhwcnc_direct(xb, wb, stride, pad)
+    y = oracle.conv2d_direct(blk_x_to_nhwc(xb), blk_w_to_krsc(wb), stride, pad)
+    assert np.array_equal(blk_y_to_nhwc(yb), y)
+
+
+def test_conv_nhwcnc_brute_force_from_the_blocked_formula(oracle):
+    """Pure-Python integer evaluation of the blocked definition:
+    Conv[nb,p,q,ob,nn,oo] = sum_{kh,kw,ic,ii} Apad[nb, p*sh+kh, q*sw+kw, ic, nn, ii]
+                            * W[kh, kw, ic, ob, ii, oo]."""
+    rng = np.random.default_rng(91)
+    NB, H, W, CB, OB, R, S, sh, sw, ph, pw = 1, 2, 3, 1, 1, 2, 2, 1, 1, 1, 1
+    xb = synth.f16_small_ints(rng, (NB, H, W, CB, 16, 16), -3, 3)
+    wb = synth.f16_small_ints(rng, (R, S, CB, OB, 16, 16), -3, 3)
+    P, Q = (H + 2 * ph - R) // sh + 1, (W + 2 * pw - S) // sw + 1
+    A = xb.astype(np.int64).tolist()
+    Wt = wb.astype(np.int64).tolist()
+    yb = oracle.conv2d_nhwcnc_direct(xb, wb, (sh, sw), (ph, pw))
+    for nb in range(NB):
+        for p in range(P):
+            for q in range(Q):
+                for ob in range(OB):
+                    for nn in range(16):
+                        for oo in range(16):
+                            acc = 0
+                            for kh in range(R):
+                                for kw in range(S):
+                                    h, w = p * sh + kh - ph, q * sw + kw - pw
+                                    if not (0 <= h < H and 0 <= w < W):
+                                        continue  # Apad is 0 in the padding
+                                    for ic in range(CB):
+                                        for ii in range(16):
+                                            acc += A[nb][h][w][ic][nn][ii] * Wt[kh][kw][ic][ob][ii][oo]
+                            assert yb[nb, p, q, ob, nn, oo] == acc
+
+
+def test_conv_nhwcnc_impulse(oracle):
+    """One 1 at image n0, pixel (h0, w0), channel c0 of a blocked input: the
+    output at image n0, pixel (h0 + ph - r, w0 + pw - s), channel k is the
+    weight W[r, s, c0, k] -- cross-correlation orientation and block indexing."""
+    NB, H, W, CB, OB, R, S = 1, 5, 6, 2, 1, 3, 3
+    n0, h0, w0, c0 = 9, 2, 4, 21
+    xb = np.zeros((NB, H, W, CB, 16, 16), np.float16)
+    xb[n0 // 16, h0, w0, c0 // 16, n0 % 16, c0 % 16] = 1.0
+    rng = np.random.default_rng(92)
+    wb = synth.f16_small_ints(rng, (R, S, CB, OB, 16, 16))
+    yb = oracle.conv2d_nhwcnc_direct(xb, wb, (1, 1), (1, 1))
+    y = blk_y_to_nhwc(yb)
+    for r in range(R):
+        for s in range(S):
+            p, q = h0 + 1 - r, w0 + 1 - s
+            if 0 <= p < H and 0 <= q < W:
+                for k in range(16 * OB):
+                    assert y[n0, p, q, k] == float(wb[r, s, c0 // 16, k // 16, c0 % 16, k % 16])
+    assert np.count_nonzero(y) <= R * S * 16 * OB
+    assert np.count_nonzero(y[np.arange(16) != n0]) == 0
+
+
+def test_blocked_workload_has_the_tutorials_shapes():
+    with open(os.path.join(GOLDEN, "conv_tutorial_sizes.json")) as f:
+        g = json.load(f)
+    b, pr = g["blocked_layout"], g["printed"]
+    wl = synth.workload("b4")
+    assert list(wl.arrays["x"].shape) == b["data_shape"]
+    assert list(wl.arrays["w"].shape) == b["kernel_shape"]
+    assert int(np.prod(b["data_shape"])) == pr["input_elements"]
+    assert int(np.prod(b["kernel_shape"])) == pr["weight_elements"]
+    assert int(np.prod(b["output_shape"])) == pr["output_elements"]
