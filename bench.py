@@ -69,7 +69,7 @@ def algorithmic_bytes(wl) -> int:
     M, N, K = d["M"], d["N"], d["K"]
     if wl.kind == "gemm_f16":
         return 2 * (M * K + N * K) + 4 * M * N
-    if wl.kind == "conv_f16":
+    if wl.kind in ("conv_f16", "conv_f16_blk"):
         return wl.arrays["x"].nbytes + wl.arrays["w"].nbytes + 4 * M * N
     if wl.kind == "conv_u8i8":
         return wl.arrays["x"].nbytes + wl.arrays["w"].nbytes + M * N + 8 * N
@@ -139,6 +139,18 @@ class Runner:
             self.call = self._direct("conv2d_u8i8_zp", *args, x.data_ptr(), pr["zA"], w.data_ptr(), pr["zB"],
                                      ctypes.byref(self.ep), self.stream)
             self.dtype, self.peak, self.unit = "i8", PEAK_I8_TOPS, "TOPS"
+        elif wl.kind == "conv_f16_blk":
+            x, w = t(wl.arrays["x"]), t(wl.arrays["w"])
+            P = (d["H"] + 2 * d["pad_h"] - d["R"]) // d["stride_h"] + 1
+            Q = (d["W"] + 2 * d["pad_w"] - d["S"]) // d["stride_w"] + 1
+            y = torch.empty((d["Nb"] // 16, P, Q, d["Kout"] // 16, 16, 16), dtype=torch.float32, device=dev)
+            args = (d["Nb"], d["H"], d["W"], d["C"], d["Kout"], d["R"], d["S"], d["stride_h"],
+                    d["stride_w"], d["pad_h"], d["pad_w"])
+            ws, nws = self._workspace(igc.conv2d_implicit_gemm_nhwcnc_workspace_size(*args), torch, dev)
+            self.keep = [x, w, y, ws]
+            self.call = self._direct("conv2d_implicit_gemm_nhwcnc", *args, x.data_ptr(), w.data_ptr(),
+                                     y.data_ptr(), ws.data_ptr(), nws, self.stream)
+            self.dtype, self.peak, self.unit = "f16", PEAK_F16_TFLOPS, "TFLOPS"
         else:
             x, w = t(wl.arrays["x"]), t(wl.arrays["w"])
             P = (d["H"] + 2 * d["pad_h"] - d["R"]) // d["stride_h"] + 1
@@ -308,9 +320,19 @@ def cpu_baseline(wl, budget_s: float) -> dict:
     d = wl.dims
     cores = oracle.num_threads()
 
+    done = [0]  # rows (pixels) the last run covered
+
     def run(nrows):
+        done[0] = nrows
         rows = np.arange(nrows)
         t0 = time.perf_counter()
+        if wl.kind == "conv_f16_blk":
+            # whole groups of 16 images (the blocked layout's unit)
+            g = max(1, -(-nrows // (16 * d["M"] // d["Nb"])))
+            oracle.conv2d_nhwcnc_direct(wl.arrays["x"][:g], wl.arrays["w"],
+                                        (d["stride_h"], d["stride_w"]), (d["pad_h"], d["pad_w"]))
+            done[0] = min(d["M"], g * 16 * d["M"] // d["Nb"])
+            return time.perf_counter() - t0
         if wl.kind == "gemm_f16":
             oracle.gemm_f16(wl.arrays["A"][rows], wl.arrays["Bt"])
         elif wl.kind == "gemm_u8i8":
@@ -337,6 +359,7 @@ def cpu_baseline(wl, budget_s: float) -> dict:
         t = run(n)
     n = int(min(d["M"], max(n, n * budget_s / max(t, 1e-9))))
     t = run(n)
+    n = done[0]
     ops = 2.0 * n * d["N"] * d["K"]
     unit = "TOPS" if wl.kind in ("gemm_u8i8", "conv_u8i8") else "TFLOPS"
     what = "output pixels" if wl.kind.startswith("conv") else "output rows"

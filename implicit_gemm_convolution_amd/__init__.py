@@ -15,6 +15,8 @@ from .binding import (  # noqa: F401
     Epilogue,
     IGCError,
     conv2d_implicit_gemm,
+    conv2d_implicit_gemm_nhwcnc,
+    conv2d_implicit_gemm_nhwcnc_workspace_size,
     conv2d_implicit_gemm_workspace_size,
     conv2d_u8i8_zp,
     conv2d_u8i8_zp_workspace_size,

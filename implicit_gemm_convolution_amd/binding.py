@@ -31,7 +31,7 @@ IGC_ENODEV = -5
 EXPORTED = ("gemm_f16f32", "gemm_u8i8_zp", "conv2d_implicit_gemm", "conv2d_u8i8_zp",
             "gemm_f16f32_workspace_size", "gemm_u8i8_zp_workspace_size",
             "conv2d_implicit_gemm_workspace_size", "conv2d_u8i8_zp_workspace_size",
-            "gemm_f16f32_noalloc",
+            "gemm_f16f32_noalloc", "conv2d_implicit_gemm_nhwcnc", "conv2d_implicit_gemm_nhwcnc_workspace_size",
             "igc_status_string", "igc_last_error", "igc_device_check", "igc_set_tuning")
 
 
@@ -86,11 +86,14 @@ def load() -> ctypes.CDLL:
     L.conv2d_implicit_gemm.argtypes = [i] * 11 + [p, p, p, p, z, p]
     L.conv2d_implicit_gemm.restype = i
     L.conv2d_u8i8_zp.argtypes = [i] * 11 + [p, i, p, i, ctypes.POINTER(Epilogue), p]
+    L.conv2d_implicit_gemm_nhwcnc.argtypes = [i] * 11 + [p, p, p, p, z, p]
+    L.conv2d_implicit_gemm_nhwcnc.restype = i
     L.conv2d_u8i8_zp.restype = i
     for name in ("gemm_f16f32_workspace_size", "gemm_u8i8_zp_workspace_size"):
         getattr(L, name).argtypes = [i, i, i, pz]
         getattr(L, name).restype = i
-    for name in ("conv2d_implicit_gemm_workspace_size", "conv2d_u8i8_zp_workspace_size"):
+    for name in ("conv2d_implicit_gemm_workspace_size", "conv2d_u8i8_zp_workspace_size",
+                 "conv2d_implicit_gemm_nhwcnc_workspace_size"):
         getattr(L, name).argtypes = [i] * 11 + [pz]
         getattr(L, name).restype = i
     L.igc_set_tuning.argtypes = [i, i]
@@ -180,6 +183,11 @@ def conv2d_u8i8_zp_workspace_size(Nb, H, W, C, Kout, R, S, stride_h, stride_w, p
                      pad_h, pad_w)
 
 
+def conv2d_implicit_gemm_nhwcnc_workspace_size(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w) -> int:
+    return _ws_query("conv2d_implicit_gemm_nhwcnc_workspace_size", Nb, H, W, C, Kout, R, S, stride_h, stride_w,
+                     pad_h, pad_w)
+
+
 def _ws_bytes(workspace, ws_bytes):
     if ws_bytes is None:
         ws_bytes = int(workspace.numel() * workspace.element_size()) if hasattr(workspace, "numel") else 0
@@ -216,6 +224,15 @@ def conv2d_implicit_gemm(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad
                                      _addr(x), _addr(w), _addr(y), _addr(workspace),
                                      _ws_bytes(workspace, ws_bytes), _stream(stream))
     return _check(st, "conv2d_implicit_gemm") if check else st
+
+
+def conv2d_implicit_gemm_nhwcnc(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, x, w, y,
+                                stream=None, *, workspace=None, ws_bytes=None, check=True) -> int:
+    """The convolution on blocked NHWCnc tensors (block 16); the workspace is required."""
+    st = load().conv2d_implicit_gemm_nhwcnc(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w,
+                                            _addr(x), _addr(w), _addr(y), _addr(workspace),
+                                            _ws_bytes(workspace, ws_bytes), _stream(stream))
+    return _check(st, "conv2d_implicit_gemm_nhwcnc") if check else st
 
 
 def conv2d_u8i8_zp(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, x, zA, w, zB, *,

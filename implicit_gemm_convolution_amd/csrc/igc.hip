@@ -200,6 +200,51 @@ __global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, int n) {
   if (i < n) p[i] = 0u;
 }
 
+// ---------------------------------------------------------------------------
+// Weights of the blocked NHWCnc convolution ([CONV-TC] "Preparation and
+// algorithm": W[kh][kw][c/16][k/16][c%16][k%16], output channels innermost)
+// rewritten in the GEMM's K-contiguous order [k][kh][kw][c] (the column-major
+// B operand), so both MFMA operands read 16 consecutive bytes of K per lane.
+// Each group of 32 threads transposes one 16 x 16 block through LDS: thread t
+// loads channel t/2, output channels 8(t%2) .. +7 (16 bytes) and stores
+// output channel t/2, channels 8(t%2) .. +7 (16 bytes).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) nhwcnc_weights_kernel(const uint16_t* __restrict__ wb,
+                                                             uint16_t* __restrict__ krsc, int RS, int C,
+                                                             int Kout, int nblocks) {
+  __shared__ uint16_t t16[8][16][17];
+  const int grp = threadIdx.x >> 5, t = threadIdx.x & 31;
+  const int bi = (int)blockIdx.x * 8 + grp;
+  const bool live = bi < nblocks;
+  if (live) {
+    const uint4 v = *reinterpret_cast<const uint4*>(wb + (long long)bi * 256 + (t >> 1) * 16 + (t & 1) * 8);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t16[grp][t >> 1][(t & 1) * 8 + e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+  }
+  __syncthreads();
+  if (live) {
+    const int CB = C >> 4, KB = Kout >> 4;
+    const int kb = bi % KB;
+    const int rc = bi / KB;  // rs * CB + cb
+    const int cb = rc % CB;
+    const int rs = rc / CB;
+    const int k = kb * 16 + (t >> 1);
+    const int c0 = cb * 16 + (t & 1) * 8;
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (uint32_t)t16[grp][(t & 1) * 8 + 2 * e][t >> 1] | ((uint32_t)t16[grp][(t & 1) * 8 + 2 * e + 1][t >> 1] << 16);
+    *reinterpret_cast<uint4*>(krsc + (long long)k * RS * C + (long long)rs * C + c0) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Workspace of the blocked-layout convolution: the stream-K part (if any)
+// first, so that its counters sit where the caller's zero fill put them,
+// then the weights in K-contiguous order, rewritten by every call.
+inline size_t nhwcnc_ws_offset(size_t sk_bytes) { return (sk_bytes + 255) / 256 * 256; }
+inline size_t nhwcnc_weight_bytes(const igc::Params& p) { return (size_t)p.N * (size_t)p.K * 2; }
+
 // Workspace bytes of the plan for an M x N x K problem of this kind on the
 // current device, with the aligned operand path (the one that may split).
 int query_workspace(int kind, int M, int N, int K, size_t* bytes) {
@@ -403,6 +448,58 @@ int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, in
   if (fast && C % 64 == 0 && (long long)R * S <= 31)
     return plan_and_launch<igc::KIND_F16_CONV_C64, 0>(p, true, workspace, ws_bytes, st);
   return plan_and_launch<igc::KIND_F16_CONV, 0>(p, fast, workspace, ws_bytes, st);
+}
+
+int conv2d_implicit_gemm_nhwcnc_workspace_size(int Nb, int H, int W, int C, int Kout, int R, int S,
+                                               int stride_h, int stride_w, int pad_h, int pad_w, size_t* bytes) {
+  g_last_error[0] = 0;
+  igc::Params p = zero_params();
+  long long nx = 0;
+  if (int st = conv_params(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, p, &nx)) return st;
+  if (Nb % 16 || C % 16 || Kout % 16) return fail(IGC_EINVAL, "Nb, C and Kout must be multiples of 16");
+  if (!bytes) return fail(IGC_EINVAL, "bytes is NULL");
+  size_t sk = 0;
+  if (int s = query_workspace(igc::KIND_F16_CONV, p.M, p.N, p.K, &sk)) return s;
+  *bytes = nhwcnc_ws_offset(sk) + nhwcnc_weight_bytes(p);
+  return IGC_OK;
+}
+
+int conv2d_implicit_gemm_nhwcnc(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_h,
+                                int stride_w, int pad_h, int pad_w, const void* x, const void* w, float* y,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  igc::Params p = zero_params();
+  long long nx = 0;
+  if (int st = conv_params(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, p, &nx)) return st;
+  if (Nb % 16 || C % 16 || Kout % 16) return fail(IGC_EINVAL, "Nb, C and Kout must be multiples of 16");
+  if (!x || !w || !y) return fail(IGC_EINVAL, "x, w or y is NULL");
+  if (!workspace) return fail(IGC_EINVAL, "the blocked layout needs a workspace (conv2d_implicit_gemm_nhwcnc_workspace_size)");
+  if (!aligned16(w) || !aligned16(workspace)) return fail(IGC_EINVAL, "w and the workspace must be 16-byte aligned");
+  int dev;
+  if (int s = check_device(&dev)) return s;
+  p.A = static_cast<const uint8_t*>(x); p.lda = 0;
+  p.ldb = p.K;
+  p.Cf = y; p.ldcf = Kout;
+  p.blk = 1;
+  p.vec_c = aligned16(y);
+  const bool fast = aligned16(x) && nx * 2 < (1LL << 31) && 256LL * p.K * 2 < (1LL << 31);
+  const int kind = (fast && C % 64 == 0 && (long long)R * S <= 31) ? igc::KIND_F16_CONV_C64 : igc::KIND_F16_CONV;
+  const Plan pl = make_plan(kind, p.M, p.N, p.K, fast, device_cus(dev), true);
+  const size_t woff = nhwcnc_ws_offset(pl.ws_bytes), wbytes = nhwcnc_weight_bytes(p);
+  if (ws_bytes < woff + wbytes)
+    return fail(IGC_EINVAL, "workspace of %zu bytes < the %zu bytes this call needs", ws_bytes, woff + wbytes);
+  uint8_t* const wk = static_cast<uint8_t*>(workspace) + woff;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the weights in the GEMM's K-contiguous order, then the GEMM on them
+  const int nblocks = R * S * (C / 16) * (Kout / 16);
+  hipLaunchKernelGGL(nhwcnc_weights_kernel, dim3((unsigned)((nblocks + 7) / 8)), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(w), reinterpret_cast<uint16_t*>(wk), R * S, C, Kout, nblocks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  p.B = wk;
+  apply_plan(p, pl, workspace);
+  if (kind == igc::KIND_F16_CONV_C64) return launch<igc::KIND_F16_CONV_C64, 0>(p, pl, true, st);
+  return launch<igc::KIND_F16_CONV, 0>(p, pl, fast, st);
 }
 
 }  // extern "C"

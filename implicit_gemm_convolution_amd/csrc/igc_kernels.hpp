@@ -102,6 +102,10 @@ struct Params {
   long long ldb;     // elements
   // implicit im2col view of an NHWC input
   int Nb, H, W, C, R, S, sh, sw, ph, pw, P, Q;
+  // blocked NHWCnc layout (block 16) of the conv input and output: GEMM row
+  // m = ((n/16 * P + p) * Q + q) * 16 + n % 16; x[n/16][h][w][c/16][n%16][c%16],
+  // y[n/16][p][q][k/16][n%16][k%16]
+  int blk;
   // fp32 output (fp16 GEMM and conv)
   float* Cf;
   long long ldcf;
@@ -400,9 +404,22 @@ struct Im2colLoader {
   __device__ __forceinline__ int row_h(int j) const { return hw[j] >> 16; }
   __device__ __forceinline__ int row_w(int j) const { return (int)(int16_t)(hw[j] & 0xffff); }
 
+  // blocked layout (fp16 only): element (pixel, channel c) of row j sits at
+  // pixel * 16C + (c / 16) * 256 + nn_j * 16 + c % 16 (nnoff[j] = nn_j * 16)
+  static constexpr bool BLK_OK = EB == 2;
+  int blk;
+  int nnoff[BLK_OK ? NR : 1];
+  __device__ __forceinline__ long long elem_index(int j, int pixel, int c) const {
+    if constexpr (BLK_OK) {
+      if (blk) return (long long)pixel * (16 * C) + ((c >> 4) << 8) + nnoff[j] + (c & 15);
+    }
+    return (long long)pixel * C + c;
+  }
+
   __device__ __forceinline__ void init(const Params& p, int m0, int kt0) {
     x = p.A;
     H = p.H; W = p.W; C = p.C; S = p.S; K = p.K;
+    blk = BLK_OK ? p.blk : 0;
     padv = (uint8_t)(p.zAp + 128);
     if (FAST) rsrc = make_rsrc(x, (uint32_t)((long long)p.Nb * H * W * C * 2));
     const int PQ = p.P * p.Q;
@@ -410,9 +427,16 @@ struct Im2colLoader {
     for (int j = 0; j < NR; ++j) {
       const int r = FAST ? Sh::lane_row() + j * 8 * Sh::NWAVES : (int)(threadIdx.x >> 3) + j * (NT / 8);
       const int m = m0 + r;
+      if constexpr (BLK_OK) nnoff[j] = 0;
       if (m < p.M) {
-        const int n = m / PQ;
-        const int pq = m - n * PQ;
+        // NHWC: m = (n*P + p)*Q + q; blocked: m = ((n16*P + p)*Q + q)*16 + nn, the
+        // pixel index then counting 16-image groups
+        const int g = blk ? (m >> 4) : m;
+        if constexpr (BLK_OK) {
+          if (blk) nnoff[j] = (m & 15) << 4;
+        }
+        const int n = g / PQ;
+        const int pq = g - n * PQ;
         const int pp = pq / p.Q;
         const int qq = pq - pp * p.Q;
         const int h0 = pp * p.sh - p.ph;
@@ -441,7 +465,7 @@ struct Im2colLoader {
     const int h = row_h(j) + r;
     const int w = row_w(j) + s;
     if ((unsigned)h >= (unsigned)H || (unsigned)w >= (unsigned)W) return 0;
-    return reinterpret_cast<const uint16_t*>(x)[(long long)(pix[j] + r * W + s) * C + c];
+    return reinterpret_cast<const uint16_t*>(x)[elem_index(j, pix[j] + r * W + s, c)];
   }
   // u8: past K (and rows past M) 0, like the row operands' K tail; padding zA
   __device__ __forceinline__ uint8_t elem8(int j, int k) const {
@@ -453,7 +477,7 @@ struct Im2colLoader {
     const int h = row_h(j) + r;
     const int w = row_w(j) + s;
     if ((unsigned)h >= (unsigned)H || (unsigned)w >= (unsigned)W) return padv;
-    return x[(long long)(pix[j] + r * W + s) * C + c];
+    return x[elem_index(j, pix[j] + r * W + s, c)];
   }
 
   // Loading K tile kt takes NPART calls part(tile, kt, j) and then
@@ -485,7 +509,8 @@ struct Im2colLoader {
       const int h = row_h(j) + cur_r;  // rows past M have h < -16000: never in range
       const int w = row_w(j) + cur_s;
       const bool ok = kin && (unsigned)h < (unsigned)H && (unsigned)w < (unsigned)W;
-      const uint32_t off = ((uint32_t)(pix[j] + tap) * (uint32_t)C + (uint32_t)cur_c) * 2u;
+      // (a chunk's 8 channels lie in one 16-channel block: cur_c % 8 == 0)
+      const uint32_t off = (uint32_t)elem_index(j, pix[j] + tap, cur_c) * 2u;
       dma16(rsrc, Sh::dst(tile, j), ok ? off : OOB);
     } else if constexpr (EB == 2) {
       const int c = threadIdx.x & 7;
@@ -540,6 +565,10 @@ struct Im2colC64Loader {
   mutable int cur_r, cur_s, cur_c;  // tap and channel of the next K tile
   mutable int fix_tap, fix_c;       // tap and channel of the next tile fix_pad() visits
   uint32_t padv4;                   // zA in every byte
+  // blocked NHWCnc input (fp16 only): every pixel and channel offset is 16
+  // times its NHWC value (16 images interleaved), plus the row's image within
+  // its group of 16 and the chunk's place in a 16-channel block
+  int blk_shift;                    // 4 blocked, 0 NHWC
 
   __device__ __forceinline__ void init(const Params& p, int m0, int kt0) {
     x = p.A;
@@ -547,20 +576,27 @@ struct Im2colC64Loader {
     bytes = (uint32_t)((long long)p.Nb * p.H * p.W * p.C * EB);
     padv4 = (uint32_t)(uint8_t)(p.zAp + 128) * 0x01010101u;
     p0 = p.ph * p.W + p.pw;
+    blk_shift = (EB == 2 && p.blk) ? 4 : 0;
     const int PQ = p.P * p.Q;
+    // chunk c of a 128-byte K-tile row (channels 8c .. 8c+7 of the tile):
+    // byte 16c (NHWC), or 512 (c / 2) + 16 (c % 2) in the blocked layout
+    const int ch = Sh::lane_chunk();
+    const uint32_t chunk_off = blk_shift ? (uint32_t)((ch >> 1) * 512 + (ch & 1) * 16) : (uint32_t)(ch * CHUNK_BYTES);
 #pragma unroll
     for (int j = 0; j < Sh::NQ; ++j) {
       const int m = m0 + Sh::lane_row() + j * 8 * Sh::NWAVES;
       pixb[j] = 0;
       mask[j] = 0;
       if (m < p.M) {
-        const int n = m / PQ;
-        const int pq = m - n * PQ;
+        const int g = blk_shift ? (m >> 4) : m;
+        const int n = g / PQ;
+        const int pq = g - n * PQ;
         const int pp = pq / p.Q;
         const int qq = pq - pp * p.Q;
         const int h0 = pp * p.sh - p.ph;
         const int w0 = qq * p.sw - p.pw;
-        pixb[j] = (uint32_t)((n * p.H * p.W + h0 * p.W + w0 + p0) * C * EB + Sh::lane_chunk() * CHUNK_BYTES);
+        const uint32_t nn_off = blk_shift ? (uint32_t)((m & 15) * 16 * EB) : 0u;
+        pixb[j] = ((uint32_t)((n * p.H * p.W + h0 * p.W + w0 + p0) * C * EB) << blk_shift) + nn_off + chunk_off;
         uint32_t mk = 0;
         for (int r = 0; r < p.R; ++r)
           for (int s2 = 0; s2 < p.S; ++s2)
@@ -596,7 +632,7 @@ struct Im2colC64Loader {
     const int tap = cur_r * S + cur_s;
     // tiles past the last tap (prefetch beyond K) use bit 31, never set
     const int bit = tap < RS ? tap : 31;
-    const long long toff = ((long long)(cur_r * W + cur_s - p0) * C + cur_c) * EB;
+    const long long toff = (((long long)(cur_r * W + cur_s - p0) * C + cur_c) * EB) << blk_shift;
     const uint64_t base = (uint64_t)(uintptr_t)x + (uint64_t)toff;
     // bytes of x past the moved base, at most 2^31 so that OOB stays out of
     // range (0 once the tap has left x: every lane then reads zeros)
@@ -1177,7 +1213,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       if (row < p.M && col < p.N) {
         const bool full = col + 3 < p.N;
         if constexpr (!INT8) {
-          float* dst = p.Cf + (long long)row * p.ldcf + col;
+          // (blocked output: 16-column block col/16 of 16-row group row/16 is
+          // one 16 x 16 array; 4 consecutive columns stay inside it)
+          float* dst = p.blk ? p.Cf + ((long long)(row >> 4) * (p.N >> 4) + (col >> 4)) * 256 + (row & 15) * 16 + (col & 15)
+                             : p.Cf + (long long)row * p.ldcf + col;
           if (full && p.vec_c) {
             store16_nt(dst, v);
           } else {

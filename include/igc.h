@@ -212,6 +212,45 @@ int conv2d_implicit_gemm_workspace_size(int Nb, int H, int W, int C, int Kout, i
                                         size_t* bytes);
 
 /*
+ * conv2d_implicit_gemm_nhwcnc -- the same convolution as conv2d_implicit_gemm
+ * (fp16 in, fp32 accumulation and output, cross-correlation, dilation 1,
+ * groups 1) on tensors in the blocked NHWCnc layout of [CONV-TC]
+ * "Preparation and algorithm" (block size 16):
+ *
+ *   x  fp16 [Nb/16][H][W][C/16][16 (n % 16)][16 (c % 16)]        (data_shape)
+ *   w  fp16 [R][S][C/16][Kout/16][16 (c % 16)][16 (k % 16)]      (kernel_shape)
+ *   y  fp32 [Nb/16][P][Q][Kout/16][16 (n % 16)][16 (k % 16)]     (output_shape)
+ *
+ *   y[n,p,q,k] = sum_{r,s,c} xpad[n, p*stride_h + r, q*stride_w + s, c] * w[r,s,c,k]
+ *
+ * with the logical indices placed in the blocks as shown.  Nb, C and Kout
+ * must be multiples of 16.  GEMM view: M = Nb*P*Q rows ordered
+ * ((n/16, p, q), n % 16), N = Kout, K = R*S*C.  The weights keep the output
+ * channels innermost, while the matrix cores read both operands with the
+ * reduction contiguous, so each call first writes the weights in K-contiguous
+ * order into the workspace (Kout*R*S*C*2 bytes); the workspace is therefore
+ * required: conv2d_implicit_gemm_nhwcnc_workspace_size gives its size, which
+ * also covers the stream-K part (zero-filled before first use, as for the
+ * other entry points).  16-byte aligned x with C a multiple of 64 and
+ * R*S <= 31 take the uniform-tap path.
+ * Errors: as conv2d_implicit_gemm, plus IGC_EINVAL when Nb, C or Kout is not
+ * a multiple of 16, when the workspace is NULL, misaligned or too small, or
+ * w is not 16-byte aligned.
+ */
+int conv2d_implicit_gemm_nhwcnc(int Nb, int H, int W, int C, int Kout, int R, int S,
+                                int stride_h, int stride_w, int pad_h, int pad_w,
+                                const void* x, const void* w, float* y,
+                                void* workspace, size_t ws_bytes,
+                                void* stream);
+
+/* conv2d_implicit_gemm_nhwcnc_workspace_size -- the workspace bytes
+ * conv2d_implicit_gemm_nhwcnc needs for these sizes on the current device
+ * (never 0).  Errors: as the convolution's argument checks, IGC_ENODEV. */
+int conv2d_implicit_gemm_nhwcnc_workspace_size(int Nb, int H, int W, int C, int Kout, int R, int S,
+                                               int stride_h, int stride_w, int pad_h, int pad_w,
+                                               size_t* bytes);
+
+/*
  * conv2d_u8i8_zp -- quantized 2-D convolution: u8 activations x i8 weights
  * with input zero points, int32 accumulation and the same fused outputs as
  * gemm_u8i8_zp (int32, dequantized fp32, requantized int8 per output

@@ -149,4 +149,4 @@ def workload(name: str, *, scale_down: int = 1) -> Workload:
     raise KeyError(name)
 
 
-WORKLOADS = ("c1", "c2", "c3", "c4", "c5", "q4")
+WORKLOADS = ("c1", "c2", "c3", "c4", "c5", "q4", "b4")

@@ -132,6 +132,26 @@ def test_conv_validation(igc):
     assert "32768" in igc.last_error()
 
 
+def test_conv_nhwcnc_validation(igc):
+    E = igc.IGC_EINVAL
+
+    def f(Nb=16, H=4, W=4, C=16, Kout=16, R=3, S=3, sh=1, sw=1, ph=1, pw=1, x=16, w=16, y=16, ws=256, nws=1 << 20):
+        return igc.conv2d_implicit_gemm_nhwcnc(Nb, H, W, C, Kout, R, S, sh, sw, ph, pw, x, w, y,
+                                               workspace=ws, ws_bytes=nws, check=False)
+
+    assert f(Nb=8) == E                                # blocks of 16 images
+    assert f(C=24) == E                                # blocks of 16 channels
+    assert f(Kout=40) == E
+    assert f(x=None) == E
+    assert f(ws=None, nws=0) == E                      # the workspace is required
+    assert "workspace" in igc.last_error()
+    assert f(w=24) == E                                # misaligned weights
+    assert f(R=7) == E                                 # filter larger than the padded input
+    out = ctypes.c_size_t(0)
+    L = igc.load()
+    assert L.conv2d_implicit_gemm_nhwcnc_workspace_size(8, 4, 4, 16, 16, 3, 3, 1, 1, 1, 1, ctypes.byref(out)) == E
+
+
 def test_qconv_validation(igc):
     E = igc.IGC_EINVAL
 

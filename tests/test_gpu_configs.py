@@ -182,3 +182,42 @@ def test_q4_full(igc, oracle):
     print(f"q4: {int(np.count_nonzero((ref > -128) & (ref < 127)))} of {ref.size} outputs unsaturated",
           flush=True)
     assert np.array_equal(Q, ref)
+
+
+def run_b4(igc, wl):
+    import torch
+
+    d = wl.dims
+    dims = (d["Nb"], d["H"], d["W"], d["C"], d["Kout"], d["R"], d["S"], d["stride_h"], d["stride_w"],
+            d["pad_h"], d["pad_w"])
+    dx, dw = to_dev(wl.arrays["x"]), to_dev(wl.arrays["w"])
+    dy = empty_dev((d["Nb"] // 16, 14, 14, d["Kout"] // 16, 16, 16), torch.float32)
+    igc.conv2d_implicit_gemm_nhwcnc(*dims, dx, dw, dy,
+                                    workspace=workspace_for(igc.conv2d_implicit_gemm_nhwcnc_workspace_size(*dims)))
+    return to_host(dy)
+
+
+def test_b4_full(igc, oracle):
+    """The 256x14x14 convolution in the tutorial's blocked NHWCnc layout, every output."""
+    wl = synth.workload("b4")
+    y = run_b4(igc, wl)
+    ref = oracle.conv2d_nhwcnc_direct(wl.arrays["x"], wl.arrays["w"], (1, 1), (1, 1))
+    assert report("b4 (all 256x14x14x512 outputs, blocked)", y, ref) <= FP_TOL
+
+
+def test_b4_streamk_full(igc, oracle):
+    """The same on 256x256 tiles with the last round's tiles shared (stream-K,
+    forced).  Whole tiles sum every output in the same K order whatever their
+    size, so the split is seen as the shared tiles' outputs differing from an
+    unsplit run on the same tiles in their last bits."""
+    wl = synth.workload("b4")
+    igc.set_tuning(0, 0)
+    try:
+        y0 = run_b4(igc, wl)
+        igc.set_tuning(0, 2)
+        y = run_b4(igc, wl)
+    finally:
+        igc.set_tuning(-1, 1)
+    assert np.any(y != y0), "the forced split left every output as the whole-tile run"
+    ref = oracle.conv2d_nhwcnc_direct(wl.arrays["x"], wl.arrays["w"], (1, 1), (1, 1))
+    assert report("b4 stream-K (all outputs, blocked)", y, ref) <= FP_TOL

@@ -541,3 +541,87 @@ def test_qconv_requant_only(igc, oracle, variant, case):
     Q = (W + 2 * pd[1] - S) // st[1] + 1
     Cref = oracle.conv2d_u8i8_direct_at(x, zA, w, zB, np.arange(Nb * P * Q), st, pd)
     assert np.array_equal(got["Q"], oracle.requant(Cref, scale, bias))
+
+
+# ----------------------------------------------------------------- blocked NHWCnc conv
+def run_conv_nhwcnc(igc, xb, wb, stride, pad, x_offset=0):
+    """x_offset: bytes by which x is shifted from a 16-byte boundary (the
+    element-wise loader)."""
+    import torch
+
+    NB, H, W, CB = xb.shape[:4]
+    R, S, _, OB = wb.shape[:4]
+    dims = (16 * NB, H, W, 16 * CB, 16 * OB, R, S, stride[0], stride[1], pad[0], pad[1])
+    P = (H + 2 * pad[0] - R) // stride[0] + 1
+    Q = (W + 2 * pad[1] - S) // stride[1] + 1
+    if x_offset:
+        raw = empty_dev((xb.size + 8,), torch.float16)
+        raw[x_offset // 2: x_offset // 2 + xb.size].copy_(to_dev(xb.reshape(-1)))
+        dx = raw.data_ptr() + x_offset
+        keep = raw
+    else:
+        keep = dx = to_dev(xb)
+    dy = to_dev(np.full((NB, P, Q, OB, 16, 16), np.nan, np.float32))
+    ws = workspace_for(igc.conv2d_implicit_gemm_nhwcnc_workspace_size(*dims))
+    igc.conv2d_implicit_gemm_nhwcnc(*dims, dx, to_dev(wb), dy, workspace=ws)
+    del keep
+    return to_host(dy)
+
+
+NHWCNC_CASES = [
+    # NB, H, W, CB, OB, R, S, stride, pad
+    (1, 14, 14, 16, 32, 3, 3, (1, 1), (1, 1)),  # 16 images of the 256x14x14 conv: uniform-tap path
+    (1, 9, 11, 4, 6, 3, 3, (1, 1), (1, 1)),     # C = 64
+    (2, 6, 7, 2, 3, 3, 3, (2, 1), (1, 0)),      # C = 32: 8-channel chunks across taps
+    (1, 8, 8, 1, 2, 1, 1, (1, 1), (0, 0)),      # C = 16, 1x1
+    (1, 13, 10, 3, 2, 5, 5, (2, 2), (2, 2)),    # C = 48
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("case", NHWCNC_CASES)
+def test_conv_nhwcnc_integer_valued_bit_exact(igc, oracle, variant, case):
+    NB, H, W, CB, OB, R, S, stride, pad = case
+    rng = np.random.default_rng(NB * 1000 + H * 100 + W * 10 + CB)
+    xb = synth.f16_small_ints(rng, (NB, H, W, CB, 16, 16), -4, 4)
+    wb = synth.f16_small_ints(rng, (R, S, CB, OB, 16, 16), -4, 4)
+    y = run_conv_nhwcnc(igc, xb, wb, stride, pad)
+    assert np.array_equal(y.astype(np.float64), oracle.conv2d_nhwcnc_direct(xb, wb, stride, pad))
+
+
+@pytest.mark.parametrize("variant", VARIANTS, indirect=True)
+@pytest.mark.parametrize("case", [NHWCNC_CASES[0], NHWCNC_CASES[2], NHWCNC_CASES[4]])
+def test_conv_nhwcnc_random_tolerance(igc, oracle, variant, case):
+    NB, H, W, CB, OB, R, S, stride, pad = case
+    rng = np.random.default_rng(7 + H + CB)
+    xb = synth.f16_normal(rng, (NB, H, W, CB, 16, 16))
+    wb = synth.f16_normal(rng, (R, S, CB, OB, 16, 16), std=0.05)
+    y = run_conv_nhwcnc(igc, xb, wb, stride, pad)
+    assert fp_rel_err(y, oracle.conv2d_nhwcnc_direct(xb, wb, stride, pad)) <= FP_TOL
+
+
+@pytest.mark.parametrize("case", [NHWCNC_CASES[1], NHWCNC_CASES[2]])
+def test_conv_nhwcnc_misaligned_input(igc, oracle, case):
+    """x two bytes past a 16-byte boundary: the element-wise loader."""
+    NB, H, W, CB, OB, R, S, stride, pad = case
+    rng = np.random.default_rng(11 + CB)
+    xb = synth.f16_small_ints(rng, (NB, H, W, CB, 16, 16), -4, 4)
+    wb = synth.f16_small_ints(rng, (R, S, CB, OB, 16, 16), -4, 4)
+    y = run_conv_nhwcnc(igc, xb, wb, stride, pad, x_offset=2)
+    assert np.array_equal(y.astype(np.float64), oracle.conv2d_nhwcnc_direct(xb, wb, stride, pad))
+
+
+def test_conv_nhwcnc_matches_the_nhwc_path(igc):
+    """The same logical convolution through both entry points gives the same
+    fp32 values (same tiles, same K order)."""
+    import torch
+
+    rng = np.random.default_rng(5)
+    NB, H, W, CB, OB = 1, 9, 11, 4, 6
+    xb = synth.f16_normal(rng, (NB, H, W, CB, 16, 16))
+    wb = synth.f16_normal(rng, (3, 3, CB, OB, 16, 16), std=0.05)
+    yb = run_conv_nhwcnc(igc, xb, wb, (1, 1), (1, 1))
+    x = np.ascontiguousarray(xb.transpose(0, 4, 1, 2, 3, 5).reshape(16 * NB, H, W, 16 * CB))
+    w = np.ascontiguousarray(wb.transpose(3, 5, 0, 1, 2, 4).reshape(16 * OB, 3, 3, 16 * CB))
+    y = run_conv(igc, x, w, (1, 1), (1, 1))
+    assert np.array_equal(yb.transpose(0, 4, 1, 2, 3, 5).reshape(y.shape), y)
