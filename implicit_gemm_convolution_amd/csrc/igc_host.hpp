@@ -34,8 +34,9 @@ enum Variant {
   V_64x64 = 2,
   V_256x128 = 3,
   V_224x256 = 4,
-  V_BYPASS = 5,  // fp16 GEMM, aligned operands: 32x32 tiles, one wave each, no LDS
-  V_COUNT = 6
+  V_BYPASS = 5,    // fp16 GEMM, aligned operands: 32x32 tiles, one wave each, no LDS
+  V_BYPASS16 = 6,  // the same with 16x16 tiles (four times the waves)
+  V_COUNT = 7
 };
 
 // Process-wide tuning overrides set by igc_set_tuning (tests and sweeps):
@@ -53,6 +54,7 @@ inline void variant_tile(int v, int& bm, int& bn) {
     case V_256x128: bm = 256; bn = 128; return;
     case V_128x128: bm = 128; bn = 128; return;
     case V_BYPASS: bm = 32; bn = 32; return;
+    case V_BYPASS16: bm = 16; bn = 16; return;
     default: bm = 64; bn = 64; return;
   }
 }
@@ -73,15 +75,21 @@ inline int choose_variant(int M, int N, int cus) {
   return V_64x64;
 }
 
-// Stream-K (shared tiles): when the 256x256 tiles do not fill the last
-// round of compute units, the whole rounds run as whole tiles and the rest
-// of the tiles' K-tile iterations are split evenly over up to one workgroup
-// per compute unit (at least 4 iterations each).  fp16 GEMM and conv only.
-// It pays only when the idle part of the last round is worth more than the
-// cost of publishing and summing the partial tiles, measured on MI355X at
-// about 26 K-tile iterations (4096^2 conv tiles: 392 tiles on 256 CUs, 36
-// iterations each, ran 12% slower split).
+// Stream-K (shared tiles): when the tiles do not fill the last round of
+// compute units (or a grid smaller than one round leaves most of them idle),
+// the whole rounds run as whole tiles and the rest of the tiles' K-tile
+// iterations are split evenly over up to one workgroup per compute unit (at
+// least 4 iterations each).  Compiled for every fp16 tile and for the u8 x i8
+// tiles of at most 128 rows.  It pays only when the idle part of the last
+// round is worth more than the cost of publishing and summing the partial
+// tiles, measured on MI355X at about 26 K-tile iterations per compute unit
+// (4096^2 conv tiles: 392 tiles of 256x256 on 256 CUs, 36 iterations each,
+// ran 12% slower split).
 constexpr long long kStreamKFixupIters = 26;
+
+inline bool streamk_compiled(bool int8, int v) {
+  return int8 ? (v == V_128x128 || v == V_64x64) : (v != V_BYPASS && v != V_BYPASS16);
+}
 
 // Everything a launch needs to know before it enqueues anything; a pure
 // function of the problem, the device's compute-unit count and the tuning
@@ -107,16 +115,22 @@ inline Plan make_plan(int kind, int M, int N, int K, bool fast, int cus, bool ws
   const bool int8 = kind == igc::KIND_U8I8_GEMM || kind == igc::KIND_U8I8_CONV;
   int v;
   if (kind == igc::KIND_F16_GEMM && fast &&
-      (fv == V_BYPASS ||
+      (fv == V_BYPASS || fv == V_BYPASS16 ||
        (fv == V_AUTO && ceil_div(M, 32) * ceil_div(N, 32) <= cus && K <= 512))) {
     // The LDS-bypass kernel wins only where the whole problem is one short
     // round: measured on MI355X, 256^3 3.6 us against 4.1 (64x64 tiles),
     // 512^3 4.8 against 4.9, but 1024^3 16.4 against 6.6 and 256x256x4096
     // 23.5 against 14.2 (a single wave then walks a long K loop alone).
-    v = V_BYPASS;
+    // Its 16x16 tiles, where they still fit one wave per compute unit, spread
+    // the problem over four times the compute units: 256^3 2.87 us against
+    // 3.73 (kernel time, rocprofv3).
+    if (fv == V_AUTO)
+      v = ceil_div(M, 16) * ceil_div(N, 16) <= cus ? V_BYPASS16 : V_BYPASS;
+    else
+      v = fv;
   } else {
     v = fv == V_AUTO ? choose_variant(M, N, cus) : fv;
-    if (v == V_BYPASS) v = V_64x64;  // (forced, for a kind or shape without the bypass kernel)
+    if (v == V_BYPASS || v == V_BYPASS16) v = V_64x64;  // (forced, for a kind or shape without the bypass kernel)
     // The element-wise (unaligned) loaders need more registers; they stop at 128x128.
     if (!fast && (v == V_256x256 || v == V_256x128 || v == V_224x256)) v = V_128x128;
   }
@@ -129,11 +143,11 @@ inline Plan make_plan(int kind, int M, int N, int K, bool fast, int cus, bool ws
   pl.dp_tiles = (int)std::min(grid, 0x7fffffffLL);
   pl.xcd_regroup = grid > cus;  // several rounds of workgroups per compute unit
   const int mode = g_streamk_mode.load(std::memory_order_relaxed);
-  if (v == V_256x256 && fast && !int8 && ws_ok && mode != 0) {
-    const long long nk = ceil_div((long long)K * 2, igc::KT_BYTES);
+  if (streamk_compiled(int8, v) && fast && ws_ok && mode != 0) {
+    const long long nk = ceil_div((long long)K * (int8 ? 1 : 2), igc::KT_BYTES);
     // iterations the last round leaves idle, per compute unit
     const long long idle = (cus - grid % cus) * nk / cus;
-    if (grid > cus && grid % cus != 0 && nk >= 4 && (mode == 2 || idle > kStreamKFixupIters)) {
+    if (grid % cus != 0 && nk >= 4 && (mode == 2 || idle > kStreamKFixupIters)) {
       const long long dp = grid / cus * cus;
       const long long iters = (grid - dp) * nk;
       const long long wgs = std::min((long long)cus, std::max(1LL, iters / 4));
@@ -197,7 +211,10 @@ int launch_variant(const igc::Params& p, const Plan& pl, hipStream_t stream) {
 
 inline int launch_bypass(const igc::Params& p, const Plan& pl, hipStream_t stream) {
   if (pl.grid > 0x7fffffffLL) return fail(IGC_EUNSUPPORTED, "too many tiles (%lld)", pl.grid);
-  hipLaunchKernelGGL((igc::gemm_f16_bypass_kernel<8>), dim3((unsigned)pl.grid), dim3(64), 0, stream, p);
+  if (pl.variant == V_BYPASS16)
+    hipLaunchKernelGGL((igc::gemm_f16_bypass_kernel<8, 16>), dim3((unsigned)pl.grid), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((igc::gemm_f16_bypass_kernel<8, 32>), dim3((unsigned)pl.grid), dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   return IGC_OK;
@@ -207,7 +224,7 @@ inline int launch_bypass(const igc::Params& p, const Plan& pl, hipStream_t strea
 template <int KIND, int SUMS>
 int launch(const igc::Params& p, const Plan& pl, bool fast, hipStream_t stream) {
   if constexpr (KIND == igc::KIND_F16_GEMM) {
-    if (pl.variant == V_BYPASS) return launch_bypass(p, pl, stream);
+    if (pl.variant == V_BYPASS || pl.variant == V_BYPASS16) return launch_bypass(p, pl, stream);
   }
   if constexpr (KIND == igc::KIND_F16_CONV_C64) {
     return launch_variant<KIND, true, SUMS>(p, pl, stream);  // dispatched only with aligned operands

@@ -138,11 +138,18 @@ struct Params {
   int* cnt;
 };
 
+// NARROW: sk_iters * sk_wgs < 2^32 (the integer kernels: K <= 33025 keeps
+// sk_iters below 2^17), so 32-bit unsigned division serves; its lowering
+// uses no fused multiply-add, which the requantize epilogue must not contain.
+template <bool NARROW = false>
 __device__ __forceinline__ long long sk_start(const Params& p, int g) {
+  if constexpr (NARROW) return (long long)((uint32_t)g * (uint32_t)p.sk_iters / (uint32_t)p.sk_wgs);
   return (long long)g * p.sk_iters / p.sk_wgs;
 }
 // the stream-K workgroup whose range holds iteration x
+template <bool NARROW = false>
 __device__ __forceinline__ int sk_owner(const Params& p, long long x) {
+  if constexpr (NARROW) return (int)(((uint32_t)(x + 1) * (uint32_t)p.sk_wgs - 1u) / (uint32_t)p.sk_iters);
   return (int)(((x + 1) * p.sk_wgs - 1) / p.sk_iters);
 }
 
@@ -763,9 +770,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // The A stage arrays also stage 32 output rows of BN fp32/int32 each in
   // the epilogue, so a tile with BM < BN allocates them at that size.
   constexpr int SA_ALLOC = SA > 32 * BN * 4 ? SA : 32 * BN * 4;
-  // stream-K (shared tiles) is compiled for the fp16 kinds; the integer GEMM
-  // always gets whole tiles (the host sets dp_tiles accordingly)
-  constexpr bool SK = !INT8 && SUMS == 0;
+  // stream-K (shared tiles): compiled for the fp16 kinds and for the integer
+  // kinds' aligned tiles of at most 128 rows (the wider integer tiles use
+  // every register); the host splits only where it is compiled
+  constexpr bool SK = INT8 ? (BM <= 128 && FAST) : (SUMS == 0);
   // (the im2col operand walks K in order, so the conv's B does too)
   constexpr bool CONV = KIND == KIND_F16_CONV || KIND == KIND_F16_CONV_C64 || KIND == KIND_U8I8_CONV;
   // u8 activations through the uniform-tap loader: padded chunks land as
@@ -817,8 +825,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   } else {
     const int g = blockIdx.x - p.dp_tiles;
     const long long base = (long long)p.dp_tiles * nk;
-    it = base + sk_start(p, g);
-    it_end = base + sk_start(p, g + 1);
+    it = base + sk_start<INT8>(p, g);
+    it_end = base + sk_start<INT8>(p, g + 1);
   }
   bool first_seg = true;
   while (it < it_end) {
@@ -1134,8 +1142,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       return v;
     };
     // K-tail padding loads as byte 0 and is stored as A' = -128: add those
-    // terms back.
-    const int pad_fix = 128 * (nk * KT_BYTES - p.K);
+    // terms back (in the segment that multiplied the partial K tile: the
+    // first with the tail-first order, else the last).
+    const bool has_tail = TAIL_FIRST ? k0 == 0 : k1 == nk;
+    const int pad_fix = has_tail ? 128 * (nk * KT_BYTES - p.K) : 0;
     if constexpr (MSUMS) {
       // racc: lane l, register e holds the sum of row l % 16 of A' block
       // 4*(l/16) + e; cacc: lane l (l % 16 = j < FN), register e holds the
@@ -1200,15 +1210,17 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   const long long xs = (long long)j_sk * nk;  // tile start in the stream-K range
   int g_lo = 0, g_hi = 0;
   if (mode) {
-    g_lo = sk_owner(p, xs);
-    g_hi = sk_owner(p, xs + nk - 1);
+    g_lo = sk_owner<INT8>(p, xs);
+    g_hi = sk_owner<INT8>(p, xs + nk - 1);
   }
   constexpr int SLOT = BM * BN * 4;  // bytes per partial tile
-  auto slot_of = [&](int gg) { return (2 * gg + (sk_start(p, gg) >= xs ? 0 : 1)) * SLOT; };
+  auto slot_of = [&](int gg) { return (2 * gg + (sk_start<INT8>(p, gg) >= xs ? 0 : 1)) * SLOT; };
   const __amdgpu_buffer_rsrc_t wsr =
       __builtin_amdgcn_make_buffer_rsrc(p.ws, (short)0, 2 * p.sk_wgs * SLOT, 0x00020000);
   // One group of 4 columns of one row leaves for the outputs.
-  auto emit = [&](uint4 v, int lrow) {
+  // corrected: v already holds the zero-point-corrected sum without the
+  // K*zA'*zB term (the shared tiles of the integer kernels)
+  auto emit = [&](uint4 v, int lrow, bool corrected) {
     const int row = m0 + lrow;
       if (row < p.M && col < p.N) {
         const bool full = col + 3 < p.N;
@@ -1229,14 +1241,15 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           // C = acc' - zA'*colsum(B) - zB*rowsum(A') + K*zA'*zB in wrapping
           // 32-bit arithmetic; the true value fits in int32 (K <= 33025).
           uint32_t rcorr = 0;
-          if constexpr ((SUMS & SUM_ROWS) != 0) rcorr = p.zB != 0 ? (uint32_t)p.zB * (uint32_t)sums[lrow] : 0u;
+          if constexpr ((SUMS & SUM_ROWS) != 0)
+            rcorr = (p.zB != 0 && !corrected) ? (uint32_t)p.zB * (uint32_t)sums[lrow] : 0u;
           const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
           int32_t c[4];
   #pragma unroll
           for (int q = 0; q < 4; ++q) {
             uint32_t ccorr = 0;
             if constexpr ((SUMS & SUM_COLS) != 0)
-              ccorr = p.zAp != 0 ? (uint32_t)p.zAp * (uint32_t)sums[BM + min(lcol + q, BN - 1)] : 0u;
+              ccorr = (p.zAp != 0 && !corrected) ? (uint32_t)p.zAp * (uint32_t)sums[BM + min(lcol + q, BN - 1)] : 0u;
             c[q] = (int32_t)(vv[q] - ccorr - rcorr + kzz);
           }
           if (p.Ci) {
@@ -1389,12 +1402,28 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
         const int voff = (lrow * BN + lcol) * 4;
         if constexpr (SK) {
           if (mode == 1) {
+            if constexpr (INT8) {
+              // this segment's share of acc' - zA'*colsum(B) - zB*rowsum(A'),
+              // from its own K range's sums (wrapping; the shares add up to
+              // the exact int32 total)
+              uint32_t rcorr = 0;
+              if constexpr ((SUMS & SUM_ROWS) != 0) rcorr = p.zB != 0 ? (uint32_t)p.zB * (uint32_t)sums[lrow] : 0u;
+              uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                uint32_t ccorr = 0;
+                if constexpr ((SUMS & SUM_COLS) != 0)
+                  ccorr = p.zAp != 0 ? (uint32_t)p.zAp * (uint32_t)sums[BM + lcol + q] : 0u;
+                vv[q] = vv[q] - ccorr - rcorr;
+              }
+              v = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+            }
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), wsr, voff,
                                                    (2 * g + (first_seg ? 0 : 1)) * SLOT, CPOL_DEV);
             continue;
           }
         }
-        if (mode == 0) emit(v, lrow);
+        if (mode == 0) emit(v, lrow, false);
       }
       __syncthreads();
     }
@@ -1445,7 +1474,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           }
         }
 #pragma unroll
-        for (int b = 0; b < RB; ++b) emit(v[b], lrow0 + b * RPP);
+        for (int b = 0; b < RB; ++b) emit(v[b], lrow0 + b * RPP, true);
       }
     }
   }
@@ -1458,7 +1487,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 // ---------------------------------------------------------------------------
 // LDS-bypass fp16 GEMM for small, latency-bound problems ([GEMM-TVM] §3.4:
 // operands loaded from global memory straight into the tensor-core operand
-// registers, no shared-memory staging).  One wave per 32 x 32 output tile;
+// registers, no shared-memory staging).  One wave per T x T output tile
+// (T = 32: 2 x 2 blocks of 16 x 16; T = 16: one block, four times as many
+// waves, so a 256^3 problem spreads over 256 compute units instead of 64);
 // lane l loads, for each 16-row block of A and of B, row l % 16 and the
 // 16-byte chunk l / 16 of each 64-byte k-step, i.e. exactly its MFMA operand.
 // KC k-steps of loads are issued before the first MFMA that needs them.  No
@@ -1467,57 +1498,63 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 // lane l holds row l % 16, columns 4*(l/16) .. +3), so each block leaves in
 // one 16-byte store per lane.
 // ---------------------------------------------------------------------------
-template <int KC>
+template <int KC, int T = 32>
 __global__ void __launch_bounds__(64, 1) gemm_f16_bypass_kernel(const Params p) {
+  static_assert(T == 16 || T == 32, "wave tile of one or two 16-row blocks per side");
+  constexpr int FB = T / 16;  // 16 x 16 blocks per side
   const int lane = threadIdx.x & 63;
   const int tm = (int)blockIdx.x / p.tiles_n;
   const int tn = (int)blockIdx.x - tm * p.tiles_n;
-  const int m0 = tm * 32, n0 = tn * 32;
+  const int m0 = tm * T, n0 = tn * T;
   const long long lda2 = p.lda * 2, ldb2 = p.ldb * 2;
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.A + m0 * lda2), (short)0, (int)(min(32, p.M - m0) * lda2), 0x00020000);
+      const_cast<uint8_t*>(p.A + m0 * lda2), (short)0, (int)(min(T, p.M - m0) * lda2), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(p.B + n0 * ldb2), (short)0, (int)(min(32, p.N - n0) * ldb2), 0x00020000);
+      const_cast<uint8_t*>(p.B + n0 * ldb2), (short)0, (int)(min(T, p.N - n0) * ldb2), 0x00020000);
   const int frow = lane & 15;
   const uint32_t chunk = (uint32_t)(lane >> 4) * 16u;
-  const uint32_t oa0 = (uint32_t)(frow * lda2) + chunk, oa1 = (uint32_t)((frow + 16) * lda2) + chunk;
-  const uint32_t ob0 = (uint32_t)(frow * ldb2) + chunk, ob1 = (uint32_t)((frow + 16) * ldb2) + chunk;
+  uint32_t oa[FB], ob[FB];
+#pragma unroll
+  for (int i = 0; i < FB; ++i) {
+    oa[i] = (uint32_t)((frow + 16 * i) * lda2) + chunk;
+    ob[i] = (uint32_t)((frow + 16 * i) * ldb2) + chunk;
+  }
   const uint32_t kbytes = (uint32_t)p.K * 2u;
   const int nks = (p.K + 31) / 32;  // 64-byte k-steps
-  f32x4 acc[2][2];
+  f32x4 acc[FB][FB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto ld = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t off, uint32_t kb) {
     // k past K reads out of range (zeros): K % 8 == 0, so a chunk is all in or all out
     const uint32_t o = kb + chunk < kbytes ? off + kb : OOB;
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)o, 0, 0));
   };
   for (int kb = 0; kb < nks; kb += KC) {
-    uint4 a0[KC], a1[KC], b0[KC], b1[KC];
+    uint4 a[KC][FB], b[KC][FB];
 #pragma unroll
     for (int s = 0; s < KC; ++s) {
       const uint32_t k = (uint32_t)(kb + s) * 64u;
-      a0[s] = ld(ra, oa0, k);
-      a1[s] = ld(ra, oa1, k);
-      b0[s] = ld(rb, ob0, k);
-      b1[s] = ld(rb, ob1, k);
+#pragma unroll
+      for (int i = 0; i < FB; ++i) {
+        a[s][i] = ld(ra, oa[i], k);
+        b[s][i] = ld(rb, ob[i], k);
+      }
     }
 #pragma unroll
-    for (int s = 0; s < KC; ++s) {
-      Mfma<KIND_F16_GEMM, 16>::run(acc[0][0], b0[s], a0[s]);
-      Mfma<KIND_F16_GEMM, 16>::run(acc[0][1], b1[s], a0[s]);
-      Mfma<KIND_F16_GEMM, 16>::run(acc[1][0], b0[s], a1[s]);
-      Mfma<KIND_F16_GEMM, 16>::run(acc[1][1], b1[s], a1[s]);
-    }
+    for (int s = 0; s < KC; ++s)
+#pragma unroll
+      for (int i = 0; i < FB; ++i)
+#pragma unroll
+        for (int j = 0; j < FB; ++j) Mfma<KIND_F16_GEMM, 16>::run(acc[i][j], b[s][j], a[s][i]);
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < FB; ++i) {
     const int row = m0 + i * 16 + frow;
     if (row >= p.M) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < FB; ++j) {
       const int col = n0 + j * 16 + (lane >> 4) * 4;
       float* dst = p.Cf + (long long)row * p.ldcf + col;
       const float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];

@@ -297,8 +297,9 @@ int igc_device_check(void);                /* IGC_OK if the current device is gf
  * made after it returns.
  *   force_variant  -1: the shape chooses the tile; 0: 256x256, 1: 128x128,
  *                  2: 64x64, 3: 256x128, 4: 224x256, 5: the fp16 LDS-bypass
- *                  kernel (32x32 tiles).  A tile the operands' path does not
- *                  have falls back to the nearest smaller one.
+ *                  kernel (32x32 tiles), 6: the same with 16x16 tiles.  A
+ *                  tile the operands' path does not have falls back to the
+ *                  nearest smaller one.
  *   streamk_mode   0: never split tiles; 1: split where it pays; 2: split
  *                  whenever the last round of tiles is partial.
  * Errors: IGC_EINVAL (value out of range).

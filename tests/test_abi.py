@@ -180,10 +180,10 @@ def test_qconv_validation(igc):
 def test_set_tuning_validation(igc):
     E = igc.IGC_EINVAL
     assert igc.set_tuning(-2, 1, check=False) == E
-    assert igc.set_tuning(6, 1, check=False) == E
+    assert igc.set_tuning(7, 1, check=False) == E
     assert igc.set_tuning(-1, 3, check=False) == E
     assert igc.set_tuning(-1, -1, check=False) == E
-    for v in range(-1, 6):
+    for v in range(-1, 7):
         for sk in range(3):
             assert igc.set_tuning(v, sk, check=False) == igc.IGC_OK
     assert igc.set_tuning(-1, 1, check=False) == igc.IGC_OK

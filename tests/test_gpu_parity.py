@@ -79,11 +79,12 @@ def test_f16_integer_valued_bit_exact(igc, oracle, variant, M, N, K):
     assert np.array_equal(C.astype(np.float64), ref)
 
 
-# The LDS-bypass fp16 kernel (forced): 32x32 tiles, one wave each, operands
-# loaded straight into the MFMA registers.
+# The LDS-bypass fp16 kernel (forced): 32x32 or 16x16 tiles, one wave each,
+# operands loaded straight into the MFMA registers.
+@pytest.mark.parametrize("bv", [5, 6])
 @pytest.mark.parametrize("M,N,K", F16_EXACT_SHAPES + [(256, 256, 1024), (70, 33, 520)])
-def test_f16_bypass_integer_valued_bit_exact(igc, oracle, M, N, K):
-    igc.set_tuning(5, 1)
+def test_f16_bypass_integer_valued_bit_exact(igc, oracle, bv, M, N, K):
+    igc.set_tuning(bv, 1)
     rng = np.random.default_rng(M * 131 + N * 7 + K)
     A = synth.f16_small_ints(rng, (M, K))
     Bt = synth.f16_small_ints(rng, (N, K))
@@ -91,9 +92,10 @@ def test_f16_bypass_integer_valued_bit_exact(igc, oracle, M, N, K):
     assert np.array_equal(C.astype(np.float64), oracle.gemm_f16(A, Bt))
 
 
+@pytest.mark.parametrize("bv", [5, 6])
 @pytest.mark.parametrize("M,N,K,ldc", [(256, 256, 256, 256), (200, 300, 1000, 301), (64, 48, 4096, 48)])
-def test_f16_bypass_random_tolerance(igc, oracle, M, N, K, ldc):
-    igc.set_tuning(5, 1)
+def test_f16_bypass_random_tolerance(igc, oracle, bv, M, N, K, ldc):
+    igc.set_tuning(bv, 1)
     rng = np.random.default_rng(M + N + K + 5)
     A = synth.f16_uniform(rng, (M, K))
     Bt = synth.f16_uniform(rng, (N, K))
@@ -625,3 +627,78 @@ def test_conv_nhwcnc_matches_the_nhwc_path(igc):
     w = np.ascontiguousarray(wb.transpose(3, 5, 0, 1, 2, 4).reshape(16 * OB, 3, 3, 16 * CB))
     y = run_conv(igc, x, w, (1, 1), (1, 1))
     assert np.array_equal(yb.transpose(0, 4, 1, 2, 3, 5).reshape(y.shape), y)
+
+
+# ----------------------------------------------------------------- split tiles on small grids
+# Grids smaller than one round of compute units with long K loops: every
+# tile's K-tile iterations are shared between workgroups (forced here; the
+# default splits where the idle part of the round is large).  The integer
+# kernels publish each segment's zero-point-corrected share and add
+# K*zA'*zB once, so the results stay exact.
+@pytest.mark.parametrize("v", ["1", "2"])
+@pytest.mark.parametrize("M,N,K", [(200, 136, 2064), (64, 64, 4096), (300, 260, 1040), (17, 260, 3008)])
+@pytest.mark.parametrize("zA,zB", [(128, 3), (0, 0), (37, -5), (255, 127), (128, 0)])
+def test_u8i8_split_tiles_bit_exact(igc, oracle, v, M, N, K, zA, zB):
+    igc.set_tuning(int(v), 2)
+    assert igc.gemm_u8i8_zp_workspace_size(M, N, K) > 0
+    rng = np.random.default_rng(M + 3 * N + 7 * K + zA - zB)
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = synth.i8_uniform(rng, (N, K), lo=-128, hi=127)
+    scale, bias = q_params(rng, N, K)
+    s = oracle.dequant_scale(0.02, 0.01)
+    got = run_u8i8(igc, A, zA, Bt, zB, scale=scale, bias=bias, dq=float(s))
+    check_u8i8(oracle, got, A, zA, Bt, zB, scale, bias)
+
+
+@pytest.mark.parametrize("v", ["1", "2"])
+def test_u8i8_split_tiles_requant_only_and_deterministic(igc, oracle, v):
+    igc.set_tuning(int(v), 2)
+    M, N, K = 256, 192, 4096
+    rng = np.random.default_rng(31)
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = synth.i8_uniform(rng, (N, K))
+    scale, bias = q_params(rng, N, K)
+    g1 = run_u8i8(igc, A, 100, Bt, -7, outputs=("Q",), scale=scale, bias=bias)
+    g2 = run_u8i8(igc, A, 100, Bt, -7, outputs=("Q",), scale=scale, bias=bias)
+    assert np.array_equal(g1["Q"], g2["Q"])
+    check_u8i8(oracle, g1, A, 100, Bt, -7, scale, bias)
+
+
+@pytest.mark.parametrize("v", ["1", "2"])
+@pytest.mark.parametrize("case", [QCONV_CASES[1], QCONV_CASES[2], QCONV_CASES[3], QCONV_CASES[8]])
+def test_qconv_split_tiles_bit_exact(igc, oracle, v, case):
+    Nb, H, W, C, Kout, R, S, stride, pad, zA, zB = case
+    igc.set_tuning(int(v), 2)
+    rng = np.random.default_rng(Nb + H + C + zA)
+    x = synth.u8_uniform(rng, (Nb, H, W, C))
+    w = synth.i8_uniform(rng, (Kout, R, S, C), lo=-128, hi=127)
+    scale, bias = q_params(rng, Kout, R * S * C)
+    got = run_qconv(igc, x, zA, w, zB, stride, pad, outputs=("C", "Q"), scale=scale, bias=bias)
+    P = (H + 2 * pad[0] - R) // stride[0] + 1
+    Q = (W + 2 * pad[1] - S) // stride[1] + 1
+    ref = oracle.conv2d_u8i8_direct_at(x, zA, w, zB, np.arange(Nb * P * Q), stride, pad)
+    assert np.array_equal(got["C"].astype(np.int64), ref)
+    assert np.array_equal(got["Q"], oracle.requant(ref, scale, bias))
+
+
+@pytest.mark.parametrize("v", ["1", "2"])
+@pytest.mark.parametrize("M,N,K", [(512, 128, 2048), (70, 33, 4104), (256, 256, 1024)])
+def test_f16_split_tiles_integer_valued_exact(igc, oracle, v, M, N, K):
+    igc.set_tuning(int(v), 2)
+    rng = np.random.default_rng(M + N + K + 9)
+    A = synth.f16_small_ints(rng, (M, K))
+    Bt = synth.f16_small_ints(rng, (N, K))
+    C = run_f16(igc, A, Bt)
+    assert np.array_equal(C.astype(np.float64), oracle.gemm_f16(A, Bt))
+
+
+@pytest.mark.parametrize("v", ["1", "2"])
+@pytest.mark.parametrize("case", [CONV_CASES[1], CONV_CASES[3]])
+def test_conv_split_tiles_integer_valued_exact(igc, oracle, v, case):
+    Nb, H, W, C, Kout, R, S, stride, pad = case
+    igc.set_tuning(int(v), 2)
+    rng = np.random.default_rng(Nb * 7 + H + C)
+    x = synth.f16_small_ints(rng, (Nb, H, W, C), -4, 4)
+    w = synth.f16_small_ints(rng, (Kout, R, S, C), -4, 4)
+    y = run_conv(igc, x, w, stride, pad)
+    assert np.array_equal(y.astype(np.float64), oracle.conv2d_direct(x, w, stride, pad))
