@@ -242,19 +242,40 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
 #endif
 // Direct-to-LDS load at byte offset off + soff (both range-checked against
 // the descriptor's size: past it, the lanes read zeros).
-// Five wait states: the compiler may produce the scalar operands (offset,
-// descriptor, M0) with vector instructions (v_readfirstlane, or v_readlane
-// when it spills scalar registers), and a vector memory instruction may only
-// read an SGPR written by a VALU instruction five wait states later.
+// One wait state: the compiler writes M0 with a scalar instruction right
+// before the asm, and an LDS-DMA load may read M0 one wait state after a
+// scalar write.  A vector memory instruction may read an SGPR written by a
+// VALU instruction (v_readfirstlane, v_readlane) only five wait states
+// later; the compiler cannot see that this asm reads its operands, so
+// tests/test_isa.py checks every shipped kernel's assembly for a VALU write
+// of an operand SGPR (descriptor, offset, M0) within the five wait states
+// before each of these loads.  Each wait state costs the wave an issue slot
+// (4 clocks): with five, the load sequence outlasted the 16-clock MFMA it
+// sits between and the matrix pipe idled.
+// The loads of the main loop take NOPS = 0 (one wait state); the prologue's,
+// where the compiler restores spilled scalar registers with v_readlane right
+// before them, take NOPS = 4 (five).
+constexpr int NOPS_LOOP = 0, NOPS_SAFE = 4;
+template <int NOPS>
 __device__ __forceinline__ void dma16s(const Rsrc& r, uint8_t* lds, uint32_t off, uint32_t soff) {
+  static_assert(NOPS == NOPS_LOOP || NOPS == NOPS_SAFE, "wait states");
   const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-  asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" : : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0)
-               : "memory");
+  if constexpr (NOPS == NOPS_SAFE)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 : : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0) : "memory");
+  else
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 : : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0) : "memory");
 }
+template <int NOPS>
 __device__ __forceinline__ void dma16(const Rsrc& r, uint8_t* lds, uint32_t off) {
+  static_assert(NOPS == NOPS_LOOP || NOPS == NOPS_SAFE, "wait states");
   if constexpr (IGC_DMA_ASM) {
     const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(r.d), "{m0}"(m0) : "memory");
+    if constexpr (NOPS == NOPS_SAFE)
+      asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(r.d), "{m0}"(m0) : "memory");
+    else
+      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(r.d), "{m0}"(m0) : "memory");
   } else {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r.r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
@@ -340,26 +361,29 @@ struct RowDmaLoader {
   // TAIL_FIRST: part() serves tiles kt >= 1 and part0() tile 0.
   static constexpr int NPART = FAST ? Sh::NQ : 1;
   __device__ __forceinline__ void advance() const {}
+  template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
 #pragma unroll
     for (int i = 0; i < NPART; ++i) {
       if (TAIL_FIRST && kt == 0)
-        part0(tile, i);
+        part0<NOPS>(tile, i);
       else
-        part(tile, kt, i);
+        part<NOPS>(tile, kt, i);
     }
   }
+  template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void part0(uint8_t* tile, int i) const {
-    dma16s(rsrc, Sh::dst(tile, i), lane_off0, (uint32_t)(i * row_step));
+    dma16s<NOPS>(rsrc, Sh::dst(tile, i), lane_off0, (uint32_t)(i * row_step));
   }
+  template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void part(uint8_t* tile, int kt, int i) const {
     if constexpr (FAST && TAIL_FIRST) {
       // tiles past K (prefetched by the pipeline, never multiplied) read
       // out of range: zeros, no memory traffic
-      dma16s(rsrc, Sh::dst(tile, i), voff[i], kt < nk ? (uint32_t)(kt * KT_BYTES - kpad) : OOB);
+      dma16s<NOPS>(rsrc, Sh::dst(tile, i), voff[i], kt < nk ? (uint32_t)(kt * KT_BYTES - kpad) : OOB);
     } else if (FAST) {
       const bool kin = kt * KT_BYTES + Sh::lane_chunk() * CHUNK_BYTES < K * EB;
-      dma16(rsrc, Sh::dst(tile, i), kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
+      dma16<NOPS>(rsrc, Sh::dst(tile, i), kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
     } else {
       constexpr int EPC = CHUNK_BYTES / EB;
       const int c = threadIdx.x & 7;  // thread t: chunk t%8 of rows t/8 + (NT/8)*j
@@ -492,9 +516,10 @@ struct Im2colLoader {
   // moves this lane's tap on by the 64 channels of one K tile); part j is one
   // direct-to-LDS load of 8 rows per wave.  Else part 0 does it all.
   static constexpr int NPART = FAST ? Sh::NQ : 1;
+  template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
 #pragma unroll
-    for (int j = 0; j < NPART; ++j) part(tile, kt, j);
+    for (int j = 0; j < NPART; ++j) part<NOPS>(tile, kt, j);
     advance();
   }
   __device__ __forceinline__ void advance() const {
@@ -509,6 +534,7 @@ struct Im2colLoader {
       }
     }
   }
+  template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void part(uint8_t* tile, int kt, int j) const {
     if (FAST) {
       const bool kin = kt * 64 + Sh::lane_chunk() * 8 < K;
@@ -518,7 +544,7 @@ struct Im2colLoader {
       const bool ok = kin && (unsigned)h < (unsigned)H && (unsigned)w < (unsigned)W;
       // (a chunk's 8 channels lie in one 16-channel block: cur_c % 8 == 0)
       const uint32_t off = (uint32_t)elem_index(j, pix[j] + tap, cur_c) * 2u;
-      dma16(rsrc, Sh::dst(tile, j), ok ? off : OOB);
+      dma16<NOPS>(rsrc, Sh::dst(tile, j), ok ? off : OOB);
     } else if constexpr (EB == 2) {
       const int c = threadIdx.x & 7;
       const int k0 = kt * 64 + c * 8;
@@ -630,11 +656,13 @@ struct Im2colC64Loader {
       }
     }
   }
+  template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
 #pragma unroll
-    for (int j = 0; j < NPART; ++j) part(tile, kt, j);
+    for (int j = 0; j < NPART; ++j) part<NOPS>(tile, kt, j);
     advance();
   }
+  template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void part(uint8_t* tile, int, int j) const {
     const int tap = cur_r * S + cur_s;
     // tiles past the last tap (prefetch beyond K) use bit 31, never set
@@ -648,7 +676,7 @@ struct Im2colC64Loader {
     Rsrc r;
     r.d = i32x4{(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)num, 0x00020000};
     const uint32_t vo = ((mask[j] >> bit) & 1u) ? pixb[j] : OOB;
-    dma16s(r, Sh::dst(tile, j), vo, 0);
+    dma16s<NOPS>(r, Sh::dst(tile, j), vo, 0);
   }
   // After this lane's loads of the next K tile (in order, one call per tile)
   // have landed in `tile`: its padded chunks get zA.  Each lane rewrites only
@@ -994,8 +1022,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // Prologue: tiles 0 .. DEPTH-1 in flight, tile 0 landed, its first
   // fragments read.
   static_for<DEPTH>([&](auto D) {
-    la.load(stA(D), k0 + decltype(D)::value);
-    lb.load(stB(D), k0 + decltype(D)::value);
+    la.template load<NOPS_SAFE>(stA(D), k0 + decltype(D)::value);
+    lb.template load<NOPS_SAFE>(stB(D), k0 + decltype(D)::value);
   });
   wait_vmcnt_lgkm0<(DEPTH - 1) * (NLA + NLB)>();
   // (zA = 0: the zeros of the out-of-range loads already are the zero point)

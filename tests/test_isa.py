@@ -130,3 +130,44 @@ def test_bypass_kernel_uses_no_lds(asm):
         assert int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", meta).group(1)) == 0
         assert "ds_read" not in body and "ds_write" not in body and "s_barrier" not in body
         assert re.search(r"global_store_dwordx4 .* nt", body), name
+
+
+def _sgprs(tok):
+    tok = tok.strip().rstrip(",")
+    m = re.fullmatch(r"s\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.fullmatch(r"s(\d+)", tok)
+    if m:
+        return {int(m.group(1))}
+    return {"m0"} if tok == "m0" else set()
+
+
+def test_direct_to_lds_loads_respect_sgpr_hazards(asm):
+    """The direct-to-LDS loads are inline assembly, which the compiler's hazard
+    recognizer does not see reading its scalar operands.  A vector memory
+    instruction may read an SGPR written by a VALU instruction only five wait
+    states later, and M0 one wait state after a scalar write; the main-loop
+    loads carry one wait state of their own, the prologue's five.  Check every
+    such load of every kernel: no VALU write of its descriptor, offset or M0
+    within the five wait states before it, and no M0 write right before it."""
+    checked = 0
+    for name, (body, _) in asm.items():
+        lines = [l.split(";")[0].strip() for l in body.splitlines()]
+        ins = [l for l in lines if l and not l.startswith(".") and not l.endswith(":")]
+        for i, l in enumerate(ins):
+            if not (l.startswith("buffer_load") and l.endswith(" lds")):
+                continue
+            checked += 1
+            ops = l.split(None, 1)[1].replace(" offen", "").replace(" lds", "").split(",")
+            reads = set().union(*[_sgprs(o) for o in ops[1:]]) | {"m0"}
+            ws, j = 0, i - 1
+            while j >= 0 and ws < 5:
+                prev = ins[j]
+                op = prev.split()[0]
+                dst = _sgprs(prev.split(None, 1)[1].split(",")[0]) if " " in prev else set()
+                assert not (op.startswith("v_") and dst & reads), (name, ws, prev, l)
+                assert not (op.startswith("s_") and "m0" in dst and ws < 1), (name, prev, l)
+                ws += int(prev.split()[1], 0) + 1 if op == "s_nop" else 1
+                j -= 1
+    assert checked > 1000
