@@ -282,6 +282,33 @@ __device__ __forceinline__ void dma16(const Rsrc& r, uint8_t* lds, uint32_t off)
   }
 }
 
+// dma16s for the lanes set in `lanes`; every other lane instead stores
+// `fill` into its own 16-byte slot of the same LDS rows (the slot its load
+// would have written: the wave's rows at M0, lane l at M0 + 16 l).  The
+// execution mask is narrowed, complemented and restored inside the asm, so
+// the load is issued even when no lane is set and every explicit vmcnt count
+// in the kernel stays exact; the store counts on lgkmcnt, which the kernel
+// waits for in full before a tile is read.
+template <int NOPS>
+__device__ __forceinline__ void dma16s_or_fill(const Rsrc& r, uint8_t* lds, uint32_t off, uint32_t soff,
+                                               uint64_t lanes, uint4 fill) {
+  static_assert(NOPS == NOPS_LOOP || NOPS == NOPS_SAFE, "wait states");
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  const uint32_t vaddr = m0 + (threadIdx.x & 63) * CHUNK_BYTES;
+  const u32x4 fv = __builtin_bit_cast(u32x4, fill);
+  uint64_t saved;
+  if constexpr (NOPS == NOPS_SAFE)
+    asm volatile(
+        "s_and_saveexec_b64 %0, %5\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+        "s_andn2_b64 exec, %0, %5\n\tds_write_b128 %6, %7\n\ts_mov_b64 exec, %0"
+        : "=&s"(saved) : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0), "s"(lanes), "v"(vaddr), "v"(fv) : "memory");
+  else
+    asm volatile(
+        "s_and_saveexec_b64 %0, %5\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+        "s_andn2_b64 exec, %0, %5\n\tds_write_b128 %6, %7\n\ts_mov_b64 exec, %0"
+        : "=&s"(saved) : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0), "s"(lanes), "v"(vaddr), "v"(fv) : "memory");
+}
+
 // Direct-to-LDS tiles of ROWS rows x 128 bytes.  Wave-instruction q fills
 // rows 8q .. 8q+7 (1 KB of LDS); lane l covers row 8q + l/8 and fetches the
 // global chunk that belongs in its LDS slot l % 8, i.e. chunk
@@ -305,6 +332,11 @@ struct DmaShape {
   __device__ static __forceinline__ uint8_t* dst(uint8_t* tile, int i) {
     return tile + (i * NWAVES + wave_id()) * 1024;
   }
+  // the same with the wave's offset (wave_id() * 1024) computed once
+  __device__ static __forceinline__ uint8_t* dst(uint8_t* tile, int i, uint32_t wofs) {
+    return tile + i * NWAVES * 1024 + wofs;
+  }
+  __device__ static __forceinline__ uint32_t wave_offset() { return (uint32_t)wave_id() * 1024u; }
 };
 
 // Operand loaded straight into LDS (A of the fp16 GEMM; the i8 B of the
@@ -319,8 +351,13 @@ struct DmaShape {
 //  arithmetic.  Otherwise tile kt holds bytes
 //  [128*kt, 128*kt + 128) and the K tail is masked in the last tile.  The
 //  two operands of a kernel must use the same order.
-template <int NT, int ROWS, int EB, bool FAST, bool TAIL_FIRST = false>
+//  WHOLE_K (FAST, K tiles walked in order, K * EB a multiple of 128: no
+//  partial tile): like TAIL_FIRST, every load is one of this lane's fixed
+//  offsets plus a scalar K offset.
+template <int NT, int ROWS, int EB, bool FAST, bool TAIL_FIRST = false, bool WHOLE_K = false>
 struct RowDmaLoader {
+  static_assert(!(TAIL_FIRST && WHOLE_K), "one K walk");
+  static constexpr bool SCALAR_K = FAST && (TAIL_FIRST || WHOLE_K);
   typedef DmaShape<NT, ROWS> Sh;
   const uint8_t* base;  // row 0 of this tile
   long long ld_bytes;
@@ -332,9 +369,11 @@ struct RowDmaLoader {
   uint32_t row_step;    // bytes between this lane's rows (uniform)
   int kpad;             // 128 * nk - K * EB: zero bytes in the partial tile
   int nk;               // K tiles
-  uint32_t voff[TAIL_FIRST ? Sh::NQ : 1];  // lane_off + i * row_step (TAIL_FIRST)
+  uint32_t voff[SCALAR_K ? Sh::NQ : 1];  // lane_off + i * row_step (scalar K offsets)
+  uint32_t wofs;        // this wave's offset in a tile's LDS rows
 
   __device__ __forceinline__ void init(const uint8_t* ptr, long long ld, int r0, int nrows, int k) {
+    wofs = Sh::wave_offset();
     ld_bytes = ld * EB;
     base = ptr + (long long)r0 * ld_bytes;
     rows_valid = nrows - r0;
@@ -347,7 +386,7 @@ struct RowDmaLoader {
       nk = max(1, (K * EB + KT_BYTES - 1) / KT_BYTES);
       kpad = nk * KT_BYTES - K * EB;
       lane_off0 = Sh::lane_chunk() * CHUNK_BYTES < KT_BYTES - kpad ? lane_off : OOB;
-      if constexpr (TAIL_FIRST) {
+      if constexpr (SCALAR_K) {
 #pragma unroll
         for (int i = 0; i < Sh::NQ; ++i) voff[i] = lane_off + (uint32_t)(i * row_step);
       }
@@ -373,17 +412,17 @@ struct RowDmaLoader {
   }
   template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void part0(uint8_t* tile, int i) const {
-    dma16s<NOPS>(rsrc, Sh::dst(tile, i), lane_off0, (uint32_t)(i * row_step));
+    dma16s<NOPS>(rsrc, Sh::dst(tile, i, wofs), lane_off0, (uint32_t)(i * row_step));
   }
   template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void part(uint8_t* tile, int kt, int i) const {
-    if constexpr (FAST && TAIL_FIRST) {
+    if constexpr (SCALAR_K) {
       // tiles past K (prefetched by the pipeline, never multiplied) read
-      // out of range: zeros, no memory traffic
-      dma16s<NOPS>(rsrc, Sh::dst(tile, i), voff[i], kt < nk ? (uint32_t)(kt * KT_BYTES - kpad) : OOB);
+      // out of range: zeros, no memory traffic (kpad = 0 without a tail)
+      dma16s<NOPS>(rsrc, Sh::dst(tile, i, wofs), voff[i], kt < nk ? (uint32_t)(kt * KT_BYTES - kpad) : OOB);
     } else if (FAST) {
       const bool kin = kt * KT_BYTES + Sh::lane_chunk() * CHUNK_BYTES < K * EB;
-      dma16<NOPS>(rsrc, Sh::dst(tile, i), kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
+      dma16<NOPS>(rsrc, Sh::dst(tile, i, wofs), kin ? lane_off + (uint32_t)(i * row_step + kt * KT_BYTES) : OOB);
     } else {
       constexpr int EPC = CHUNK_BYTES / EB;
       const int c = threadIdx.x & 7;  // thread t: chunk t%8 of rows t/8 + (NT/8)*j
@@ -447,8 +486,11 @@ struct Im2colLoader {
     return (long long)pixel * C + c;
   }
 
+  uint32_t wofs;  // this wave's offset in a tile's LDS rows
+
   __device__ __forceinline__ void init(const Params& p, int m0, int kt0) {
     x = p.A;
+    wofs = Sh::wave_offset();
     H = p.H; W = p.W; C = p.C; S = p.S; K = p.K;
     blk = BLK_OK ? p.blk : 0;
     padv = (uint8_t)(p.zAp + 128);
@@ -544,7 +586,7 @@ struct Im2colLoader {
       const bool ok = kin && (unsigned)h < (unsigned)H && (unsigned)w < (unsigned)W;
       // (a chunk's 8 channels lie in one 16-channel block: cur_c % 8 == 0)
       const uint32_t off = (uint32_t)elem_index(j, pix[j] + tap, cur_c) * 2u;
-      dma16<NOPS>(rsrc, Sh::dst(tile, j), ok ? off : OOB);
+      dma16<NOPS>(rsrc, Sh::dst(tile, j, wofs), ok ? off : OOB);
     } else if constexpr (EB == 2) {
       const int c = threadIdx.x & 7;
       const int k0 = kt * 64 + c * 8;
@@ -582,8 +624,11 @@ struct Im2colLoader {
 // buffer descriptor's base instead (scalar arithmetic), and each row keeps a
 // bit mask of the taps that fall inside the image (the zero padding), so a
 // load costs three vector instructions: the mask bit, a compare and a select
-// of the out-of-range offset.  Padded chunks land as zero bytes; for u8
-// activations fix_pad() then overwrites them with the zero point zA.
+// of the out-of-range offset.  Padded chunks land as zero bytes.  For u8
+// activations with a zero point zA != 0 the padding must hold zA: there the
+// padded lanes take no part in the load and store zA into their own LDS
+// slots at once (the stage is free when its loads are issued, and no load
+// writes those slots), so the tile is complete when its loads land.
 template <int NT, int ROWS, int EB = 2>
 struct Im2colC64Loader {
   typedef DmaShape<NT, ROWS> Sh;
@@ -595,19 +640,24 @@ struct Im2colC64Loader {
   int p0;               // ph*W + pw: keeps the per-row offsets non-negative
   uint32_t pixb[Sh::NQ];  // (pixel of tap (0,0) + p0) * C * EB + chunk * 16
   uint32_t mask[Sh::NQ];  // bit r*S+s: tap (r, s) of this row is inside the image
+  mutable uint32_t vo[Sh::NQ];  // pixb, or OOB where the current tap is padding
+  mutable int vo_tap;           // the tap vo[] was formed for
   mutable int cur_r, cur_s, cur_c;  // tap and channel of the next K tile
-  mutable int fix_tap, fix_c;       // tap and channel of the next tile fix_pad() visits
   uint32_t padv4;                   // zA in every byte
+  bool padz;                        // u8 with zA != 0: padded chunks stored as zA
   // blocked NHWCnc input (fp16 only): every pixel and channel offset is 16
   // times its NHWC value (16 images interleaved), plus the row's image within
   // its group of 16 and the chunk's place in a 16-channel block
   int blk_shift;                    // 4 blocked, 0 NHWC
+  uint32_t wofs;                    // this wave's offset in a tile's LDS rows
 
   __device__ __forceinline__ void init(const Params& p, int m0, int kt0) {
     x = p.A;
+    wofs = Sh::wave_offset();
     C = p.C; S = p.S; W = p.W; RS = p.R * p.S;
     bytes = (uint32_t)((long long)p.Nb * p.H * p.W * p.C * EB);
     padv4 = (uint32_t)(uint8_t)(p.zAp + 128) * 0x01010101u;
+    padz = EB == 1 && p.zAp != -128;
     p0 = p.ph * p.W + p.pw;
     blk_shift = (EB == 2 && p.blk) ? 4 : 0;
     const int PQ = p.P * p.Q;
@@ -643,8 +693,7 @@ struct Im2colC64Loader {
     cur_c = k - rs * C;
     cur_r = rs / S;
     cur_s = rs - cur_r * S;
-    fix_tap = rs;
-    fix_c = cur_c;
+    vo_tap = -1;
   }
   __device__ __forceinline__ void advance() const {
     cur_c += CPT;
@@ -656,6 +705,17 @@ struct Im2colC64Loader {
       }
     }
   }
+  // the per-row offsets of the current tap, formed once per tap (a tap
+  // spans C / CPT K tiles) instead of once per load
+  __device__ __forceinline__ void retap(int tap) const {
+    if (tap != vo_tap) {
+      // tiles past the last tap (prefetch beyond K) use bit 31, never set
+      const int bit = tap < RS ? tap : 31;
+#pragma unroll
+      for (int j = 0; j < Sh::NQ; ++j) vo[j] = ((mask[j] >> bit) & 1u) ? pixb[j] : OOB;
+      vo_tap = tap;
+    }
+  }
   template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void load(uint8_t* tile, int kt) const {
 #pragma unroll
@@ -665,8 +725,7 @@ struct Im2colC64Loader {
   template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void part(uint8_t* tile, int, int j) const {
     const int tap = cur_r * S + cur_s;
-    // tiles past the last tap (prefetch beyond K) use bit 31, never set
-    const int bit = tap < RS ? tap : 31;
+    retap(tap);
     const long long toff = (((long long)(cur_r * W + cur_s - p0) * C + cur_c) * EB) << blk_shift;
     const uint64_t base = (uint64_t)(uintptr_t)x + (uint64_t)toff;
     // bytes of x past the moved base, at most 2^31 so that OOB stays out of
@@ -675,25 +734,16 @@ struct Im2colC64Loader {
     const uint32_t num = left <= 0 ? 0u : left >= (long long)OOB ? OOB : (uint32_t)left;
     Rsrc r;
     r.d = i32x4{(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)num, 0x00020000};
-    const uint32_t vo = ((mask[j] >> bit) & 1u) ? pixb[j] : OOB;
-    dma16s<NOPS>(r, Sh::dst(tile, j), vo, 0);
-  }
-  // After this lane's loads of the next K tile (in order, one call per tile)
-  // have landed in `tile`: its padded chunks get zA.  Each lane rewrites only
-  // the LDS slots its own direct-to-LDS loads filled.  Tiles past the last
-  // tap (prefetched, never multiplied) are left alone.
-  __device__ __forceinline__ void fix_pad(uint8_t* tile) const {
-    if (fix_tap < RS) {
-      const uint4 zv = make_uint4(padv4, padv4, padv4, padv4);
-#pragma unroll
-      for (int j = 0; j < NPART; ++j)
-        if (!((mask[j] >> fix_tap) & 1u)) lds_write16(Sh::dst(tile, j), (threadIdx.x & 63) * CHUNK_BYTES, zv);
+    if constexpr (EB == 1) {
+      if (padz) {
+        // (tiles past the last tap, prefetched and never multiplied, get
+        // zA everywhere)
+        dma16s_or_fill<NOPS>(r, Sh::dst(tile, j, wofs), pixb[j], 0, __builtin_amdgcn_ballot_w64(vo[j] != OOB),
+                             make_uint4(padv4, padv4, padv4, padv4));
+        return;
+      }
     }
-    fix_c += CPT;
-    if (fix_c == C) {
-      fix_c = 0;
-      ++fix_tap;
-    }
+    dma16s<NOPS>(r, Sh::dst(tile, j, wofs), vo[j], 0);
   }
 };
 
@@ -804,16 +854,19 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr bool SK = INT8 ? (BM <= 128 && FAST) : (SUMS == 0);
   // (the im2col operand walks K in order, so the conv's B does too)
   constexpr bool CONV = KIND == KIND_F16_CONV || KIND == KIND_F16_CONV_C64 || KIND == KIND_U8I8_CONV;
-  // u8 activations through the uniform-tap loader: padded chunks land as
-  // zeros and are rewritten with zA before the barrier that publishes a tile
-  constexpr bool PADFIX = KIND == KIND_U8I8_CONV && FAST;
+  // u8 activations through the uniform-tap loader (padding stored as zA by
+  // the loader itself)
+  constexpr bool U8_UNIFORM_TAPS = KIND == KIND_U8I8_CONV && FAST;
   constexpr bool TAIL_FIRST = FAST && !CONV;
   typedef typename std::conditional<
-      KIND == KIND_F16_CONV_C64 || PADFIX, Im2colC64Loader<NT, BM, EB>,
+      KIND == KIND_F16_CONV_C64 || U8_UNIFORM_TAPS, Im2colC64Loader<NT, BM, EB>,
       typename std::conditional<KIND == KIND_F16_CONV || KIND == KIND_U8I8_CONV, Im2colLoader<NT, BM, FAST, EB>,
                                 RowDmaLoader<NT, BM, EB, FAST, TAIL_FIRST>>::type>::type ALoader;
   static_assert(KIND != KIND_F16_CONV_C64 || FAST, "the uniform-tap conv loader needs aligned operands");
-  typedef RowDmaLoader<NT, BN, EB, FAST, TAIL_FIRST> BLoader;
+  // the uniform-tap convolutions walk K in order with whole K tiles (C a
+  // multiple of the tile's channels)
+  constexpr bool WHOLE_K = KIND == KIND_F16_CONV_C64 || U8_UNIFORM_TAPS;
+  typedef RowDmaLoader<NT, BN, EB, FAST, TAIL_FIRST, WHOLE_K> BLoader;
   // direct-to-LDS loads per K tile per wave (counted by vmcnt); the
   // element-wise path of unaligned operands is waited for as it goes
   constexpr int NLA = FAST ? ALoader::NPART : 0;
@@ -1026,14 +1079,6 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     lb.template load<NOPS_SAFE>(stB(D), k0 + decltype(D)::value);
   });
   wait_vmcnt_lgkm0<(DEPTH - 1) * (NLA + NLB)>();
-  // (zA = 0: the zeros of the out-of-range loads already are the zero point)
-  const bool padfix = PADFIX && p.zAp != -128;
-  if constexpr (PADFIX) {
-    if (padfix) {
-      la.fix_pad(stA(std::integral_constant<int, 0>()));
-      wait_vmcnt_lgkm0<(DEPTH - 1) * (NLA + NLB)>();
-    }
-  }
   lds_barrier();
 #pragma unroll
   for (int i = 0; i < FM; ++i) read_a(sa0, 0, i, fa[0][i]);
@@ -1083,12 +1128,6 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     la.advance();
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt_lgkm0<(DEPTH - 2) * (NLA + NLB) + NLA>();
-    if constexpr (PADFIX) {
-      if (padfix) {
-        la.fix_pad(stA(std::integral_constant<int, u + 1>()));
-        wait_vmcnt_lgkm0<(DEPTH - 2) * (NLA + NLB) + NLA>();
-      }
-    }
     lds_barrier();
     const uint8_t* As1 = stA(std::integral_constant<int, u + 1>());
     const uint8_t* Bs1 = stB(std::integral_constant<int, u + 1>());
