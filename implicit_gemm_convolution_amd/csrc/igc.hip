@@ -116,6 +116,10 @@ int conv_params(int Nb, int H, int W, int C, int Kout, int R, int S, int stride_
   p.Nb = Nb; p.H = H; p.W = W; p.C = C; p.R = R; p.S = S;
   p.sh = stride_h; p.sw = stride_w; p.ph = pad_h; p.pw = pad_w;
   p.P = (int)P; p.Q = (int)Q;
+  p.fd_pq = make_fastdiv(P * Q);
+  p.fd_q = make_fastdiv(Q);
+  p.fd_c = make_fastdiv(C);
+  p.fd_s = make_fastdiv(S);
   *nx_out = nx;
   return IGC_OK;
 }

@@ -162,11 +162,21 @@ inline Plan make_plan(int kind, int M, int N, int K, bool fast, int cus, bool ws
   return pl;
 }
 
+// The reciprocal of d for igc::FastDiv (1 <= d < 2^31).
+inline igc::FastDiv make_fastdiv(long long d) {
+  igc::FastDiv f;
+  f.d = (uint32_t)d;
+  f.m = d <= 1 ? 0u : (uint32_t)((1ULL << 32) / (unsigned long long)d + 1);
+  return f;
+}
+
 // Fills the split and workspace fields of p from the plan; ws is the
 // caller's workspace (used only when the plan needs one).
 inline void apply_plan(igc::Params& p, const Plan& pl, void* ws) {
   p.tiles_m = pl.tiles_m;
   p.tiles_n = pl.tiles_n;
+  p.fd_group = make_fastdiv(8LL * pl.tiles_n);
+  p.fd_glast = make_fastdiv(pl.tiles_m % 8 ? pl.tiles_m % 8 : 8);
   p.dp_tiles = pl.dp_tiles;
   p.xcd_regroup = pl.xcd_regroup;
   p.sk_wgs = pl.sk_wgs;

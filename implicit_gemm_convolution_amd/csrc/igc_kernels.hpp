@@ -92,6 +92,19 @@ constexpr int KT_BYTES = 128;    // bytes of K per tile row
 constexpr int CHUNK_BYTES = 16;  // one vector load
 constexpr int CPR = KT_BYTES / CHUNK_BYTES;  // chunks per tile row
 
+// n / d for 0 <= n < 2^31 and 1 <= d < 2^31 with a reciprocal formed on the
+// host: m = floor(2^32 / d) + 1 (0 for d = 1).  umulhi(n, m) is n / d or one
+// more; one compare corrects it.  A runtime division costs a few dozen
+// instructions on the GPU, and the tile and im2col set-up of every workgroup
+// needs several.
+struct FastDiv {
+  uint32_t d, m;
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    const uint32_t q = __umulhi(n, m);
+    return m == 0 ? n : q - (q * d > n ? 1u : 0u);
+  }
+};
+
 struct Params {
   // GEMM view: M x N output, K reduction.
   int M, N, K;
@@ -102,6 +115,7 @@ struct Params {
   long long ldb;     // elements
   // implicit im2col view of an NHWC input
   int Nb, H, W, C, R, S, sh, sw, ph, pw, P, Q;
+  FastDiv fd_pq, fd_q, fd_c, fd_s;  // divisions by P*Q, Q, C and S
   // blocked NHWCnc layout (block 16) of the conv input and output: GEMM row
   // m = ((n/16 * P + p) * Q + q) * 16 + n % 16; x[n/16][h][w][c/16][n%16][c%16],
   // y[n/16][p][q][k/16][n%16][k%16]
@@ -132,6 +146,7 @@ struct Params {
   // counted in cnt (one counter per stream-K tile, zero between launches).
   int dp_tiles;
   int xcd_regroup;  // regroup whole tiles by XCD (see dp_tile)
+  FastDiv fd_group, fd_glast;  // tile_coords: by 8 * tiles_n, and by the last group's tile rows
   int sk_wgs;
   long long sk_iters;
   float* ws;
@@ -163,13 +178,18 @@ __device__ __forceinline__ int sk_owner(const Params& p, long long x) {
 // ---------------------------------------------------------------------------
 template <int GROUP_M>
 __device__ __forceinline__ void tile_coords(const Params& p, int t, int& tm, int& tn) {
-  const int per_group = GROUP_M * p.tiles_n;
-  const int group = t / per_group;
+  static_assert(GROUP_M == 8, "the host forms the reciprocals for groups of 8 tile rows");
+  const int group = (int)p.fd_group.div((uint32_t)t);  // t / (GROUP_M * tiles_n)
   const int first_m = group * GROUP_M;
-  const int gsize = min(p.tiles_m - first_m, GROUP_M);
-  const int in_group = t - group * per_group;
-  tm = first_m + in_group % gsize;
-  tn = in_group / gsize;
+  const int in_group = t - group * GROUP_M * p.tiles_n;
+  if (p.tiles_m - first_m >= GROUP_M) {
+    tm = first_m + (in_group & (GROUP_M - 1));
+    tn = in_group / GROUP_M;
+  } else {  // the last, partial group of tile rows
+    const int q = (int)p.fd_glast.div((uint32_t)in_group);
+    tm = first_m + in_group - q * (p.tiles_m - first_m);
+    tn = q;
+  }
 }
 // logical tile of whole-tile workgroup b
 // (the regrouping is applied when the grid takes several rounds of compute
@@ -466,6 +486,7 @@ struct Im2colLoader {
   int pix[NR];  // pixel index in x of (n, p*sh - ph, q*sw - pw), i.e. of tap (0, 0)
   int hw[NR];   // (p*sh - ph) << 16 | (q*sw - pw) & 0xffff; INT32_MIN for rows past M
   int H, W, C, S, K;
+  FastDiv fd_c, fd_s;
   uint8_t padv;  // u8 padding value (zA)
   Rsrc rsrc;
   // tap of this lane's chunk for the next K tile to be loaded (FAST)
@@ -508,9 +529,9 @@ struct Im2colLoader {
         if constexpr (BLK_OK) {
           if (blk) nnoff[j] = (m & 15) << 4;
         }
-        const int n = g / PQ;
+        const int n = (int)p.fd_pq.div((uint32_t)g);
         const int pq = g - n * PQ;
-        const int pp = pq / p.Q;
+        const int pp = (int)p.fd_q.div((uint32_t)pq);
         const int qq = pq - pp * p.Q;
         const int h0 = pp * p.sh - p.ph;
         const int w0 = qq * p.sw - p.pw;
@@ -523,17 +544,19 @@ struct Im2colLoader {
     }
     // tap of k = chunk*8 of K tile kt0
     const int k0 = FAST ? kt0 * 64 + Sh::lane_chunk() * 8 : 0;
-    const int rs = k0 / C;
+    const int rs = (int)p.fd_c.div((uint32_t)k0);
     cur_c = k0 - rs * C;
-    cur_r = rs / S;
+    cur_r = (int)p.fd_s.div((uint32_t)rs);
     cur_s = rs - cur_r * S;
+    fd_c = p.fd_c;
+    fd_s = p.fd_s;
   }
 
   __device__ __forceinline__ uint16_t elem(int j, int k) const {
     if (hw[j] == INT32_MIN || k >= K) return 0;
-    const int rs = k / C;
+    const int rs = (int)fd_c.div((uint32_t)k);
     const int c = k - rs * C;
-    const int r = rs / S;
+    const int r = (int)fd_s.div((uint32_t)rs);
     const int s = rs - r * S;
     const int h = row_h(j) + r;
     const int w = row_w(j) + s;
@@ -543,9 +566,9 @@ struct Im2colLoader {
   // u8: past K (and rows past M) 0, like the row operands' K tail; padding zA
   __device__ __forceinline__ uint8_t elem8(int j, int k) const {
     if (hw[j] == INT32_MIN || k >= K) return 0;
-    const int rs = k / C;
+    const int rs = (int)fd_c.div((uint32_t)k);
     const int c = k - rs * C;
-    const int r = rs / S;
+    const int r = (int)fd_s.div((uint32_t)rs);
     const int s = rs - r * S;
     const int h = row_h(j) + r;
     const int w = row_w(j) + s;
@@ -661,6 +684,9 @@ struct Im2colC64Loader {
     p0 = p.ph * p.W + p.pw;
     blk_shift = (EB == 2 && p.blk) ? 4 : 0;
     const int PQ = p.P * p.Q;
+    // one bit at r*S for every filter row r
+    uint32_t rep = 0;
+    for (int r = 0; r < p.R; ++r) rep |= 1u << (r * p.S);
     // chunk c of a 128-byte K-tile row (channels 8c .. 8c+7 of the tile):
     // byte 16c (NHWC), or 512 (c / 2) + 16 (c % 2) in the blocked layout
     const int ch = Sh::lane_chunk();
@@ -672,26 +698,31 @@ struct Im2colC64Loader {
       mask[j] = 0;
       if (m < p.M) {
         const int g = blk_shift ? (m >> 4) : m;
-        const int n = g / PQ;
+        const int n = (int)p.fd_pq.div((uint32_t)g);
         const int pq = g - n * PQ;
-        const int pp = pq / p.Q;
+        const int pp = (int)p.fd_q.div((uint32_t)pq);
         const int qq = pq - pp * p.Q;
         const int h0 = pp * p.sh - p.ph;
         const int w0 = qq * p.sw - p.pw;
         const uint32_t nn_off = blk_shift ? (uint32_t)((m & 15) * 16 * EB) : 0u;
         pixb[j] = ((uint32_t)((n * p.H * p.W + h0 * p.W + w0 + p0) * C * EB) << blk_shift) + nn_off + chunk_off;
-        uint32_t mk = 0;
-        for (int r = 0; r < p.R; ++r)
-          for (int s2 = 0; s2 < p.S; ++s2)
-            if ((unsigned)(h0 + r) < (unsigned)p.H && (unsigned)(w0 + s2) < (unsigned)p.W)
-              mk |= 1u << (r * p.S + s2);
-        mask[j] = mk;
+        // taps (r, s) inside the image: r in [r_lo, r_hi], s in [s_lo, s_hi];
+        // bit r*S + s of the mask is the product of a column run (bits s_lo
+        // .. s_hi) and one bit at r*S per row of the row run (no carries:
+        // R*S <= 31)
+        const int r_lo = max(0, -h0), r_hi = min(p.R - 1, p.H - 1 - h0);
+        const int s_lo = max(0, -w0), s_hi = min(p.S - 1, p.W - 1 - w0);
+        // (shift counts clamped to 31: a window wholly in the padding has
+        // r_lo > r_hi or s_lo > s_hi, and its mask is 0)
+        const uint32_t cols = (2u << min(max(s_hi, 0), 30)) - (1u << min(s_lo, 31));
+        const uint32_t rows = rep & ((2u << min(max(r_hi, 0) * p.S, 30)) - (1u << min(r_lo * p.S, 31)));
+        mask[j] = (r_lo <= r_hi && s_lo <= s_hi) ? rows * cols : 0u;
       }
     }
     const int k = kt0 * CPT;
-    const int rs = k / C;
+    const int rs = (int)p.fd_c.div((uint32_t)k);
     cur_c = k - rs * C;
-    cur_r = rs / S;
+    cur_r = (int)p.fd_s.div((uint32_t)rs);
     cur_s = rs - cur_r * S;
     vo_tap = -1;
   }
@@ -900,8 +931,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // that may start and end inside tiles.  It is walked in segments of one
   // tile each.
   long long it, it_end;
-  if ((int)blockIdx.x < p.dp_tiles) {
-    it = (long long)dp_tile(p, blockIdx.x) * nk;
+  const bool whole = (int)blockIdx.x < p.dp_tiles;
+  const int t_whole = whole ? dp_tile(p, blockIdx.x) : 0;
+  if (whole) {
+    it = (long long)t_whole * nk;
     it_end = it + nk;
   } else {
     const int g = blockIdx.x - p.dp_tiles;
@@ -923,8 +956,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   const int lane = tid & 63;
   const int wave = wave_s;
   const int wm = wave / WN, wn = wave % WN;
-  const int t = (int)(it / nk);
-  const int k0 = (int)(it - (long long)t * nk);
+  // (a whole-tile workgroup's one segment is its tile; no division)
+  const int t = (!SK || whole) ? t_whole : (int)(it / nk);
+  const int k0 = (!SK || whole) ? 0 : (int)(it - (long long)t * nk);
   const int k1 = (int)min((long long)nk, (long long)k0 + (it_end - it));
   int tm, tn;
   tile_coords<8>(p, t, tm, tn);

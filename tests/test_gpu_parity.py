@@ -324,6 +324,7 @@ def run_conv(igc, x, w, stride, pad):
 
 CONV_CASES = [
     # Nb, H, W, C, Kout, R, S, stride, pad
+    (4, 3, 3, 64, 24, 3, 3, (1, 1), (0, 0)),      # 1x1 output: P*Q = Q = 1
     (1, 14, 14, 256, 512, 3, 3, (1, 1), (1, 1)),   # one image of the 256-batch workload
     (2, 9, 11, 64, 96, 3, 3, (1, 1), (1, 1)),
     (3, 8, 8, 16, 24, 1, 1, (1, 1), (0, 0)),
@@ -483,6 +484,7 @@ def run_qconv(igc, x, zA, w, zB, stride, pad, outputs=("C",), scale=None, bias=N
 
 QCONV_CASES = [
     # Nb, H, W, C, Kout, R, S, stride, pad, zA, zB
+    (4, 3, 3, 128, 24, 3, 3, (1, 1), (0, 0), 61, 2),  # 1x1 output: P*Q = Q = 1
     (1, 14, 14, 256, 512, 3, 3, (1, 1), (1, 1), 100, 0),    # one image of the 256-batch shape
     (2, 9, 11, 128, 96, 3, 3, (1, 1), (1, 1), 128, 3),      # uniform taps, zA' = 0
     (2, 13, 10, 128, 40, 5, 5, (2, 2), (2, 2), 37, -5),
@@ -510,7 +512,7 @@ def test_qconv_int32_bit_exact(igc, oracle, variant, case):
     assert np.array_equal(got["C"].astype(np.int64), ref)
 
 
-@pytest.mark.parametrize("case", [QCONV_CASES[0], QCONV_CASES[2], QCONV_CASES[5]])
+@pytest.mark.parametrize("case", [QCONV_CASES[0], QCONV_CASES[1], QCONV_CASES[3], QCONV_CASES[6]])
 def test_qconv_dequant_and_requant_bit_exact(igc, oracle, case):
     Nb, H, W, C, Kout, R, S, st, pd, zA, zB = case
     rng = np.random.default_rng(3 * sum(case[:7]) + zA)
@@ -530,7 +532,7 @@ def test_qconv_dequant_and_requant_bit_exact(igc, oracle, case):
 
 
 @pytest.mark.parametrize("variant", VARIANTS, indirect=True)
-@pytest.mark.parametrize("case", [QCONV_CASES[0], QCONV_CASES[2], QCONV_CASES[4]])
+@pytest.mark.parametrize("case", [QCONV_CASES[1], QCONV_CASES[3], QCONV_CASES[5]])
 def test_qconv_requant_only(igc, oracle, variant, case):
     Nb, H, W, C, Kout, R, S, st, pd, zA, zB = case
     rng = np.random.default_rng(7 * sum(case[:7]) + zA)
@@ -665,7 +667,7 @@ def test_u8i8_split_tiles_requant_only_and_deterministic(igc, oracle, v):
 
 
 @pytest.mark.parametrize("v", ["1", "2"])
-@pytest.mark.parametrize("case", [QCONV_CASES[1], QCONV_CASES[2], QCONV_CASES[3], QCONV_CASES[8]])
+@pytest.mark.parametrize("case", [QCONV_CASES[2], QCONV_CASES[3], QCONV_CASES[4], QCONV_CASES[9]])
 def test_qconv_split_tiles_bit_exact(igc, oracle, v, case):
     Nb, H, W, C, Kout, R, S, stride, pad, zA, zB = case
     igc.set_tuning(int(v), 2)
