@@ -308,7 +308,9 @@ __device__ __forceinline__ void dma16(const Rsrc& r, uint8_t* lds, uint32_t off)
 // execution mask is narrowed, complemented and restored inside the asm, so
 // the load is issued even when no lane is set and every explicit vmcnt count
 // in the kernel stays exact; the store counts on lgkmcnt, which the kernel
-// waits for in full before a tile is read.
+// waits for in full before a tile is read.  The scalar mask operations set
+// SCC, so the asm declares it clobbered: the compiler may otherwise keep a
+// comparison live in SCC across it.
 template <int NOPS>
 __device__ __forceinline__ void dma16s_or_fill(const Rsrc& r, uint8_t* lds, uint32_t off, uint32_t soff,
                                                uint64_t lanes, uint4 fill) {
@@ -321,12 +323,14 @@ __device__ __forceinline__ void dma16s_or_fill(const Rsrc& r, uint8_t* lds, uint
     asm volatile(
         "s_and_saveexec_b64 %0, %5\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
         "s_andn2_b64 exec, %0, %5\n\tds_write_b128 %6, %7\n\ts_mov_b64 exec, %0"
-        : "=&s"(saved) : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0), "s"(lanes), "v"(vaddr), "v"(fv) : "memory");
+        : "=&s"(saved) : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0), "s"(lanes), "v"(vaddr), "v"(fv)
+        : "memory", "scc");
   else
     asm volatile(
         "s_and_saveexec_b64 %0, %5\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
         "s_andn2_b64 exec, %0, %5\n\tds_write_b128 %6, %7\n\ts_mov_b64 exec, %0"
-        : "=&s"(saved) : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0), "s"(lanes), "v"(vaddr), "v"(fv) : "memory");
+        : "=&s"(saved) : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0), "s"(lanes), "v"(vaddr), "v"(fv)
+        : "memory", "scc");
 }
 
 // Direct-to-LDS tiles of ROWS rows x 128 bytes.  Wave-instruction q fills
@@ -648,10 +652,10 @@ struct Im2colLoader {
 // bit mask of the taps that fall inside the image (the zero padding), so a
 // load costs three vector instructions: the mask bit, a compare and a select
 // of the out-of-range offset.  Padded chunks land as zero bytes.  For u8
-// activations with a zero point zA != 0 the padding must hold zA: there the
-// padded lanes take no part in the load and store zA into their own LDS
-// slots at once (the stage is free when its loads are issued, and no load
-// writes those slots), so the tile is complete when its loads land.
+// activations the padding must hold the zero point zA: there the padded
+// lanes take no part in the load and store zA into their own LDS slots at
+// once (the stage is free when its loads are issued, and no load writes
+// those slots), so the tile is complete when its loads land.
 template <int NT, int ROWS, int EB = 2>
 struct Im2colC64Loader {
   typedef DmaShape<NT, ROWS> Sh;
@@ -667,7 +671,6 @@ struct Im2colC64Loader {
   mutable int vo_tap;           // the tap vo[] was formed for
   mutable int cur_r, cur_s, cur_c;  // tap and channel of the next K tile
   uint32_t padv4;                   // zA in every byte
-  bool padz;                        // u8 with zA != 0: padded chunks stored as zA
   // blocked NHWCnc input (fp16 only): every pixel and channel offset is 16
   // times its NHWC value (16 images interleaved), plus the row's image within
   // its group of 16 and the chunk's place in a 16-channel block
@@ -680,7 +683,6 @@ struct Im2colC64Loader {
     C = p.C; S = p.S; W = p.W; RS = p.R * p.S;
     bytes = (uint32_t)((long long)p.Nb * p.H * p.W * p.C * EB);
     padv4 = (uint32_t)(uint8_t)(p.zAp + 128) * 0x01010101u;
-    padz = EB == 1 && p.zAp != -128;
     p0 = p.ph * p.W + p.pw;
     blk_shift = (EB == 2 && p.blk) ? 4 : 0;
     const int PQ = p.P * p.Q;
@@ -766,15 +768,14 @@ struct Im2colC64Loader {
     Rsrc r;
     r.d = i32x4{(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)num, 0x00020000};
     if constexpr (EB == 1) {
-      if (padz) {
-        // (tiles past the last tap, prefetched and never multiplied, get
-        // zA everywhere)
-        dma16s_or_fill<NOPS>(r, Sh::dst(tile, j, wofs), pixb[j], 0, __builtin_amdgcn_ballot_w64(vo[j] != OOB),
-                             make_uint4(padv4, padv4, padv4, padv4));
-        return;
-      }
+      // (tiles past the last tap, prefetched and never multiplied, get zA
+      // everywhere; with zA = 0 the stores write the zeros an out-of-range
+      // load would)
+      dma16s_or_fill<NOPS>(r, Sh::dst(tile, j, wofs), pixb[j], 0, __builtin_amdgcn_ballot_w64(vo[j] != OOB),
+                           make_uint4(padv4, padv4, padv4, padv4));
+    } else {
+      dma16s<NOPS>(r, Sh::dst(tile, j, wofs), vo[j], 0);
     }
-    dma16s<NOPS>(r, Sh::dst(tile, j, wofs), vo[j], 0);
   }
 };
 

@@ -171,3 +171,44 @@ def test_direct_to_lds_loads_respect_sgpr_hazards(asm):
                 ws += int(prev.split()[1], 0) + 1 if op == "s_nop" else 1
                 j -= 1
     assert checked > 1000
+
+
+# Scalar ALU instructions that set SCC, and those that read it.
+_SCC_WRITE = re.compile(r"^s_(add|sub|addk|addc|subb|min|max|and|or|xor|andn2|orn2|nand|nor|xnor|lshl|lshr|ashr|bfe|"
+                        r"cmp|cmpk|bitcmp|not|abs|absdiff|bcnt|quadmask|wqm|lshl\d_add)\w*")
+_SCC_READ = re.compile(r"^s_(cselect|cbranch_scc|addc|subb|cmov|cmovk)\w*")
+
+
+def scc_reads_after_asm(body):
+    """Instructions that read SCC while its last writer was an inline-asm
+    block (an SCC clobber the asm did not declare), in program order."""
+    bad, in_asm, asm_writes, scc_from_asm = [], False, False, False
+    for line in body.splitlines():
+        t = line.split(";")[0].strip()
+        if ";;#ASMSTART" in line:
+            in_asm, asm_writes = True, False
+            continue
+        if ";;#ASMEND" in line:
+            in_asm = False
+            scc_from_asm = scc_from_asm or asm_writes
+            continue
+        if not t or t.startswith("."):
+            if t.startswith(".LBB"):
+                scc_from_asm = False  # a join: other paths reach it
+            continue
+        op = t.split()[0]
+        if in_asm:
+            asm_writes = asm_writes or bool(_SCC_WRITE.match(op))
+            continue
+        if _SCC_READ.match(op) and scc_from_asm:
+            bad.append(t)
+        if _SCC_WRITE.match(op):
+            scc_from_asm = False
+    return bad
+
+
+def test_no_scc_read_across_asm(asm):
+    """The inline-asm blocks that set SCC declare it clobbered, so no
+    compiled comparison is kept in SCC across one."""
+    for name, (body, _) in asm.items():
+        assert not scc_reads_after_asm(body), (name, scc_reads_after_asm(body)[:4])
