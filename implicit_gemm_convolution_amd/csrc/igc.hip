@@ -265,6 +265,18 @@ int query_workspace(int kind, int M, int N, int K, size_t* bytes) {
 
 using namespace igc_host;
 
+// The uniform-tap conv loaders address x through a 2^31-byte buffer whose
+// base is x moved back by the padding's offset ((ph*W + pw) pixels), with
+// the K tile's tap and channel position as a scalar offset: x plus the
+// padding's offset, and the largest scalar offset (a filter row past the
+// last, for the tiles prefetched beyond K), must both stay below 2^31 bytes.
+static bool uniform_taps_fit(const igc::Params& p, long long x_bytes, int eb, bool blocked) {
+  const long long sc = (long long)eb * (blocked ? 16 : 1);
+  const long long pad_off = ((long long)p.ph * p.W + p.pw) * p.C * sc;
+  const long long max_off = ((long long)(p.R + 1) * p.W + p.S) * p.C * sc;
+  return x_bytes + pad_off < (1LL << 31) && max_off < (1LL << 31);
+}
+
 extern "C" {
 
 const char* igc_status_string(int status) {
@@ -420,7 +432,7 @@ int conv2d_u8i8_zp(int Nb, int H, int W, int C, int Kout, int R, int S, int stri
   epilogue_params(p, ep);
   // whole 128-channel K tiles within one tap: the uniform-tap loader
   const bool fast = aligned16(x) && aligned16(w) && C % 128 == 0 && (long long)R * S <= 31 &&
-                    nx < (1LL << 31) && 256LL * p.K < (1LL << 31);
+                    nx < (1LL << 31) && 256LL * p.K < (1LL << 31) && uniform_taps_fit(p, nx, 1, false);
   return launch_u8i8<igc::KIND_U8I8_CONV>(p, fast, ep->workspace, ep->ws_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -449,7 +461,7 @@ int conv2d_implicit_gemm(int Nb, int H, int W, int C, int Kout, int R, int S, in
                     256LL * p.K * 2 < (1LL << 31);
   hipStream_t st = static_cast<hipStream_t>(stream);
   // whole 64-channel K tiles within one tap: the uniform-tap loader
-  if (fast && C % 64 == 0 && (long long)R * S <= 31)
+  if (fast && C % 64 == 0 && (long long)R * S <= 31 && uniform_taps_fit(p, nx * 2, 2, false))
     return plan_and_launch<igc::KIND_F16_CONV_C64, 0>(p, true, workspace, ws_bytes, st);
   return plan_and_launch<igc::KIND_F16_CONV, 0>(p, fast, workspace, ws_bytes, st);
 }
@@ -487,7 +499,8 @@ int conv2d_implicit_gemm_nhwcnc(int Nb, int H, int W, int C, int Kout, int R, in
   p.blk = 1;
   p.vec_c = aligned16(y);
   const bool fast = aligned16(x) && nx * 2 < (1LL << 31) && 256LL * p.K * 2 < (1LL << 31);
-  const int kind = (fast && C % 64 == 0 && (long long)R * S <= 31) ? igc::KIND_F16_CONV_C64 : igc::KIND_F16_CONV;
+  const int kind = (fast && C % 64 == 0 && (long long)R * S <= 31 && uniform_taps_fit(p, nx * 2, 2, true))
+                       ? igc::KIND_F16_CONV_C64 : igc::KIND_F16_CONV;
   const Plan pl = make_plan(kind, p.M, p.N, p.K, fast, device_cus(dev), true);
   const size_t woff = nhwcnc_ws_offset(pl.ws_bytes), wbytes = nhwcnc_weight_bytes(p);
   if (ws_bytes < woff + wbytes)

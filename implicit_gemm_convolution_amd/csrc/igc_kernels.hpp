@@ -647,44 +647,51 @@ struct Im2colLoader {
 // The implicit-im2col A operand when a K tile (128 bytes: 64 fp16 or 128 u8
 // channels) always lies in one tap: C a multiple of it and R*S <= 31 (FAST
 // only).  The tap (r, s) is then the same for all lanes, so the tap walk is
-// scalar.  A row's input pixel is a fixed per-lane offset; the tap moves the
-// buffer descriptor's base instead (scalar arithmetic), and each row keeps a
-// bit mask of the taps that fall inside the image (the zero padding), so a
-// load costs three vector instructions: the mask bit, a compare and a select
-// of the out-of-range offset.  Padded chunks land as zero bytes.  For u8
-// activations the padding must hold the zero point zA: there the padded
-// lanes take no part in the load and store zA into their own LDS slots at
-// once (the stage is free when its loads are issued, and no load writes
-// those slots), so the tile is complete when its loads land.
+// scalar.  A row's input pixel is a fixed per-lane offset from a fixed
+// buffer base (x moved back by the padding's offset, so every offset is
+// non-negative); the K tile's position, ((r*W + s)*C + c) elements, is the
+// load's scalar offset.  In NHWC that position grows by 128 bytes per K tile
+// (tap (r, s+1) channel 0 follows tap (r, s) channel C-1 in memory), plus
+// (W - S)*C elements when the walk moves to the next filter row, so a K tile
+// costs a few scalar additions.  Each row keeps a bit mask of the taps that
+// fall inside the image (the zero padding); once per tap the per-lane offset
+// becomes OOB where the tap is padding, so that lane's load reads zeros.
+// The buffer spans 2^31 bytes (OOB): valid offsets stay below it (the host
+// checks that x plus the padding's offset, and the largest scalar offset, fit
+// in 2^31 bytes).  For u8 activations the padding must hold the zero point
+// zA: there the padded lanes take no part in the load and store zA into their
+// own LDS slots at once (the stage is free when its loads are issued, and no
+// load writes those slots), so the tile is complete when its loads land.
 template <int NT, int ROWS, int EB = 2>
 struct Im2colC64Loader {
   typedef DmaShape<NT, ROWS> Sh;
   static constexpr int NPART = Sh::NQ;
   static constexpr int CPT = KT_BYTES / EB;  // channels per K tile
-  const uint8_t* x;
-  uint32_t bytes;       // size of x
-  int C, S, W, RS;
-  int p0;               // ph*W + pw: keeps the per-row offsets non-negative
-  uint32_t pixb[Sh::NQ];  // (pixel of tap (0,0) + p0) * C * EB + chunk * 16
+  Rsrc rsrc;            // x moved back by the padding's offset, 2^31 bytes
+  int C, S, RS;
+  uint32_t pixb[Sh::NQ];  // (pixel of tap (0,0) + ph*W + pw) * C * EB + chunk * 16
   uint32_t mask[Sh::NQ];  // bit r*S+s: tap (r, s) of this row is inside the image
   mutable uint32_t vo[Sh::NQ];  // pixb, or OOB where the current tap is padding
   mutable int vo_tap;           // the tap vo[] was formed for
-  mutable int cur_r, cur_s, cur_c;  // tap and channel of the next K tile
-  uint32_t padv4;                   // zA in every byte
+  mutable int cur_tap, cur_s, cur_c;  // tap r*S + s, s and channel of the next K tile
+  mutable uint32_t soff;        // scalar offset of the next K tile: ((r*W + s)*C + c)*EB
+  uint32_t step, row_jump;      // soff per K tile; extra soff when s wraps
+  uint32_t padv4;               // zA in every byte
   // blocked NHWCnc input (fp16 only): every pixel and channel offset is 16
   // times its NHWC value (16 images interleaved), plus the row's image within
   // its group of 16 and the chunk's place in a 16-channel block
-  int blk_shift;                    // 4 blocked, 0 NHWC
-  uint32_t wofs;                    // this wave's offset in a tile's LDS rows
+  int blk_shift;                // 4 blocked, 0 NHWC
+  uint32_t wofs;                // this wave's offset in a tile's LDS rows
 
   __device__ __forceinline__ void init(const Params& p, int m0, int kt0) {
-    x = p.A;
     wofs = Sh::wave_offset();
-    C = p.C; S = p.S; W = p.W; RS = p.R * p.S;
-    bytes = (uint32_t)((long long)p.Nb * p.H * p.W * p.C * EB);
+    C = p.C; S = p.S; RS = p.R * p.S;
     padv4 = (uint32_t)(uint8_t)(p.zAp + 128) * 0x01010101u;
-    p0 = p.ph * p.W + p.pw;
+    const int p0 = p.ph * p.W + p.pw;
     blk_shift = (EB == 2 && p.blk) ? 4 : 0;
+    rsrc = make_rsrc((const void*)((uintptr_t)p.A - ((uintptr_t)p0 * C * EB << blk_shift)), OOB);
+    step = (uint32_t)(KT_BYTES << blk_shift);
+    row_jump = (uint32_t)(((long long)(p.W - S) * C * EB) << blk_shift);
     const int PQ = p.P * p.Q;
     // one bit at r*S for every filter row r
     uint32_t rep = 0;
@@ -724,17 +731,21 @@ struct Im2colC64Loader {
     const int k = kt0 * CPT;
     const int rs = (int)p.fd_c.div((uint32_t)k);
     cur_c = k - rs * C;
-    cur_r = (int)p.fd_s.div((uint32_t)rs);
-    cur_s = rs - cur_r * S;
+    cur_tap = rs;
+    const int r = (int)p.fd_s.div((uint32_t)rs);
+    cur_s = rs - r * S;
+    soff = (uint32_t)((((long long)(r * p.W + cur_s) * C + cur_c) * EB) << blk_shift);
     vo_tap = -1;
   }
   __device__ __forceinline__ void advance() const {
     cur_c += CPT;
+    soff += step;
     if (cur_c == C) {
       cur_c = 0;
+      ++cur_tap;
       if (++cur_s == S) {
         cur_s = 0;
-        ++cur_r;
+        soff += row_jump;
       }
     }
   }
@@ -757,24 +768,15 @@ struct Im2colC64Loader {
   }
   template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void part(uint8_t* tile, int, int j) const {
-    const int tap = cur_r * S + cur_s;
-    retap(tap);
-    const long long toff = (((long long)(cur_r * W + cur_s - p0) * C + cur_c) * EB) << blk_shift;
-    const uint64_t base = (uint64_t)(uintptr_t)x + (uint64_t)toff;
-    // bytes of x past the moved base, at most 2^31 so that OOB stays out of
-    // range (0 once the tap has left x: every lane then reads zeros)
-    const long long left = (long long)bytes - toff;
-    const uint32_t num = left <= 0 ? 0u : left >= (long long)OOB ? OOB : (uint32_t)left;
-    Rsrc r;
-    r.d = i32x4{(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)num, 0x00020000};
+    retap(cur_tap);
     if constexpr (EB == 1) {
       // (tiles past the last tap, prefetched and never multiplied, get zA
       // everywhere; with zA = 0 the stores write the zeros an out-of-range
       // load would)
-      dma16s_or_fill<NOPS>(r, Sh::dst(tile, j, wofs), pixb[j], 0, __builtin_amdgcn_ballot_w64(vo[j] != OOB),
+      dma16s_or_fill<NOPS>(rsrc, Sh::dst(tile, j, wofs), pixb[j], soff, __builtin_amdgcn_ballot_w64(vo[j] != OOB),
                            make_uint4(padv4, padv4, padv4, padv4));
     } else {
-      dma16s<NOPS>(r, Sh::dst(tile, j, wofs), vo[j], 0);
+      dma16s<NOPS>(rsrc, Sh::dst(tile, j, wofs), vo[j], soff);
     }
   }
 };
