@@ -156,6 +156,9 @@ int plan_and_launch(igc::Params& p, bool fast, void* ws, size_t ws_bytes, hipStr
   const Plan pl = make_plan(KIND, p.M, p.N, p.K, fast, device_cus(dev), ws != nullptr);
   if (int s = check_workspace(pl, ws, ws_bytes)) return s;
   apply_plan(p, pl, ws);
+  if constexpr (KIND == igc::KIND_U8I8_GEMM || KIND == igc::KIND_U8I8_CONV) {
+    if (req_tiles(p, pl, fast)) return launch<KIND, SUMS | igc::REQ_TILES>(p, pl, fast, stream);
+  }
   return launch<KIND, SUMS>(p, pl, fast, stream);
 }
 

@@ -202,6 +202,14 @@ int launch_one(const igc::Params& p, const Plan& pl, hipStream_t stream) {
 
 template <int KIND, bool FAST, int SUMS>
 int launch_variant(const igc::Params& p, const Plan& pl, hipStream_t stream) {
+  if constexpr ((SUMS & igc::REQ_TILES) != 0) {
+    // whole requantize-only tiles: compiled for the 256-column integer tiles
+    if constexpr (FAST) {
+      if (pl.variant == V_224x256) return launch_one<KIND, 224, 256, 2, 2, FAST, SUMS>(p, pl, stream);
+      if (pl.variant == V_256x256) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, pl, stream);
+    }
+    return fail(IGC_EUNSUPPORTED, "internal: variant %d has no whole-tile requantize-only kernel", pl.variant);
+  }
   switch (pl.variant) {
     case V_224x256:
       if constexpr (FAST) return launch_one<KIND, 224, 256, 2, 2, FAST, SUMS>(p, pl, stream);
@@ -236,7 +244,7 @@ int launch(const igc::Params& p, const Plan& pl, bool fast, hipStream_t stream) 
   if constexpr (KIND == igc::KIND_F16_GEMM) {
     if (pl.variant == V_BYPASS || pl.variant == V_BYPASS16) return launch_bypass(p, pl, stream);
   }
-  if constexpr (KIND == igc::KIND_F16_CONV_C64) {
+  if constexpr (KIND == igc::KIND_F16_CONV_C64 || (SUMS & igc::REQ_TILES) != 0) {
     return launch_variant<KIND, true, SUMS>(p, pl, stream);  // dispatched only with aligned operands
   } else {
     return fast ? launch_variant<KIND, true, SUMS>(p, pl, stream)
@@ -244,8 +252,16 @@ int launch(const igc::Params& p, const Plan& pl, bool fast, hipStream_t stream) 
   }
 }
 
-// The (kind, zero-point sums) pairs the C ABI launches: the fp16 kinds
-// without sums, the u8 x i8 kinds with each subset of SUM_ROWS | SUM_COLS.
+// Whole requantize-only tiles (REQ_TILES): every tile whole, requantized
+// int8 the only output, no split, a 256-column integer tile.
+inline bool req_tiles(const igc::Params& p, const Plan& pl, bool fast) {
+  return fast && p.Qo && !p.Ci && !p.D && p.vec_q && pl.sk_wgs == 0 &&
+         (pl.variant == V_256x256 || pl.variant == V_224x256) && p.M % pl.bm == 0 && p.N % pl.bn == 0;
+}
+
+// The (kind, variant) pairs the C ABI launches: the fp16 kinds without
+// sums, the u8 x i8 kinds with each subset of SUM_ROWS | SUM_COLS, alone
+// and with REQ_TILES.
 #define IGC_LAUNCH_KINDS(X)         \
   X(0, igc::KIND_F16_GEMM, 0)       \
   X(1, igc::KIND_F16_CONV, 0)       \
@@ -257,7 +273,15 @@ int launch(const igc::Params& p, const Plan& pl, bool fast, hipStream_t stream) 
   X(7, igc::KIND_U8I8_CONV, 0)      \
   X(8, igc::KIND_U8I8_CONV, 1)      \
   X(9, igc::KIND_U8I8_CONV, 2)      \
-  X(10, igc::KIND_U8I8_CONV, 3)
+  X(10, igc::KIND_U8I8_CONV, 3)     \
+  X(11, igc::KIND_U8I8_GEMM, 4)     \
+  X(12, igc::KIND_U8I8_GEMM, 5)     \
+  X(13, igc::KIND_U8I8_GEMM, 6)     \
+  X(14, igc::KIND_U8I8_GEMM, 7)     \
+  X(15, igc::KIND_U8I8_CONV, 4)     \
+  X(16, igc::KIND_U8I8_CONV, 5)     \
+  X(17, igc::KIND_U8I8_CONV, 6)     \
+  X(18, igc::KIND_U8I8_CONV, 7)
 
 #define IGC_EXTERN_LAUNCH(n, K, S) \
   extern template int launch<K, S>(const igc::Params&, const Plan&, bool, hipStream_t);

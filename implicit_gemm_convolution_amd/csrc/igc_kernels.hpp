@@ -857,9 +857,13 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---------------------------------------------------------------------------
 // The kernel.
-//  SUMS (u8 x i8 only): the zero-point sums the mainloop accumulates, a mask
+//  VAR (u8 x i8 only): the zero-point sums the mainloop accumulates, a mask
 //  of SUM_ROWS (rowsum(A'), needed when zB != 0) and SUM_COLS (colsum(B),
-//  needed when zA != 128); each is compiled only into the kernels that use it.
+//  needed when zA != 128), each compiled only into the kernels that use it;
+//  plus REQ_TILES when every tile of the launch is whole, requantized int8
+//  is the only output and no tile is split: the epilogue is then compiled
+//  with its requantize-in-registers path alone (with the staged path beside
+//  it, the 256-column integer tiles spill registers).
 //  DEPTH: K tiles in flight ahead of the one being multiplied.  A has
 //  DEPTH + 1 LDS stages; B has 2 at DEPTH 2 (the 160 KiB of LDS at 256 x 256)
 //  and DEPTH + 1 otherwise.  Every launch uses DEPTH 2: deeper rings for the
@@ -867,9 +871,11 @@ __device__ __forceinline__ void lds_barrier() {
 //  MI355X, whose small launches are bound by fixed costs and a low clock,
 //  not by load latency.
 // ---------------------------------------------------------------------------
-constexpr int SUM_ROWS = 1, SUM_COLS = 2;
-template <int KIND, int BM, int BN, int WM, int WN, bool FAST, int SUMS = 0, int DEPTH = 2>
+constexpr int SUM_ROWS = 1, SUM_COLS = 2, REQ_TILES = 4;
+template <int KIND, int BM, int BN, int WM, int WN, bool FAST, int VAR = 0, int DEPTH = 2>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
+  constexpr int SUMS = VAR & (SUM_ROWS | SUM_COLS);
+  constexpr bool REQ = (VAR & REQ_TILES) != 0;
   constexpr int NT = 64 * WM * WN;
   constexpr bool INT8 = KIND == KIND_U8I8_GEMM || KIND == KIND_U8I8_CONV;
   constexpr int EB = INT8 ? 1 : 2;
@@ -885,7 +891,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // stream-K (shared tiles): compiled for the fp16 kinds and for the integer
   // kinds' aligned tiles of at most 128 rows (the wider integer tiles use
   // every register); the host splits only where it is compiled
-  constexpr bool SK = INT8 ? (BM <= 128 && FAST) : (SUMS == 0);
+  constexpr bool SK = INT8 ? (BM <= 128 && FAST && !REQ) : (SUMS == 0);
+  static_assert(!REQ || (INT8 && FAST), "whole requantize-only tiles: the aligned integer kernels");
   // (the im2col operand walks K in order, so the conv's B does too)
   constexpr bool CONV = KIND == KIND_F16_CONV || KIND == KIND_F16_CONV_C64 || KIND == KIND_U8I8_CONV;
   // u8 activations through the uniform-tap loader (padding stored as zA by
@@ -1414,7 +1421,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // rows and a row read are free of bank conflicts), and write it out in
   // 16-byte rows.  Other tiles and outputs take the staged int32 path below.
   bool qonly = false;
-  if constexpr (INT8) qonly = mode == 0 && p.Qo && !p.Ci && !p.D && p.vec_q && m0 + BM <= p.M && n0 + BN <= p.N;
+  if constexpr (INT8) qonly = REQ || (mode == 0 && p.Qo && !p.Ci && !p.D && p.vec_q && m0 + BM <= p.M && n0 + BN <= p.N);
   if (qonly) {
     if constexpr (INT8) {
       static_assert(BM * BN <= RA * SA_ALLOC, "the int8 tile fits in the A stages");
@@ -1469,7 +1476,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       for (int r = tid / CQ; r < BM; r += RPQ)
         store16_nt(p.Qo + (long long)(m0 + r) * p.ldq + n0 + qc, lds_read16(qs, qoff(r, qc)));
     }
-  } else {
+  } else if constexpr (!REQ) {
     if constexpr (INT8) {
       if (p.Qo) {
 #pragma unroll

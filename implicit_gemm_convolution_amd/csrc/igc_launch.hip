@@ -1,5 +1,5 @@
-// igc_launch.hip -- kernel instantiations: launch<KIND, SUMS> of igc_host.hpp
-// for the (kind, zero-point sums) pairs of IGC_LAUNCH_KINDS.  The build
+// igc_launch.hip -- kernel instantiations: launch<KIND, VAR> of igc_host.hpp
+// for the (kind, variant) pairs of IGC_LAUNCH_KINDS.  The build
 // compiles this file once per pair with -DIGC_LAUNCH_UNIT=<n>, so the kinds
 // compile in parallel; without the define it instantiates every pair.
 #include "igc_host.hpp"
@@ -38,6 +38,30 @@ template int launch<igc::KIND_U8I8_CONV, 2>(const igc::Params&, const Plan&, boo
 #endif
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 10
 template int launch<igc::KIND_U8I8_CONV, 3>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 11
+template int launch<igc::KIND_U8I8_GEMM, 4>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 12
+template int launch<igc::KIND_U8I8_GEMM, 5>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 13
+template int launch<igc::KIND_U8I8_GEMM, 6>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 14
+template int launch<igc::KIND_U8I8_GEMM, 7>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 15
+template int launch<igc::KIND_U8I8_CONV, 4>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 16
+template int launch<igc::KIND_U8I8_CONV, 5>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 17
+template int launch<igc::KIND_U8I8_CONV, 6>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 18
+template int launch<igc::KIND_U8I8_CONV, 7>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
 
 }  // namespace igc_host

@@ -283,6 +283,46 @@ def test_u8i8_requant_only_whole_and_edge_tiles(igc, oracle, variant, zA, zB):
     assert np.array_equal(got["Q"], ref)
 
 
+# Every tile whole, requantized int8 the only output: the 256-column tiles
+# take the kernels compiled with the requantize-in-registers epilogue alone
+# (all four zero-point sums masks), for the GEMM and the convolution.
+@pytest.mark.parametrize("v,M", [(0, 512), (4, 448)])
+@pytest.mark.parametrize("zA,zB", [(128, 0), (128, 3), (37, 0), (37, -5)])
+def test_u8i8_requant_whole_tiles(igc, oracle, v, M, zA, zB):
+    N, K = 512, 384
+    rng = np.random.default_rng(zA * 11 + zB + v + 2000)
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = synth.i8_uniform(rng, (N, K))
+    scale, bias = q_params(rng, N, K)
+    igc.set_tuning(v, 1)
+    try:
+        got = run_u8i8(igc, A, zA, Bt, zB, outputs=("Q",), scale=scale, bias=bias)
+    finally:
+        igc.set_tuning(-1, 1)
+    ref = oracle.requant(oracle.gemm_u8i8_naive(A, zA, Bt, zB), scale, bias)
+    assert np.count_nonzero((ref > -128) & (ref < 127)) > ref.size // 2
+    assert np.array_equal(got["Q"], ref)
+
+
+@pytest.mark.parametrize("v,Nb,HW", [(0, 4, 8), (4, 7, 8)])  # M = Nb*HW*HW = 256 / 448
+@pytest.mark.parametrize("zA,zB", [(100, 0), (0, 3)])
+def test_qconv_requant_whole_tiles(igc, oracle, v, Nb, HW, zA, zB):
+    C, Kout = 128, 256
+    rng = np.random.default_rng(v * 13 + zA + zB)
+    x = synth.u8_uniform(rng, (Nb, HW, HW, C))
+    w = synth.i8_uniform(rng, (Kout, 3, 3, C))
+    scale, bias = q_params(rng, Kout, 9 * C)
+    igc.set_tuning(v, 1)
+    try:
+        got = run_qconv(igc, x, zA, w, zB, (1, 1), (1, 1), outputs=("Q",), scale=scale, bias=bias)
+    finally:
+        igc.set_tuning(-1, 1)
+    C32 = oracle.conv2d_u8i8_direct_at(x, zA, w, zB, np.arange(Nb * HW * HW), (1, 1), (1, 1))
+    ref = oracle.requant(C32, scale, bias)
+    assert np.count_nonzero((ref > -128) & (ref < 127)) > ref.size // 2
+    assert np.array_equal(got["Q"], ref)
+
+
 @pytest.mark.parametrize("K", [33024, 33025])
 def test_u8i8_extreme_values_at_overflow_bound(igc, oracle, K):
     # |C| = 255 * 255 * K reaches 2,147,450,625 at K = 33025 (just below 2^31).

@@ -74,9 +74,15 @@ def test_no_scratch_in_main_loops_and_lds_within_limit(tiled):
         if bn == 256 and kind not in INT_KINDS:
             assert scratch == 0, (name, scratch)
         if bn == 256 and kind in INT_KINDS:
-            # the u8 x i8 256x256 epilogue (all 256 accumulator registers
-            # live across its two paths) spills a few accumulators once per tile
-            assert scratch <= (256 if bm == 256 else 0), (name, scratch)
+            var = int(re.search(r"gemm_kernel<(?:[^,]+, ){6}(\d+),", name).group(1))
+            if var & 4:
+                # whole requantize-only tiles: the epilogue has one path; without
+                # zero-point sums nothing spills (the 8192^3 requantize GEMM)
+                assert scratch <= (0 if var == 4 or bm != 256 else 16), (name, scratch)
+            else:
+                # the u8 x i8 256x256 epilogue (all 256 accumulator registers
+                # live across its two paths) spills a few accumulators once per tile
+                assert scratch <= (256 if bm == 256 else 0), (name, scratch)
 
 
 def test_fast_kernels_load_straight_into_lds_and_stream_outputs(tiled):
@@ -106,7 +112,8 @@ def test_zero_point_sums_on_matrix_cores_where_accumulators_fit(tiled):
     seen = 0
     for name, (body, _) in tiled.items():
         m = re.search(r"gemm_kernel<(\d+), (\d+), (\d+), \d+, \d+, (true|false), (\d+), \d+>", name)
-        kind, bm, bn, sums = int(m.group(1)), int(m.group(2)), int(m.group(3)), int(m.group(5))
+        # (the sums are the low two bits of the kernel's VAR argument)
+        kind, bm, bn, sums = int(m.group(1)), int(m.group(2)), int(m.group(3)), int(m.group(5)) & 3
         if kind not in INT_KINDS or sums == 0:
             continue
         dot4 = "v_dot4" in body
