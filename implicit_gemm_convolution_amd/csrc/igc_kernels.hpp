@@ -672,6 +672,7 @@ struct Im2colC64Loader {
   uint32_t pixb[Sh::NQ];  // (pixel of tap (0,0) + ph*W + pw) * C * EB + chunk * 16
   uint32_t mask[Sh::NQ];  // bit r*S+s: tap (r, s) of this row is inside the image
   mutable uint32_t vo[Sh::NQ];  // pixb, or OOB where the current tap is padding
+  mutable uint64_t lanes[EB == 1 ? Sh::NQ : 1];  // u8: the lanes of load j inside the image
   mutable int vo_tap;           // the tap vo[] was formed for
   mutable int cur_tap, cur_s, cur_c;  // tap r*S + s, s and channel of the next K tile
   mutable uint32_t soff;        // scalar offset of the next K tile: ((r*W + s)*C + c)*EB
@@ -756,7 +757,10 @@ struct Im2colC64Loader {
       // tiles past the last tap (prefetch beyond K) use bit 31, never set
       const int bit = tap < RS ? tap : 31;
 #pragma unroll
-      for (int j = 0; j < Sh::NQ; ++j) vo[j] = ((mask[j] >> bit) & 1u) ? pixb[j] : OOB;
+      for (int j = 0; j < Sh::NQ; ++j) {
+        vo[j] = ((mask[j] >> bit) & 1u) ? pixb[j] : OOB;
+        if constexpr (EB == 1) lanes[j] = __builtin_amdgcn_ballot_w64(vo[j] != OOB);
+      }
       vo_tap = tap;
     }
   }
@@ -770,14 +774,18 @@ struct Im2colC64Loader {
   __device__ __forceinline__ void part(uint8_t* tile, int, int j) const {
     retap(cur_tap);
     if constexpr (EB == 1) {
-      // (tiles past the last tap, prefetched and never multiplied, get zA
-      // everywhere; with zA = 0 the stores write the zeros an out-of-range
-      // load would)
-      dma16s_or_fill<NOPS>(rsrc, Sh::dst(tile, j, wofs), pixb[j], soff, __builtin_amdgcn_ballot_w64(vo[j] != OOB),
-                           make_uint4(padv4, padv4, padv4, padv4));
-    } else {
-      dma16s<NOPS>(rsrc, Sh::dst(tile, j, wofs), vo[j], soff);
+      // The masked form only where one of the load's 8 rows is padding for
+      // this tap (about 4 loads in 10 at 3x3, pad 1, 14x14); a wave-uniform
+      // branch.  (Tiles past the last tap, prefetched and never multiplied,
+      // get zA everywhere; with zA = 0 the stores write the zeros an
+      // out-of-range load would.)
+      if (lanes[j] != ~0ull) {
+        dma16s_or_fill<NOPS>(rsrc, Sh::dst(tile, j, wofs), pixb[j], soff, lanes[j],
+                             make_uint4(padv4, padv4, padv4, padv4));
+        return;
+      }
     }
+    dma16s<NOPS>(rsrc, Sh::dst(tile, j, wofs), vo[j], soff);
   }
 };
 
