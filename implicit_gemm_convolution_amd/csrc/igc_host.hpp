@@ -133,6 +133,10 @@ inline Plan make_plan(int kind, int M, int N, int K, bool fast, int cus, bool ws
     if (v == V_BYPASS || v == V_BYPASS16) v = V_64x64;  // (forced, for a kind or shape without the bypass kernel)
     // The element-wise (unaligned) loaders need more registers; they stop at 128x128.
     if (!fast && (v == V_256x256 || v == V_256x128 || v == V_224x256)) v = V_128x128;
+    // The uniform-tap u8 convolution keeps two registers per fragment row (its
+    // rows' tap masks and conversion constants) beside the accumulators: at
+    // 256x256 the K loop would spill, so its 256-row tile is the 224-row one.
+    if (kind == igc::KIND_U8I8_CONV && fast && v == V_256x256) v = V_224x256;
   }
   pl.variant = v;
   variant_tile(v, pl.bm, pl.bn);
@@ -206,7 +210,8 @@ int launch_variant(const igc::Params& p, const Plan& pl, hipStream_t stream) {
     // whole requantize-only tiles: compiled for the 256-column integer tiles
     if constexpr (FAST) {
       if (pl.variant == V_224x256) return launch_one<KIND, 224, 256, 2, 2, FAST, SUMS>(p, pl, stream);
-      if (pl.variant == V_256x256) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, pl, stream);
+      if constexpr (KIND != igc::KIND_U8I8_CONV)
+        if (pl.variant == V_256x256) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, pl, stream);
     }
     return fail(IGC_EUNSUPPORTED, "internal: variant %d has no whole-tile requantize-only kernel", pl.variant);
   }
@@ -214,8 +219,8 @@ int launch_variant(const igc::Params& p, const Plan& pl, hipStream_t stream) {
     case V_224x256:
       if constexpr (FAST) return launch_one<KIND, 224, 256, 2, 2, FAST, SUMS>(p, pl, stream);
       break;
-    case V_256x256:
-      if constexpr (FAST) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, pl, stream);
+    case V_256x256:  // (not for the uniform-tap u8 convolution, see make_plan)
+      if constexpr (FAST && KIND != igc::KIND_U8I8_CONV) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, pl, stream);
       break;
     case V_256x128:
       if constexpr (FAST) return launch_one<KIND, 256, 128, 2, 2, FAST, SUMS>(p, pl, stream);

@@ -302,37 +302,6 @@ __device__ __forceinline__ void dma16(const Rsrc& r, uint8_t* lds, uint32_t off)
   }
 }
 
-// dma16s for the lanes set in `lanes`; every other lane instead stores
-// `fill` into its own 16-byte slot of the same LDS rows (the slot its load
-// would have written: the wave's rows at M0, lane l at M0 + 16 l).  The
-// execution mask is narrowed, complemented and restored inside the asm, so
-// the load is issued even when no lane is set and every explicit vmcnt count
-// in the kernel stays exact; the store counts on lgkmcnt, which the kernel
-// waits for in full before a tile is read.  The scalar mask operations set
-// SCC, so the asm declares it clobbered: the compiler may otherwise keep a
-// comparison live in SCC across it.
-template <int NOPS>
-__device__ __forceinline__ void dma16s_or_fill(const Rsrc& r, uint8_t* lds, uint32_t off, uint32_t soff,
-                                               uint64_t lanes, uint4 fill) {
-  static_assert(NOPS == NOPS_LOOP || NOPS == NOPS_SAFE, "wait states");
-  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-  const uint32_t vaddr = m0 + (threadIdx.x & 63) * CHUNK_BYTES;
-  const u32x4 fv = __builtin_bit_cast(u32x4, fill);
-  uint64_t saved;
-  if constexpr (NOPS == NOPS_SAFE)
-    asm volatile(
-        "s_and_saveexec_b64 %0, %5\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
-        "s_andn2_b64 exec, %0, %5\n\tds_write_b128 %6, %7\n\ts_mov_b64 exec, %0"
-        : "=&s"(saved) : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0), "s"(lanes), "v"(vaddr), "v"(fv)
-        : "memory", "scc");
-  else
-    asm volatile(
-        "s_and_saveexec_b64 %0, %5\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
-        "s_andn2_b64 exec, %0, %5\n\tds_write_b128 %6, %7\n\ts_mov_b64 exec, %0"
-        : "=&s"(saved) : "v"(off), "s"(r.d), "s"(soff), "{m0}"(m0), "s"(lanes), "v"(vaddr), "v"(fv)
-        : "memory", "scc");
-}
-
 // Direct-to-LDS tiles of ROWS rows x 128 bytes.  Wave-instruction q fills
 // rows 8q .. 8q+7 (1 KB of LDS); lane l covers row 8q + l/8 and fetches the
 // global chunk that belongs in its LDS slot l % 8, i.e. chunk
@@ -644,6 +613,36 @@ struct Im2colLoader {
   }
 };
 
+// Convolution output row g = (n, p, q): its image n and the input position
+// (h0, w0) of tap (0, 0).
+__device__ __forceinline__ void conv_row(const Params& p, int g, int& n, int& h0, int& w0) {
+  n = (int)p.fd_pq.div((uint32_t)g);
+  const int pq = g - n * (p.P * p.Q);
+  const int pp = (int)p.fd_q.div((uint32_t)pq);
+  const int qq = pq - pp * p.Q;
+  h0 = pp * p.sh - p.ph;
+  w0 = qq * p.sw - p.pw;
+}
+// One bit at r*S for every filter row r.
+__device__ __forceinline__ uint32_t conv_tap_rows(const Params& p) {
+  uint32_t rep = 0;
+  for (int r = 0; r < p.R; ++r) rep |= 1u << (r * p.S);
+  return rep;
+}
+// Bit r*S + s set where tap (r, s) of the output row whose tap (0, 0) is at
+// (h0, w0) lies inside the image (R*S <= 31): r in [r_lo, r_hi], s in
+// [s_lo, s_hi], the product of a column run (bits s_lo .. s_hi) and one bit
+// at r*S per row of the row run (no carries).
+__device__ __forceinline__ uint32_t conv_tap_mask(const Params& p, int h0, int w0, uint32_t rep) {
+  const int r_lo = max(0, -h0), r_hi = min(p.R - 1, p.H - 1 - h0);
+  const int s_lo = max(0, -w0), s_hi = min(p.S - 1, p.W - 1 - w0);
+  // (shift counts clamped to 31: a window wholly in the padding has
+  // r_lo > r_hi or s_lo > s_hi, and its mask is 0)
+  const uint32_t cols = (2u << min(max(s_hi, 0), 30)) - (1u << min(s_lo, 31));
+  const uint32_t rows = rep & ((2u << min(max(r_hi, 0) * p.S, 30)) - (1u << min(r_lo * p.S, 31)));
+  return (r_lo <= r_hi && s_lo <= s_hi) ? rows * cols : 0u;
+}
+
 // The implicit-im2col A operand when a K tile (128 bytes: 64 fp16 or 128 u8
 // channels) always lies in one tap: C a multiple of it and R*S <= 31 (FAST
 // only).  The tap (r, s) is then the same for all lanes, so the tap walk is
@@ -658,10 +657,9 @@ struct Im2colLoader {
 // becomes OOB where the tap is padding, so that lane's load reads zeros.
 // The buffer spans 2^31 bytes (OOB): valid offsets stay below it (the host
 // checks that x plus the padding's offset, and the largest scalar offset, fit
-// in 2^31 bytes).  For u8 activations the padding must hold the zero point
-// zA: there the padded lanes take no part in the load and store zA into their
-// own LDS slots at once (the stage is free when its loads are issued, and no
-// load writes those slots), so the tile is complete when its loads land.
+// in 2^31 bytes).  u8 activations: the padding must hold the zero point zA;
+// the kernel turns the zero rows into zA - 128 when it converts fragments to
+// signed bytes (see gemm_kernel).
 template <int NT, int ROWS, int EB = 2>
 struct Im2colC64Loader {
   typedef DmaShape<NT, ROWS> Sh;
@@ -672,12 +670,10 @@ struct Im2colC64Loader {
   uint32_t pixb[Sh::NQ];  // (pixel of tap (0,0) + ph*W + pw) * C * EB + chunk * 16
   uint32_t mask[Sh::NQ];  // bit r*S+s: tap (r, s) of this row is inside the image
   mutable uint32_t vo[Sh::NQ];  // pixb, or OOB where the current tap is padding
-  mutable uint64_t lanes[EB == 1 ? Sh::NQ : 1];  // u8: the lanes of load j inside the image
   mutable int vo_tap;           // the tap vo[] was formed for
   mutable int cur_tap, cur_s, cur_c;  // tap r*S + s, s and channel of the next K tile
   mutable uint32_t soff;        // scalar offset of the next K tile: ((r*W + s)*C + c)*EB
   uint32_t step, row_jump;      // soff per K tile; extra soff when s wraps
-  uint32_t padv4;               // zA in every byte
   // blocked NHWCnc input (fp16 only): every pixel and channel offset is 16
   // times its NHWC value (16 images interleaved), plus the row's image within
   // its group of 16 and the chunk's place in a 16-channel block
@@ -687,16 +683,12 @@ struct Im2colC64Loader {
   __device__ __forceinline__ void init(const Params& p, int m0, int kt0) {
     wofs = Sh::wave_offset();
     C = p.C; S = p.S; RS = p.R * p.S;
-    padv4 = (uint32_t)(uint8_t)(p.zAp + 128) * 0x01010101u;
     const int p0 = p.ph * p.W + p.pw;
     blk_shift = (EB == 2 && p.blk) ? 4 : 0;
     rsrc = make_rsrc((const void*)((uintptr_t)p.A - ((uintptr_t)p0 * C * EB << blk_shift)), OOB);
     step = (uint32_t)(KT_BYTES << blk_shift);
     row_jump = (uint32_t)(((long long)(p.W - S) * C * EB) << blk_shift);
-    const int PQ = p.P * p.Q;
-    // one bit at r*S for every filter row r
-    uint32_t rep = 0;
-    for (int r = 0; r < p.R; ++r) rep |= 1u << (r * p.S);
+    const uint32_t rep = conv_tap_rows(p);
     // chunk c of a 128-byte K-tile row (channels 8c .. 8c+7 of the tile):
     // byte 16c (NHWC), or 512 (c / 2) + 16 (c % 2) in the blocked layout
     const int ch = Sh::lane_chunk();
@@ -707,26 +699,11 @@ struct Im2colC64Loader {
       pixb[j] = 0;
       mask[j] = 0;
       if (m < p.M) {
-        const int g = blk_shift ? (m >> 4) : m;
-        const int n = (int)p.fd_pq.div((uint32_t)g);
-        const int pq = g - n * PQ;
-        const int pp = (int)p.fd_q.div((uint32_t)pq);
-        const int qq = pq - pp * p.Q;
-        const int h0 = pp * p.sh - p.ph;
-        const int w0 = qq * p.sw - p.pw;
+        int n, h0, w0;
+        conv_row(p, blk_shift ? (m >> 4) : m, n, h0, w0);
         const uint32_t nn_off = blk_shift ? (uint32_t)((m & 15) * 16 * EB) : 0u;
         pixb[j] = ((uint32_t)((n * p.H * p.W + h0 * p.W + w0 + p0) * C * EB) << blk_shift) + nn_off + chunk_off;
-        // taps (r, s) inside the image: r in [r_lo, r_hi], s in [s_lo, s_hi];
-        // bit r*S + s of the mask is the product of a column run (bits s_lo
-        // .. s_hi) and one bit at r*S per row of the row run (no carries:
-        // R*S <= 31)
-        const int r_lo = max(0, -h0), r_hi = min(p.R - 1, p.H - 1 - h0);
-        const int s_lo = max(0, -w0), s_hi = min(p.S - 1, p.W - 1 - w0);
-        // (shift counts clamped to 31: a window wholly in the padding has
-        // r_lo > r_hi or s_lo > s_hi, and its mask is 0)
-        const uint32_t cols = (2u << min(max(s_hi, 0), 30)) - (1u << min(s_lo, 31));
-        const uint32_t rows = rep & ((2u << min(max(r_hi, 0) * p.S, 30)) - (1u << min(r_lo * p.S, 31)));
-        mask[j] = (r_lo <= r_hi && s_lo <= s_hi) ? rows * cols : 0u;
+        mask[j] = conv_tap_mask(p, h0, w0, rep);
       }
     }
     const int k = kt0 * CPT;
@@ -757,10 +734,7 @@ struct Im2colC64Loader {
       // tiles past the last tap (prefetch beyond K) use bit 31, never set
       const int bit = tap < RS ? tap : 31;
 #pragma unroll
-      for (int j = 0; j < Sh::NQ; ++j) {
-        vo[j] = ((mask[j] >> bit) & 1u) ? pixb[j] : OOB;
-        if constexpr (EB == 1) lanes[j] = __builtin_amdgcn_ballot_w64(vo[j] != OOB);
-      }
+      for (int j = 0; j < Sh::NQ; ++j) vo[j] = ((mask[j] >> bit) & 1u) ? pixb[j] : OOB;
       vo_tap = tap;
     }
   }
@@ -773,18 +747,6 @@ struct Im2colC64Loader {
   template <int NOPS = NOPS_LOOP>
   __device__ __forceinline__ void part(uint8_t* tile, int, int j) const {
     retap(cur_tap);
-    if constexpr (EB == 1) {
-      // The masked form only where one of the load's 8 rows is padding for
-      // this tap (about 4 loads in 10 at 3x3, pad 1, 14x14); a wave-uniform
-      // branch.  (Tiles past the last tap, prefetched and never multiplied,
-      // get zA everywhere; with zA = 0 the stores write the zeros an
-      // out-of-range load would.)
-      if (lanes[j] != ~0ull) {
-        dma16s_or_fill<NOPS>(rsrc, Sh::dst(tile, j, wofs), pixb[j], soff, lanes[j],
-                             make_uint4(padv4, padv4, padv4, padv4));
-        return;
-      }
-    }
     dma16s<NOPS>(rsrc, Sh::dst(tile, j, wofs), vo[j], soff);
   }
 };
@@ -1038,6 +1000,45 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // of K: 64 for 16 x 16 blocks, 32 for 32 x 32).
   const int frow = lane % MB;
   const int fhalf = lane / MB;
+  // The u8 convolution through the uniform-tap loader: a padded row's K tile
+  // lands as zero bytes, and the conversion to signed bytes (A xor 0x80 =
+  // A - 128) xors each fragment row with xk[i]: 0x80808080 where the current
+  // tap is inside the image, 0x80808080 xor (zA in every byte) where it is
+  // padding, so a padded row becomes zA - 128 like an input byte equal to
+  // zA.  xk follows the tap of the K tile being multiplied (a tap spans
+  // C / 128 tiles); row 0's constant moves to the next tile's tap when the
+  // last k-step begins (its last chunk converts the next tile's first
+  // fragment), the others at the end of the tile.
+  constexpr uint32_t X80 = 0x80808080u;
+  uint32_t fmask[U8_UNIFORM_TAPS ? FM : 1];  // tap-inside bits of this lane's fragment rows
+  uint32_t xk[U8_UNIFORM_TAPS ? FM : 1];
+  uint32_t xz = X80;
+  int xtap = 0, xleft = 1, xtpt = 1;  // tap of the K tile in use, its tiles left, tiles per tap
+  if constexpr (U8_UNIFORM_TAPS) {
+    xz = X80 ^ ((uint32_t)(uint8_t)(p.zAp + 128) * 0x01010101u);
+    const uint32_t rep = conv_tap_rows(p);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = m0 + wm * TM + i * MB + frow;
+      fmask[i] = 0;
+      if (m < p.M) {
+        int n, h0, w0;
+        conv_row(p, m, n, h0, w0);
+        fmask[i] = conv_tap_mask(p, h0, w0, rep);
+      }
+    }
+    const int k = k0 * KT_BYTES;  // u8: one byte per channel
+    xtap = (int)p.fd_c.div((uint32_t)k);
+    xtpt = p.C / KT_BYTES;
+    xleft = xtpt - (k - xtap * p.C) / KT_BYTES;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) xk[i] = ((fmask[i] >> xtap) & 1u) ? X80 : xz;
+  }
+  // the conversion constant of fragment row i
+  auto xconst = [&](int i) -> uint32_t {
+    if constexpr (U8_UNIFORM_TAPS) return xk[i];
+    else return X80;
+  };
   uint4 fa[2][FM], fb[2][FN];
   auto read_a = [&](const uint8_t* As, int ks, int i, uint4& a) {
     a = lds_read16(As, swz(wm * TM + i * MB + frow, ks * LPR + fhalf));
@@ -1083,10 +1084,11 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       }
     uint4 axn = a_up;
     if constexpr (INT8) {
-      axn.x ^= 0x80808080u;
-      axn.y ^= 0x80808080u;
-      axn.z ^= 0x80808080u;
-      axn.w ^= 0x80808080u;
+      const uint32_t xc = xconst((c + 1) % FM);  // a_up is fragment row (c + 1) % FM
+      axn.x ^= xc;
+      axn.y ^= xc;
+      axn.z ^= xc;
+      axn.w ^= xc;
     }
 #pragma unroll
     for (int j = 1; j < FN; ++j) Mfma<KIND, MB>::run(acc[c][j], b[j], ac);
@@ -1137,11 +1139,12 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 #pragma unroll
   for (int j = 0; j < FN; ++j) read_b(sb0, 0, j, fb[0][j]);
   if constexpr (INT8) {
+    const uint32_t xc = xconst(0);
     ax = fa[0][0];
-    ax.x ^= 0x80808080u;
-    ax.y ^= 0x80808080u;
-    ax.z ^= 0x80808080u;
-    ax.w ^= 0x80808080u;
+    ax.x ^= xc;
+    ax.y ^= xc;
+    ax.z ^= xc;
+    ax.w ^= xc;
   }
 
   // K tile kt (D = DEPTH): A in stage kt % RA, B in stage kt % RB.  On entry
@@ -1183,6 +1186,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     lds_barrier();
     const uint8_t* As1 = stA(std::integral_constant<int, u + 1>());
     const uint8_t* Bs1 = stB(std::integral_constant<int, u + 1>());
+    // row 0's conversion constant now serves the next tile's first fragment
+    if constexpr (U8_UNIFORM_TAPS) xk[0] = ((fmask[0] >> (xleft == 1 ? xtap + 1 : xtap)) & 1u) ? X80 : xz;
 #pragma unroll
     for (int c = 0; c < FM; ++c) {
       chunk(c, fa[buf], fb[buf], As1, Bs1, 0, fa[buf ^ 1], fb[buf ^ 1],
@@ -1193,6 +1198,14 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       });
     }
     lb.advance();
+    if constexpr (U8_UNIFORM_TAPS) {
+      if (--xleft == 0) {
+        ++xtap;
+        xleft = xtpt;
+#pragma unroll
+        for (int i = 1; i < FM; ++i) xk[i] = ((fmask[i] >> xtap) & 1u) ? X80 : xz;
+      }
+    }
   };
   for (int kt = k0; kt < k1; kt += UNR) {
     tile(kt, std::integral_constant<int, 0>());

@@ -304,7 +304,8 @@ def test_u8i8_requant_whole_tiles(igc, oracle, v, M, zA, zB):
     assert np.array_equal(got["Q"], ref)
 
 
-@pytest.mark.parametrize("v,Nb,HW", [(0, 4, 8), (4, 7, 8)])  # M = Nb*HW*HW = 256 / 448
+# (the uniform-tap u8 convolution runs its 256-row tile as the 224-row one)
+@pytest.mark.parametrize("v,Nb,HW", [(4, 14, 4), (4, 7, 8), (0, 7, 8)])  # M = Nb*HW*HW = 224 / 448
 @pytest.mark.parametrize("zA,zB", [(100, 0), (0, 3)])
 def test_qconv_requant_whole_tiles(igc, oracle, v, Nb, HW, zA, zB):
     C, Kout = 128, 256
