@@ -518,8 +518,8 @@ int conv2d_implicit_gemm_nhwcnc(int Nb, int H, int W, int C, int Kout, int R, in
   if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   p.B = wk;
   apply_plan(p, pl, workspace);
-  if (kind == igc::KIND_F16_CONV_C64) return launch<igc::KIND_F16_CONV_C64, 0>(p, pl, true, st);
-  return launch<igc::KIND_F16_CONV, 0>(p, pl, fast, st);
+  if (kind == igc::KIND_F16_CONV_C64) return launch<igc::KIND_F16_CONV_C64, igc::BLK_OUT>(p, pl, true, st);
+  return launch<igc::KIND_F16_CONV, igc::BLK_OUT>(p, pl, fast, st);
 }
 
 }  // extern "C"

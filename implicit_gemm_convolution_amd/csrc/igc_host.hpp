@@ -265,8 +265,8 @@ inline bool req_tiles(const igc::Params& p, const Plan& pl, bool fast) {
 }
 
 // The (kind, variant) pairs the C ABI launches: the fp16 kinds without
-// sums, the u8 x i8 kinds with each subset of SUM_ROWS | SUM_COLS, alone
-// and with REQ_TILES.
+// sums (the convolutions also with BLK_OUT), the u8 x i8 kinds with each
+// subset of SUM_ROWS | SUM_COLS, alone and with REQ_TILES.
 #define IGC_LAUNCH_KINDS(X)         \
   X(0, igc::KIND_F16_GEMM, 0)       \
   X(1, igc::KIND_F16_CONV, 0)       \
@@ -286,7 +286,9 @@ inline bool req_tiles(const igc::Params& p, const Plan& pl, bool fast) {
   X(15, igc::KIND_U8I8_CONV, 4)     \
   X(16, igc::KIND_U8I8_CONV, 5)     \
   X(17, igc::KIND_U8I8_CONV, 6)     \
-  X(18, igc::KIND_U8I8_CONV, 7)
+  X(18, igc::KIND_U8I8_CONV, 7)     \
+  X(19, igc::KIND_F16_CONV, 8)      \
+  X(20, igc::KIND_F16_CONV_C64, 8)
 
 #define IGC_EXTERN_LAUNCH(n, K, S) \
   extern template int launch<K, S>(const igc::Params&, const Plan&, bool, hipStream_t);

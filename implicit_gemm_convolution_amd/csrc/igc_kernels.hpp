@@ -833,7 +833,9 @@ __device__ __forceinline__ void lds_barrier() {
 //  plus REQ_TILES when every tile of the launch is whole, requantized int8
 //  is the only output and no tile is split: the epilogue is then compiled
 //  with its requantize-in-registers path alone (with the staged path beside
-//  it, the 256-column integer tiles spill registers).
+//  it, the 256-column integer tiles spill registers).  fp16 convolution:
+//  BLK_OUT writes the output in the blocked NHWCnc layout (the launch's
+//  p.blk), so the row-major kernels carry no blocked code.
 //  DEPTH: K tiles in flight ahead of the one being multiplied.  A has
 //  DEPTH + 1 LDS stages; B has 2 at DEPTH 2 (the 160 KiB of LDS at 256 x 256)
 //  and DEPTH + 1 otherwise.  Every launch uses DEPTH 2: deeper rings for the
@@ -841,11 +843,12 @@ __device__ __forceinline__ void lds_barrier() {
 //  MI355X, whose small launches are bound by fixed costs and a low clock,
 //  not by load latency.
 // ---------------------------------------------------------------------------
-constexpr int SUM_ROWS = 1, SUM_COLS = 2, REQ_TILES = 4;
+constexpr int SUM_ROWS = 1, SUM_COLS = 2, REQ_TILES = 4, BLK_OUT = 8;
 template <int KIND, int BM, int BN, int WM, int WN, bool FAST, int VAR = 0, int DEPTH = 2>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int SUMS = VAR & (SUM_ROWS | SUM_COLS);
   constexpr bool REQ = (VAR & REQ_TILES) != 0;
+  constexpr bool BLKO = (VAR & BLK_OUT) != 0;
   constexpr int NT = 64 * WM * WN;
   constexpr bool INT8 = KIND == KIND_U8I8_GEMM || KIND == KIND_U8I8_CONV;
   constexpr int EB = INT8 ? 1 : 2;
@@ -863,6 +866,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // every register); the host splits only where it is compiled
   constexpr bool SK = INT8 ? (BM <= 128 && FAST && !REQ) : (SUMS == 0);
   static_assert(!REQ || (INT8 && FAST), "whole requantize-only tiles: the aligned integer kernels");
+  static_assert(!BLKO || !INT8, "blocked output: the fp16 convolution");
   // (the im2col operand walks K in order, so the conv's B does too)
   constexpr bool CONV = KIND == KIND_F16_CONV || KIND == KIND_F16_CONV_C64 || KIND == KIND_U8I8_CONV;
   // u8 activations through the uniform-tap loader (padding stored as zA by
@@ -1352,15 +1356,18 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // One group of 4 columns of one row leaves for the outputs.
   // corrected: v already holds the zero-point-corrected sum without the
   // K*zA'*zB term (the shared tiles of the integer kernels)
-  auto emit = [&](uint4 v, int lrow, bool corrected) {
+  // lc: the thread's first column within the tile (lcol but for blocked
+  // output passes)
+  auto emit = [&](uint4 v, int lrow, bool corrected, int lc) {
     const int row = m0 + lrow;
+    const int col = n0 + lc;
       if (row < p.M && col < p.N) {
         const bool full = col + 3 < p.N;
         if constexpr (!INT8) {
           // (blocked output: 16-column block col/16 of 16-row group row/16 is
           // one 16 x 16 array; 4 consecutive columns stay inside it)
-          float* dst = p.blk ? p.Cf + ((long long)(row >> 4) * (p.N >> 4) + (col >> 4)) * 256 + (row & 15) * 16 + (col & 15)
-                             : p.Cf + (long long)row * p.ldcf + col;
+          float* dst = BLKO ? p.Cf + ((long long)(row >> 4) * (p.N >> 4) + (col >> 4)) * 256 + (row & 15) * 16 + (col & 15)
+                            : p.Cf + (long long)row * p.ldcf + col;
           if (full && p.vec_c) {
             store16_nt(dst, v);
           } else {
@@ -1524,12 +1531,29 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
         }
       }
       __syncthreads();
+      // A whole tile into the blocked layout (fp16 convolution, NHWCnc
+      // output): each wave stores one 16 x 16 block per pass, lane l taking
+      // row l % 16 and columns 4 (l / 16) .. +3 of it, so one store
+      // instruction writes the block's 1 KB of y; the 16 rows of a pass read
+      // distinct LDS banks.  Otherwise (below) a wave stores one row per pass.
+      if (BLKO && mode == 0) {
+        if constexpr (BLKO) {
+          constexpr int PB = BN / 64;  // passes per 16-row band
+          static_assert(NT == 256 && MB == 16, "blocked passes: 4 waves x 16 columns of 16 x 16 blocks");
+  #pragma unroll
+          for (int pass = 0; pass < TM / RPP; ++pass) {
+            const int rr = (pass / PB) * 16 + (lane & 15);  // row within the wave-row
+            const int lc = (pass % PB) * 64 + wave * 16 + 4 * (lane >> 4);
+            const uint8_t* arr = stage_rt((pass / PB) / 2);
+            emit(*reinterpret_cast<const uint4*>(arr + stage_off(rr & 31, lc)), h * TM + rr, false, lc);
+          }
+        }
+      } else {
   #pragma unroll
       for (int pass = 0; pass < TM / RPP; ++pass) {
         const int rr = rr0 + pass * RPP;         // row within the wave-row
         const uint8_t* arr = stage_rt((pass * RPP) / 32);
         const int lrow = h * TM + rr;
-        const int row = m0 + lrow;
         uint4 v = *reinterpret_cast<const uint4*>(arr + stage_off(rr & 31, lcol));
         const int voff = (lrow * BN + lcol) * 4;
         if constexpr (SK) {
@@ -1555,7 +1579,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
             continue;
           }
         }
-        if (mode == 0) emit(v, lrow, false);
+        if (mode == 0) emit(v, lrow, false, lcol);
+      }
       }
       __syncthreads();
     }
@@ -1606,7 +1631,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           }
         }
 #pragma unroll
-        for (int b = 0; b < RB; ++b) emit(v[b], lrow0 + b * RPP, true);
+        for (int b = 0; b < RB; ++b) emit(v[b], lrow0 + b * RPP, true, lcol);
       }
     }
   }

@@ -63,5 +63,11 @@ template int launch<igc::KIND_U8I8_CONV, 6>(const igc::Params&, const Plan&, boo
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 18
 template int launch<igc::KIND_U8I8_CONV, 7>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 19
+template int launch<igc::KIND_F16_CONV, 8>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 20
+template int launch<igc::KIND_F16_CONV_C64, 8>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
 
 }  // namespace igc_host
