@@ -1086,16 +1086,42 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           read_a(As_n, ks_n, r - FN, an[r - FN]);
         ++nrd;
       }
+    constexpr int NV = (INT8 ? 4 : 0) + ((!MSUMS && (SUMS & SUM_ROWS)) ? 4 : 0) +
+                       ((!MSUMS && (SUMS & SUM_COLS)) ? 4 * ((FN + FM - 1) / FM) : 0);
+    // u8 without v_dot4 sums: the conversion of the next chunk's fragment
+    // goes between the row's last two MFMAs (fenced), so the reads issued
+    // early in the chunk have it to land before the conversion waits for
+    // them, and the last MFMA covers the conversion's latency.  (Left to the
+    // scheduler, the conversion followed the first read, behind an LDS wait
+    // two MFMAs into the chunk.)
+    constexpr bool LATE_X = INT8 && NV == 4 && FN >= 4;
     uint4 axn = a_up;
-    if constexpr (INT8) {
-      const uint32_t xc = xconst((c + 1) % FM);  // a_up is fragment row (c + 1) % FM
-      axn.x ^= xc;
-      axn.y ^= xc;
-      axn.z ^= xc;
-      axn.w ^= xc;
-    }
+    auto convert = [&]() {
+      if constexpr (INT8) {
+        const uint32_t xc = xconst((c + 1) % FM);  // a_up is fragment row (c + 1) % FM
+        axn.x ^= xc;
+        axn.y ^= xc;
+        axn.z ^= xc;
+        axn.w ^= xc;
+      }
+    };
+    if constexpr (LATE_X) {
 #pragma unroll
-    for (int j = 1; j < FN; ++j) Mfma<KIND, MB>::run(acc[c][j], b[j], ac);
+      for (int j = 1; j < FN - 1; ++j) Mfma<KIND, MB>::run(acc[c][j], b[j], ac);
+#pragma unroll
+      for (int q = 1; q < FN - 1; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (q <= nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      convert();
+      __builtin_amdgcn_sched_barrier(0);
+      Mfma<KIND, MB>::run(acc[c][FN - 1], b[FN - 1], ac);
+    } else {
+      convert();
+#pragma unroll
+      for (int j = 1; j < FN; ++j) Mfma<KIND, MB>::run(acc[c][j], b[j], ac);
+    }
     if constexpr (MSUMS) {
       if constexpr ((SUMS & SUM_ROWS) != 0) Mfma<KIND, MB>::run(racc, onehot[c], ac);
       if constexpr ((SUMS & SUM_COLS) != 0) {
@@ -1112,11 +1138,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       }
     }
     // between the MFMAs: the reads first, then the vector ALU work
-    constexpr int NV = (INT8 ? 4 : 0) + ((!MSUMS && (SUMS & SUM_ROWS)) ? 4 : 0) +
-                       ((!MSUMS && (SUMS & SUM_COLS)) ? 4 * ((FN + FM - 1) / FM) : 0);
     int nv = 0;
 #pragma unroll
-    for (int q = 1; q < FN; ++q) {
+    for (int q = 1; q < (LATE_X ? 1 : FN); ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       if (q <= nrd) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
