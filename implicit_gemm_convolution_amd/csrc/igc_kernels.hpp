@@ -796,6 +796,18 @@ struct Mfma<KIND_U8I8_GEMM, 16> {
   }
 };
 
+// The requantize step's rounding and saturation of y to int8: clamping y to
+// [-128, 127] first gives the same result (the bounds are integers and
+// rounding is monotonic); adding 1.5 * 2^23 then rounds in fp32 to the
+// nearest integer, ties to even, and leaves that integer in two's
+// complement in the low mantissa bits: the int8 value is the low byte of
+// the sum's bit pattern.  (Two operations instead of a rounding, a clamp and
+// a conversion.)
+__device__ __forceinline__ uint32_t requant_bits(float y) {
+  const float v = fminf(fmaxf(y, -128.f), 127.f);
+  return __builtin_bit_cast(uint32_t, v + 12582912.0f);
+}
+
 __device__ __forceinline__ int sum_bytes(uint4 v, int acc) {
   acc = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, acc, false);
   acc = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, acc, false);
@@ -1342,7 +1354,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       }
     }
   }
-  if constexpr (INT8) kzz = (uint32_t)p.K * (uint32_t)p.zAp * (uint32_t)p.zB;
+  // (nonzero only when both zA' and zB are, i.e. with both sums compiled)
+  if constexpr (INT8 && SUMS == (SUM_ROWS | SUM_COLS)) kzz = (uint32_t)p.K * (uint32_t)p.zAp * (uint32_t)p.zB;
 
   constexpr int GPR = BN / 4;    // 4-column groups per row
   constexpr int RPP = NT / GPR;  // rows per pass of the whole workgroup
@@ -1450,10 +1463,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
             for (int q = 0; q < 4; ++q) {
               const float t = cf[q] * q_scale[q];  // separately rounded: built with -ffp-contract=off
               const float y = t + q_bias[q];
-              float r = __builtin_rintf(y);         // half to even
-              r = fminf(fmaxf(r, -128.f), 127.f);
-              qv[q] = (int8_t)(int)r;
-              packed |= (uint32_t)(uint8_t)qv[q] << (8 * q);
+              const uint32_t r = requant_bits(y);  // half to even, saturated
+              qv[q] = (int8_t)(uint8_t)r;
+              packed |= (r & 0xffu) << (8 * q);
             }
             if (full && p.vec_q) {
               store4_nt(dst, packed);
@@ -1511,9 +1523,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
               const int32_t c = (int32_t)(vv[q] - ccorr[q] - rcorr + kzz);
               const float t = (float)c * sc[q];  // separately rounded: built with -ffp-contract=off
               const float y = t + bi[q];
-              float r = __builtin_rintf(y);      // half to even
-              r = fminf(fmaxf(r, -128.f), 127.f);
-              qi[q] = (int)r;
+              qi[q] = (int)requant_bits(y);      // half to even, saturated, in the low byte
             }
             const uint32_t lo = __builtin_amdgcn_perm((uint32_t)qi[1], (uint32_t)qi[0], 0x0c0c0400u);
             const uint32_t hi = __builtin_amdgcn_perm((uint32_t)qi[3], (uint32_t)qi[2], 0x04000c0cu);

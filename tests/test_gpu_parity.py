@@ -324,6 +324,30 @@ def test_qconv_requant_whole_tiles(igc, oracle, v, Nb, HW, zA, zB):
     assert np.array_equal(got["Q"], ref)
 
 
+# Requantize rounding at exact halves: scale 0.5 and bias 0 put every odd
+# accumulator on a tie (round half to even), and 127.5 / -128.5 at the
+# saturation bounds; whole tiles (the in-register path) and edge tiles (the
+# staged path).
+@pytest.mark.parametrize("v,M,N", [(0, 256, 256), (4, 448, 256), (0, 260, 250)])
+def test_u8i8_requant_ties_to_even(igc, oracle, v, M, N):
+    K = 16
+    rng = np.random.default_rng(M + N + v)
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    scale = np.full(N, 0.5, np.float32)
+    bias = np.zeros(N, np.float32)
+    igc.set_tuning(v, 1)
+    try:
+        got = run_u8i8(igc, A, 128, Bt, 0, outputs=("Q",), scale=scale, bias=bias)
+    finally:
+        igc.set_tuning(-1, 1)
+    C = oracle.gemm_u8i8_naive(A, 128, Bt, 0)
+    ref = oracle.requant(C, scale, bias)
+    assert np.count_nonzero((C % 2 == 1) & (np.abs(C) < 256)) > C.size // 10  # ties, unsaturated
+    assert np.count_nonzero(np.isin(C, (255, -257))) > 0  # 127.5 and -128.5
+    assert np.array_equal(got["Q"], ref)
+
+
 @pytest.mark.parametrize("K", [33024, 33025])
 def test_u8i8_extreme_values_at_overflow_bound(igc, oracle, K):
     # |C| = 255 * 255 * K reaches 2,147,450,625 at K = 33025 (just below 2^31).
