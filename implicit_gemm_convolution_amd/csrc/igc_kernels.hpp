@@ -1101,12 +1101,12 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     constexpr int NV = (INT8 ? 4 : 0) + ((!MSUMS && (SUMS & SUM_ROWS)) ? 4 : 0) +
                        ((!MSUMS && (SUMS & SUM_COLS)) ? 4 * ((FN + FM - 1) / FM) : 0);
     // u8 without v_dot4 sums: the conversion of the next chunk's fragment
-    // goes between the row's last two MFMAs (fenced), so the reads issued
+    // goes before the row's last two MFMAs (fenced), so the reads issued
     // early in the chunk have it to land before the conversion waits for
-    // them, and the last MFMA covers the conversion's latency.  (Left to the
-    // scheduler, the conversion followed the first read, behind an LDS wait
-    // two MFMAs into the chunk.)
-    constexpr bool LATE_X = INT8 && NV == 4 && FN >= 4;
+    // them, and two MFMAs cover the conversion's latency before the next
+    // chunk reads it.  (Left to the scheduler, the conversion followed the
+    // first read, behind an LDS wait two MFMAs into the chunk.)
+    constexpr bool LATE_X = INT8 && NV == 4 && FN >= 4 && FN - 2 > 2;
     uint4 axn = a_up;
     auto convert = [&]() {
       if constexpr (INT8) {
@@ -1119,15 +1119,16 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     };
     if constexpr (LATE_X) {
 #pragma unroll
-      for (int j = 1; j < FN - 1; ++j) Mfma<KIND, MB>::run(acc[c][j], b[j], ac);
+      for (int j = 1; j < FN - 2; ++j) Mfma<KIND, MB>::run(acc[c][j], b[j], ac);
 #pragma unroll
-      for (int q = 1; q < FN - 1; ++q) {
+      for (int q = 1; q < FN - 2; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         if (q <= nrd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       }
       __builtin_amdgcn_sched_barrier(0);
       convert();
       __builtin_amdgcn_sched_barrier(0);
+      Mfma<KIND, MB>::run(acc[c][FN - 2], b[FN - 2], ac);
       Mfma<KIND, MB>::run(acc[c][FN - 1], b[FN - 1], ac);
     } else {
       convert();
