@@ -30,4 +30,5 @@ from .binding import (  # noqa: F401
     load,
     set_tuning,
     status_string,
+    u8i8_colsum,
 )

@@ -32,6 +32,7 @@ EXPORTED = ("gemm_f16f32", "gemm_u8i8_zp", "conv2d_implicit_gemm", "conv2d_u8i8_
             "gemm_f16f32_workspace_size", "gemm_u8i8_zp_workspace_size",
             "conv2d_implicit_gemm_workspace_size", "conv2d_u8i8_zp_workspace_size",
             "gemm_f16f32_noalloc", "conv2d_implicit_gemm_nhwcnc", "conv2d_implicit_gemm_nhwcnc_workspace_size",
+            "u8i8_colsum",
             "igc_status_string", "igc_last_error", "igc_device_check", "igc_set_tuning")
 
 
@@ -55,6 +56,7 @@ class Epilogue(ctypes.Structure):
         ("bias_n", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("ws_bytes", ctypes.c_size_t),
+        ("colsum_B", ctypes.c_void_p),
     ]
 
 
@@ -96,6 +98,8 @@ def load() -> ctypes.CDLL:
                  "conv2d_implicit_gemm_nhwcnc_workspace_size"):
         getattr(L, name).argtypes = [i] * 11 + [pz]
         getattr(L, name).restype = i
+    L.u8i8_colsum.argtypes = [i, i, p, i, p, p]
+    L.u8i8_colsum.restype = i
     L.igc_set_tuning.argtypes = [i, i]
     L.igc_set_tuning.restype = i
     L.igc_status_string.argtypes = [i]
@@ -208,11 +212,18 @@ def gemm_f16f32_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream=None, *, check=T
     return _check(st, "gemm_f16f32_noalloc") if check else st
 
 
+def u8i8_colsum(N, K, B, ldb, colsum, stream=None, *, check=True) -> int:
+    """colsum[n] = sum_k B[n*ldb + k] (int32), for the colsum_B argument."""
+    st = load().u8i8_colsum(N, K, _addr(B), ldb, _addr(colsum), _stream(stream))
+    return _check(st, "u8i8_colsum") if check else st
+
+
 def gemm_u8i8_zp(M, N, K, A, lda, zA, B, ldb, zB, *, C_i32=None, ldc=0, D_f32=None, ldd=0,
                  dq_scale=0.0, Q_i8=None, ldq=0, scale_n=None, bias_n=None, stream=None,
-                 workspace=None, ws_bytes=None, check=True) -> int:
+                 workspace=None, ws_bytes=None, colsum_B=None, check=True) -> int:
     ep = Epilogue(_addr(C_i32), ldc, _addr(D_f32), ldd, float(dq_scale), _addr(Q_i8), ldq,
-                  _addr(scale_n), _addr(bias_n), _addr(workspace), _ws_bytes(workspace, ws_bytes))
+                  _addr(scale_n), _addr(bias_n), _addr(workspace), _ws_bytes(workspace, ws_bytes),
+                  _addr(colsum_B))
     st = load().gemm_u8i8_zp(M, N, K, _addr(A), lda, zA, _addr(B), ldb, zB, ctypes.byref(ep),
                              _stream(stream))
     return _check(st, "gemm_u8i8_zp") if check else st
@@ -238,9 +249,10 @@ def conv2d_implicit_gemm_nhwcnc(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad
 def conv2d_u8i8_zp(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, x, zA, w, zB, *,
                    C_i32=None, ldc=0, D_f32=None, ldd=0, dq_scale=0.0, Q_i8=None, ldq=0,
                    scale_n=None, bias_n=None, stream=None, workspace=None, ws_bytes=None,
-                   check=True) -> int:
+                   colsum_B=None, check=True) -> int:
     ep = Epilogue(_addr(C_i32), ldc, _addr(D_f32), ldd, float(dq_scale), _addr(Q_i8), ldq,
-                  _addr(scale_n), _addr(bias_n), _addr(workspace), _ws_bytes(workspace, ws_bytes))
+                  _addr(scale_n), _addr(bias_n), _addr(workspace), _ws_bytes(workspace, ws_bytes),
+                  _addr(colsum_B))
     st = load().conv2d_u8i8_zp(Nb, H, W, C, Kout, R, S, stride_h, stride_w, pad_h, pad_w, _addr(x), zA,
                                _addr(w), zB, ctypes.byref(ep), _stream(stream))
     return _check(st, "conv2d_u8i8_zp") if check else st

@@ -135,6 +135,7 @@ int check_epilogue(const igc_u8i8_epilogue* ep, int N, int K) {
     if (ep->ldq < N) return fail(IGC_EINVAL, "ldq=%d < N=%d", ep->ldq, N);
     if (!ep->scale_n || !ep->bias_n) return fail(IGC_EINVAL, "Q_i8 needs scale_n and bias_n");
   }
+  if ((reinterpret_cast<uintptr_t>(ep->colsum_B) & 3u) != 0) return fail(IGC_EINVAL, "colsum_B is not 4-byte aligned");
   return IGC_OK;
 }
 
@@ -142,6 +143,7 @@ void epilogue_params(igc::Params& p, const igc_u8i8_epilogue* ep) {
   p.Ci = ep->C_i32; p.ldci = ep->ldc;
   p.D = ep->D_f32; p.ldd = ep->ldd; p.dq = ep->dq_scale;
   p.Qo = ep->Q_i8; p.ldq = ep->ldq; p.scale = ep->scale_n; p.bias = ep->bias_n;
+  p.colsum = ep->colsum_B;
   p.vec_c = aligned16(ep->C_i32) && ep->ldc % 4 == 0;
   p.vec_d = aligned16(ep->D_f32) && ep->ldd % 4 == 0;
   p.vec_q = (reinterpret_cast<uintptr_t>(ep->Q_i8) & 3u) == 0 && ep->ldq % 4 == 0;
@@ -157,7 +159,13 @@ int plan_and_launch(igc::Params& p, bool fast, void* ws, size_t ws_bytes, hipStr
   if (int s = check_workspace(pl, ws, ws_bytes)) return s;
   apply_plan(p, pl, ws);
   if constexpr (KIND == igc::KIND_U8I8_GEMM || KIND == igc::KIND_U8I8_CONV) {
-    if (req_tiles(p, pl, fast)) return launch<KIND, SUMS | igc::REQ_TILES>(p, pl, fast, stream);
+    if (req_tiles(p, pl, fast)) {
+      // the caller's column sums replace the K loop's
+      if constexpr ((SUMS & igc::SUM_COLS) != 0)
+        if (p.colsum)
+          return launch<KIND, (SUMS & igc::SUM_ROWS) | igc::REQ_TILES | igc::COLS_IN>(p, pl, fast, stream);
+      return launch<KIND, SUMS | igc::REQ_TILES>(p, pl, fast, stream);
+    }
   }
   return launch<KIND, SUMS>(p, pl, fast, stream);
 }
@@ -205,6 +213,33 @@ int scratch_address(int dev, void** out) {
 __global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* p, int n) {
   const int i = (int)(blockIdx.x * 256 + threadIdx.x);
   if (i < n) p[i] = 0u;
+}
+
+// Column sums of an int8 operand stored as N rows of K ([GEMM-TVM] §2.3, the
+// zA * colsum(B) term): one wave per row, each lane summing every 64th
+// 16-byte chunk (aligned rows) or every 64th byte, then a reduction across
+// the wave.
+__global__ void __launch_bounds__(256) i8_colsum_kernel(const int8_t* __restrict__ B, int ldb, int N, int K,
+                                                        int32_t* __restrict__ out) {
+  const int n = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (n >= N) return;
+  const int8_t* row = B + (long long)n * ldb;
+  int s = 0;
+  if ((reinterpret_cast<uintptr_t>(row) & 15u) == 0 && K % 16 == 0) {
+    for (int k = lane * 16; k < K; k += 64 * 16) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + k);
+      s = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, s, false);
+      s = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, s, false);
+      s = __builtin_amdgcn_sdot4((int)v.z, 0x01010101, s, false);
+      s = __builtin_amdgcn_sdot4((int)v.w, 0x01010101, s, false);
+    }
+  } else {
+    for (int k = lane; k < K; k += 64) s += row[k];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) out[n] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -384,6 +419,22 @@ int gemm_u8i8_zp_workspace_size(int M, int N, int K, size_t* bytes) {
   g_last_error[0] = 0;
   if (M < 0 || N < 0 || K < 0) return fail(IGC_EINVAL, "negative size M=%d N=%d K=%d", M, N, K);
   return query_workspace(igc::KIND_U8I8_GEMM, M, N, K, bytes);
+}
+
+int u8i8_colsum(int N, int K, const int8_t* B, int ldb, int32_t* colsum, void* stream) {
+  g_last_error[0] = 0;
+  if (N < 0 || K < 0) return fail(IGC_EINVAL, "negative size N=%d K=%d", N, K);
+  if (ldb < K) return fail(IGC_EINVAL, "ldb=%d < K=%d", ldb, K);
+  if (K > 33025) return fail(IGC_EOVERFLOW, "K=%d > 33025", K);
+  if (N == 0) return IGC_OK;
+  if (!colsum || (!B && K > 0)) return fail(IGC_EINVAL, "B or colsum is NULL");
+  int dev;
+  if (int s = check_device(&dev)) return s;
+  hipLaunchKernelGGL(i8_colsum_kernel, dim3((unsigned)((N + 3) / 4)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     B, ldb, N, K, colsum);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return IGC_OK;
 }
 
 int gemm_u8i8_zp(int M, int N, int K, const uint8_t* A, int lda, int zA, const int8_t* B, int ldb,

@@ -266,7 +266,8 @@ inline bool req_tiles(const igc::Params& p, const Plan& pl, bool fast) {
 
 // The (kind, variant) pairs the C ABI launches: the fp16 kinds without
 // sums (the convolutions also with BLK_OUT), the u8 x i8 kinds with each
-// subset of SUM_ROWS | SUM_COLS, alone and with REQ_TILES.
+// subset of SUM_ROWS | SUM_COLS, alone and with REQ_TILES, and REQ_TILES
+// with the caller's column sums (COLS_IN, with or without SUM_ROWS).
 #define IGC_LAUNCH_KINDS(X)         \
   X(0, igc::KIND_F16_GEMM, 0)       \
   X(1, igc::KIND_F16_CONV, 0)       \
@@ -288,7 +289,11 @@ inline bool req_tiles(const igc::Params& p, const Plan& pl, bool fast) {
   X(17, igc::KIND_U8I8_CONV, 6)     \
   X(18, igc::KIND_U8I8_CONV, 7)     \
   X(19, igc::KIND_F16_CONV, 8)      \
-  X(20, igc::KIND_F16_CONV_C64, 8)
+  X(20, igc::KIND_F16_CONV_C64, 8)  \
+  X(21, igc::KIND_U8I8_GEMM, 20)    \
+  X(22, igc::KIND_U8I8_GEMM, 21)    \
+  X(23, igc::KIND_U8I8_CONV, 20)    \
+  X(24, igc::KIND_U8I8_CONV, 21)
 
 #define IGC_EXTERN_LAUNCH(n, K, S) \
   extern template int launch<K, S>(const igc::Params&, const Plan&, bool, hipStream_t);

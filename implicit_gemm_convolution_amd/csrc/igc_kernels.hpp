@@ -135,6 +135,7 @@ struct Params {
   long long ldq;
   const float* scale;
   const float* bias;
+  const int32_t* colsum;  // optional precomputed colsum(B) (length N)
   // 16-byte (int8: 4-byte) vector stores allowed for each output
   int vec_c, vec_d, vec_q;
   // Work split.  Workgroups [0, dp_tiles) each compute one whole tile.  The
@@ -847,7 +848,9 @@ __device__ __forceinline__ void lds_barrier() {
 //  with its requantize-in-registers path alone (with the staged path beside
 //  it, the 256-column integer tiles spill registers).  fp16 convolution:
 //  BLK_OUT writes the output in the blocked NHWCnc layout (the launch's
-//  p.blk), so the row-major kernels carry no blocked code.
+//  p.blk), so the row-major kernels carry no blocked code.  u8 x i8:
+//  COLS_IN (with REQ_TILES) takes colsum(B) from p.colsum instead of forming
+//  it in the K loop (SUM_COLS then not set).
 //  DEPTH: K tiles in flight ahead of the one being multiplied.  A has
 //  DEPTH + 1 LDS stages; B has 2 at DEPTH 2 (the 160 KiB of LDS at 256 x 256)
 //  and DEPTH + 1 otherwise.  Every launch uses DEPTH 2: deeper rings for the
@@ -855,12 +858,13 @@ __device__ __forceinline__ void lds_barrier() {
 //  MI355X, whose small launches are bound by fixed costs and a low clock,
 //  not by load latency.
 // ---------------------------------------------------------------------------
-constexpr int SUM_ROWS = 1, SUM_COLS = 2, REQ_TILES = 4, BLK_OUT = 8;
+constexpr int SUM_ROWS = 1, SUM_COLS = 2, REQ_TILES = 4, BLK_OUT = 8, COLS_IN = 16;
 template <int KIND, int BM, int BN, int WM, int WN, bool FAST, int VAR = 0, int DEPTH = 2>
 __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr int SUMS = VAR & (SUM_ROWS | SUM_COLS);
   constexpr bool REQ = (VAR & REQ_TILES) != 0;
   constexpr bool BLKO = (VAR & BLK_OUT) != 0;
+  constexpr bool CIN = (VAR & COLS_IN) != 0;
   constexpr int NT = 64 * WM * WN;
   constexpr bool INT8 = KIND == KIND_U8I8_GEMM || KIND == KIND_U8I8_CONV;
   constexpr int EB = INT8 ? 1 : 2;
@@ -879,6 +883,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   constexpr bool SK = INT8 ? (BM <= 128 && FAST && !REQ) : (SUMS == 0);
   static_assert(!REQ || (INT8 && FAST), "whole requantize-only tiles: the aligned integer kernels");
   static_assert(!BLKO || !INT8, "blocked output: the fp16 convolution");
+  static_assert(!CIN || (REQ && (SUMS & SUM_COLS) == 0), "precomputed column sums: whole requantize-only tiles");
   // (the im2col operand walks K in order, so the conv's B does too)
   constexpr bool CONV = KIND == KIND_F16_CONV || KIND == KIND_F16_CONV_C64 || KIND == KIND_U8I8_CONV;
   // u8 activations through the uniform-tap loader (padding stored as zA by
@@ -1355,8 +1360,9 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       }
     }
   }
-  // (nonzero only when both zA' and zB are, i.e. with both sums compiled)
-  if constexpr (INT8 && SUMS == (SUM_ROWS | SUM_COLS)) kzz = (uint32_t)p.K * (uint32_t)p.zAp * (uint32_t)p.zB;
+  // (nonzero only when both zA' and zB are, i.e. with both sums in use)
+  if constexpr (INT8 && (SUMS & SUM_ROWS) != 0 && ((SUMS & SUM_COLS) != 0 || CIN))
+    kzz = (uint32_t)p.K * (uint32_t)p.zAp * (uint32_t)p.zB;
 
   constexpr int GPR = BN / 4;    // 4-column groups per row
   constexpr int RPP = NT / GPR;  // rows per pass of the whole workgroup
@@ -1506,7 +1512,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           float sc[4], bi[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            ccorr[q] = ((SUMS & SUM_COLS) != 0 && p.zAp != 0) ? (uint32_t)p.zAp * (uint32_t)sums[BM + lc + q] : 0u;
+            if constexpr (CIN)
+              ccorr[q] = (uint32_t)p.zAp * (uint32_t)p.colsum[n0 + lc + q];
+            else
+              ccorr[q] = ((SUMS & SUM_COLS) != 0 && p.zAp != 0) ? (uint32_t)p.zAp * (uint32_t)sums[BM + lc + q] : 0u;
             sc[q] = p.scale[n0 + lc + q];
             bi[q] = p.bias[n0 + lc + q];
           }

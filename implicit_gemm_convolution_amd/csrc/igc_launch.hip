@@ -69,5 +69,17 @@ template int launch<igc::KIND_F16_CONV, 8>(const igc::Params&, const Plan&, bool
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 20
 template int launch<igc::KIND_F16_CONV_C64, 8>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 21
+template int launch<igc::KIND_U8I8_GEMM, 20>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 22
+template int launch<igc::KIND_U8I8_GEMM, 21>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 23
+template int launch<igc::KIND_U8I8_CONV, 20>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 24
+template int launch<igc::KIND_U8I8_CONV, 21>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
 
 }  // namespace igc_host

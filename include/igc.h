@@ -129,6 +129,16 @@ int gemm_f16f32_noalloc(int M, int N, int K,
  *   workspace,      optional caller-owned workspace (see the conventions above
  *   ws_bytes        and gemm_u8i8_zp_workspace_size); NULL / 0 for none.
  *
+ *   colsum_B        optional int32 device vector of length N holding
+ *                   colsum(B)[n] = sum_k B[k,n] (the weights' column sums,
+ *                   for static weights computed once with u8i8_colsum), 4-byte
+ *                   aligned; NULL to have the kernel form the sums it needs
+ *                   itself.  Where a launch can use it (zA != 128, whole
+ *                   tiles, Q_i8 the only output, no split) the K loop forms
+ *                   no column sums; elsewhere it is not read.  The results
+ *                   are those of the definition either way, provided the
+ *                   vector holds the column sums of this call's B.
+ *
  * Int -> fp32 conversions round to nearest even; the two fp32 operations of
  * the requantize step are separately rounded (no fused multiply-add).
  */
@@ -144,6 +154,7 @@ typedef struct igc_u8i8_epilogue {
   const float* bias_n;
   void* workspace;
   size_t ws_bytes;
+  const int32_t* colsum_B;
 } igc_u8i8_epilogue;
 
 /*
@@ -174,6 +185,24 @@ int gemm_u8i8_zp(int M, int N, int K,
 
 /* gemm_u8i8_zp_workspace_size -- as gemm_f16f32_workspace_size, for gemm_u8i8_zp. */
 int gemm_u8i8_zp_workspace_size(int M, int N, int K, size_t* bytes);
+
+/*
+ * u8i8_colsum -- the column sums of an int8 B operand, for the colsum_B
+ * field of igc_u8i8_epilogue: colsum[n] = sum_k B[n*ldb + k] for n < N, in
+ * int32 (exact for K <= 33025 * 2, far beyond the K the GEMM accepts).
+ *
+ * Definition: [GEMM-TVM] §2.3: the zero-point term zA * colsum(B) of the
+ * four-term expansion; B is the weight operand, fixed across calls, so its
+ * sums can be formed once.  For the convolution B is the KRSC weight tensor
+ * (N = Kout rows of K = R*S*C, ldb = K).
+ *
+ *   B       int8, N rows of K (column-major K x N): B[n*ldb + k], ldb >= K.
+ *   colsum  int32 device vector of length N, written on `stream`.
+ *
+ * Errors: IGC_EINVAL (negative size, ldb < K, NULL pointer with N > 0),
+ * IGC_EOVERFLOW (K > 33025), IGC_ENODEV, IGC_EHIP.
+ */
+int u8i8_colsum(int N, int K, const int8_t* B, int ldb, int32_t* colsum, void* stream);
 
 /*
  * conv2d_implicit_gemm -- 2-D convolution (cross-correlation, no filter flip),

@@ -76,7 +76,8 @@ DESCRIPTIONS = {
           "(GEMM M=50176 N=512 K=2304)",
     "c5": "gemm_u8i8_zp M=N=K=8192, zA=128 zB=0, per-channel scale+bias, RNE int8 requant",
     "q4": "conv2d_u8i8_zp NHWC 256x14x14x256 u8 (zA=100) * KRSC 512x3x3x256 i8 (zB=0), s1 p1, "
-          "per-channel scale+bias, RNE int8 requant (GEMM M=50176 N=512 K=2304)",
+          "per-channel scale+bias, RNE int8 requant (GEMM M=50176 N=512 K=2304); the weights' column sums "
+          "formed once (u8i8_colsum, static weights) and passed as colsum_B",
     "b4": "conv2d_implicit_gemm_nhwcnc blocked NHWCnc x (16,14,14,16,16,16) * w (3,3,16,32,16,16), s1 p1, "
           "fp16 in, fp32 out (the 256x14x14 conv in the tutorial's layout; GEMM M=50176 N=512 K=2304)",
 }

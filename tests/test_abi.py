@@ -108,6 +108,22 @@ def test_gemm_u8i8_validation(igc):
     assert f(M=0) == igc.IGC_OK
     st = igc.load().gemm_u8i8_zp(4, 4, 16, 1, 16, 128, 1, 16, 0, None, None)
     assert st == E                                     # NULL epilogue descriptor
+    assert f(colsum_B=0x1002) == E                     # colsum_B not 4-byte aligned
+
+
+def test_colsum_validation(igc):
+    E = igc.IGC_EINVAL
+
+    def f(N=4, K=16, B=16, ldb=16, out=16):
+        return igc.u8i8_colsum(N, K, B, ldb, out, check=False)
+
+    assert f(N=-1) == E
+    assert f(K=-1) == E
+    assert f(ldb=15) == E
+    assert f(B=None) == E
+    assert f(out=None) == E
+    assert f(K=33026, ldb=33026) == igc.IGC_EOVERFLOW
+    assert f(N=0, B=None, out=None) == igc.IGC_OK
 
 
 def test_conv_validation(igc):
@@ -215,6 +231,7 @@ def test_valid_call_without_gpu_reports_nodev(igc):
     except ImportError:
         pass
     assert igc.gemm_f16f32(4, 4, 8, 16, 8, 16, 8, 16, 4, check=False) == igc.IGC_ENODEV
+    assert igc.u8i8_colsum(4, 16, 16, 16, 16, check=False) == igc.IGC_ENODEV
     assert igc.device_check() == igc.IGC_ENODEV
     out = ctypes.c_size_t(0)
     assert igc.load().gemm_f16f32_workspace_size(4096, 4096, 4096, ctypes.byref(out)) == igc.IGC_ENODEV

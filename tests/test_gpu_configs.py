@@ -159,9 +159,11 @@ def test_c4_streamk_sampled_pixels(igc, oracle):
     assert report(f"c4 stream-K, {len(pix)} sampled pixels", y[pix], ref) <= FP_TOL
 
 
-def test_q4_full(igc, oracle):
+@pytest.mark.parametrize("precomputed_colsum", [True, False])
+def test_q4_full(igc, oracle, precomputed_colsum):
     """The quantized convolution at the 256x14x14 conv shape, requantized
-    int8, on every output."""
+    int8, on every output: with the weights' column sums formed once and
+    passed in (as the benchmark runs it), and formed in the K loop."""
     import torch
 
     wl = synth.workload("q4")
@@ -174,8 +176,13 @@ def test_q4_full(igc, oracle):
     dQ = empty_dev((M, N), torch.int8)
     dS, dBi = to_dev(scale), to_dev(bias)
     dx, dw = to_dev(x), to_dev(w)
+    cs = None
+    if precomputed_colsum:
+        Kd = d["R"] * d["S"] * d["C"]
+        cs = empty_dev((N,), torch.int32)
+        igc.u8i8_colsum(N, Kd, dw, Kd, cs)
     igc.conv2d_u8i8_zp(*dims, dx, pr["zA"], dw, pr["zB"], Q_i8=dQ, ldq=N, scale_n=dS, bias_n=dBi,
-                       workspace=workspace_for(igc.conv2d_u8i8_zp_workspace_size(*dims)))
+                       workspace=workspace_for(igc.conv2d_u8i8_zp_workspace_size(*dims)), colsum_B=cs)
     Q = to_host(dQ)
     C = oracle.conv2d_u8i8_direct_at(x, pr["zA"], w, pr["zB"], np.arange(M), (1, 1), (1, 1))
     ref = oracle.requant(C, scale, bias)

@@ -179,7 +179,7 @@ def test_f16_k_zero_and_empty(igc):
 
 # ----------------------------------------------------------------- u8 x i8
 def run_u8i8(igc, A, zA, Bt, zB, outputs=("C", "D", "Q"), scale=None, bias=None, dq=0.0,
-             lda=None, ldb=None):
+             lda=None, ldb=None, colsum_B=None):
     import torch
 
     M, K = A.shape
@@ -189,7 +189,7 @@ def run_u8i8(igc, A, zA, Bt, zB, outputs=("C", "D", "Q"), scale=None, bias=None,
     dA = to_dev(strided(A, lda))
     dB = to_dev(strided(Bt, ldb))
     out = {}
-    kw = dict(dq_scale=dq)
+    kw = dict(dq_scale=dq, colsum_B=colsum_B)
     if "C" in outputs:
         out["C"] = empty_dev((M, N), torch.int32)
         kw.update(C_i32=out["C"], ldc=N)
@@ -346,6 +346,67 @@ def test_u8i8_requant_ties_to_even(igc, oracle, v, M, N):
     assert np.count_nonzero((C % 2 == 1) & (np.abs(C) < 256)) > C.size // 10  # ties, unsaturated
     assert np.count_nonzero(np.isin(C, (255, -257))) > 0  # 127.5 and -128.5
     assert np.array_equal(got["Q"], ref)
+
+
+def test_u8i8_colsum(igc, oracle):
+    import torch
+
+    for N, K, ldb in [(512, 2304, 2304), (37, 1000, 1003), (3, 1, 1), (256, 33025, 33025)]:
+        rng = np.random.default_rng(N + K)
+        Bt = synth.i8_uniform(rng, (N, K))
+        dB = to_dev(strided(Bt, ldb))
+        out = empty_dev((N,), torch.int32)
+        igc.u8i8_colsum(N, K, dB, ldb, out)
+        assert np.array_equal(to_host(out).astype(np.int64), oracle.i8_colsum(Bt))
+
+
+# The caller's column sums (colsum_B): used by whole requantize-only tiles
+# (the kernels then form no column sums), ignored elsewhere; the results are
+# the same either way.
+@pytest.mark.parametrize("v,M,N,outputs", [(0, 512, 512, ("Q",)), (4, 448, 256, ("Q",)),
+                                           (0, 520, 300, ("Q",)), (4, 448, 256, ("C", "Q")),
+                                           (1, 512, 512, ("Q",))])
+@pytest.mark.parametrize("zA,zB", [(37, 0), (200, -5), (128, 3)])
+def test_u8i8_precomputed_colsum(igc, oracle, v, M, N, outputs, zA, zB):
+    import torch
+
+    K = 384
+    rng = np.random.default_rng(M + N + zA + v)
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = synth.i8_uniform(rng, (N, K))
+    scale, bias = q_params(rng, N, K)
+    cs = empty_dev((N,), torch.int32)
+    igc.u8i8_colsum(N, K, to_dev(Bt), K, cs)
+    igc.set_tuning(v, 1)
+    try:
+        got = run_u8i8(igc, A, zA, Bt, zB, outputs=outputs, scale=scale, bias=bias, colsum_B=cs)
+    finally:
+        igc.set_tuning(-1, 1)
+    C = oracle.gemm_u8i8_naive(A, zA, Bt, zB)
+    assert np.array_equal(got["Q"], oracle.requant(C, scale, bias))
+    if "C" in outputs:
+        assert np.array_equal(got["C"].astype(np.int64), C)
+
+
+@pytest.mark.parametrize("v,Nb,HW", [(4, 7, 8), (-1, 4, 14)])
+@pytest.mark.parametrize("zA,zB", [(100, 0), (0, 3)])
+def test_qconv_precomputed_colsum(igc, oracle, v, Nb, HW, zA, zB):
+    import torch
+
+    C, Kout, R, S = 128, 256, 3, 3
+    rng = np.random.default_rng(v + zA + zB + 7)
+    x = synth.u8_uniform(rng, (Nb, HW, HW, C))
+    w = synth.i8_uniform(rng, (Kout, R, S, C))
+    scale, bias = q_params(rng, Kout, R * S * C)
+    cs = empty_dev((Kout,), torch.int32)
+    igc.u8i8_colsum(Kout, R * S * C, to_dev(w), R * S * C, cs)
+    igc.set_tuning(v, 1)
+    try:
+        got = run_qconv(igc, x, zA, w, zB, (1, 1), (1, 1), outputs=("Q",), scale=scale, bias=bias, colsum_B=cs)
+    finally:
+        igc.set_tuning(-1, 1)
+    C32 = oracle.conv2d_u8i8_direct_at(x, zA, w, zB, np.arange(Nb * HW * HW), (1, 1), (1, 1))
+    assert np.array_equal(got["Q"], oracle.requant(C32, scale, bias))
 
 
 @pytest.mark.parametrize("K", [33024, 33025])
@@ -520,7 +581,7 @@ def test_streamk_workspace_contract(igc, oracle):
 
 
 # ----------------------------------------------------------------- quantized conv
-def run_qconv(igc, x, zA, w, zB, stride, pad, outputs=("C",), scale=None, bias=None, dq=0.0):
+def run_qconv(igc, x, zA, w, zB, stride, pad, outputs=("C",), scale=None, bias=None, dq=0.0, colsum_B=None):
     import torch
 
     Nb, H, W, C = x.shape
@@ -529,7 +590,7 @@ def run_qconv(igc, x, zA, w, zB, stride, pad, outputs=("C",), scale=None, bias=N
     Q = (W + 2 * pad[1] - S) // stride[1] + 1
     M = Nb * P * Q
     dx, dw = to_dev(x), to_dev(w)
-    out, kw = {}, dict(dq_scale=dq)
+    out, kw = {}, dict(dq_scale=dq, colsum_B=colsum_B)
     if "C" in outputs:
         out["C"] = empty_dev((M, Kout), torch.int32)
         kw.update(C_i32=out["C"], ldc=Kout)
