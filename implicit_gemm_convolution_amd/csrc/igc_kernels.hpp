@@ -1500,25 +1500,45 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
       uint8_t* const qs = sa0;     // the A stage arrays are contiguous
       auto qoff = [](int r, int c) { return r * BN + ((((c >> 4) ^ (r & (CQ - 1)))) << 4) + (c & 15); };
       if constexpr (SUMS != 0) __syncthreads();  // the published row / column sums
+      // Each group of 4 columns needs its scale and bias (and the caller's
+      // column sums) from memory: they are loaded one group ahead, so the
+      // loads of group t+1 are in flight while group t is requantized
+      // (loaded where used, every group waited out a load's full latency;
+      // loaded for all groups at once they spill registers).
+      constexpr int NG = FN * (NE / 4);  // column groups of a lane
+      auto group_col = [&](int t) { return wn * TN + (t / (NE / 4)) * MB + acc_col(4 * (t % (NE / 4))); };
+      float nsc[4], nbi[4];
+      int32_t ncs[4];
+      auto fetch = [&](int t) {
+        const int lc = group_col(t);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          nsc[q] = p.scale[n0 + lc + q];
+          nbi[q] = p.bias[n0 + lc + q];
+          if constexpr (CIN) ncs[q] = p.colsum[n0 + lc + q];
+        }
+      };
+      fetch(0);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int g4 = 0; g4 < NE / 4; ++g4) {
-          // (a scheduling fence per block column keeps its scale / bias loads
-          // here; hoisted for all columns at once they spill registers)
+          // (a scheduling fence per group keeps its loads one group ahead)
           __builtin_amdgcn_sched_barrier(0);
-          const int lc = wn * TN + j * MB + acc_col(4 * g4);  // tile column of the first of the 4
+          const int t = j * (NE / 4) + g4;
+          const int lc = group_col(t);  // tile column of the first of the 4
           uint32_t ccorr[4];
           float sc[4], bi[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             if constexpr (CIN)
-              ccorr[q] = (uint32_t)p.zAp * (uint32_t)p.colsum[n0 + lc + q];
+              ccorr[q] = (uint32_t)p.zAp * (uint32_t)ncs[q];
             else
               ccorr[q] = ((SUMS & SUM_COLS) != 0 && p.zAp != 0) ? (uint32_t)p.zAp * (uint32_t)sums[BM + lc + q] : 0u;
-            sc[q] = p.scale[n0 + lc + q];
-            bi[q] = p.bias[n0 + lc + q];
+            sc[q] = nsc[q];
+            bi[q] = nbi[q];
           }
+          if (t + 1 < NG) fetch(t + 1);
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
             const uint4 v = acc_quad(i, j, g4);
