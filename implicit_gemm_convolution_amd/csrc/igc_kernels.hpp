@@ -681,7 +681,25 @@ struct Im2colC64Loader {
   int blk_shift;                // 4 blocked, 0 NHWC
   uint32_t wofs;                // this wave's offset in a tile's LDS rows
 
-  __device__ __forceinline__ void init(const Params& p, int m0, int kt0) {
+  // Output row m's entry in the tile's row table: the byte offset of its
+  // tap (0, 0) pixel from the buffer base, and its tap mask; zeros past M
+  // (no tap inside: every load of the row reads zeros).  rep: conv_tap_rows.
+  // Branch-free: the values it reads from the parameters must not become
+  // results of a divergent branch (the scalar K walk uses them).
+  __device__ static __forceinline__ uint2 row_entry(const Params& p, int m, uint32_t rep) {
+    const bool in = m < p.M;
+    m = in ? m : p.M - 1;
+    const int bs = (EB == 2 && p.blk) ? 4 : 0;
+    int n, h0, w0;
+    conv_row(p, bs ? (m >> 4) : m, n, h0, w0);
+    const int p0 = p.ph * p.W + p.pw;
+    const uint32_t nn_off = bs ? (uint32_t)((m & 15) * 16 * EB) : 0u;
+    const uint32_t pix = ((uint32_t)((n * p.H * p.W + h0 * p.W + w0 + p0) * p.C * EB) << bs) + nn_off;
+    const uint32_t mk = conv_tap_mask(p, h0, w0, rep);
+    return make_uint2(in ? pix : 0u, in ? mk : 0u);
+  }
+  // rows: the tile's row table (row_entry of rows m0 .. m0 + ROWS - 1)
+  __device__ __forceinline__ void init(const Params& p, const uint2* rows, int kt0) {
     wofs = Sh::wave_offset();
     C = p.C; S = p.S; RS = p.R * p.S;
     const int p0 = p.ph * p.W + p.pw;
@@ -689,23 +707,15 @@ struct Im2colC64Loader {
     rsrc = make_rsrc((const void*)((uintptr_t)p.A - ((uintptr_t)p0 * C * EB << blk_shift)), OOB);
     step = (uint32_t)(KT_BYTES << blk_shift);
     row_jump = (uint32_t)(((long long)(p.W - S) * C * EB) << blk_shift);
-    const uint32_t rep = conv_tap_rows(p);
     // chunk c of a 128-byte K-tile row (channels 8c .. 8c+7 of the tile):
     // byte 16c (NHWC), or 512 (c / 2) + 16 (c % 2) in the blocked layout
     const int ch = Sh::lane_chunk();
     const uint32_t chunk_off = blk_shift ? (uint32_t)((ch >> 1) * 512 + (ch & 1) * 16) : (uint32_t)(ch * CHUNK_BYTES);
 #pragma unroll
     for (int j = 0; j < Sh::NQ; ++j) {
-      const int m = m0 + Sh::lane_row() + j * 8 * Sh::NWAVES;
-      pixb[j] = 0;
-      mask[j] = 0;
-      if (m < p.M) {
-        int n, h0, w0;
-        conv_row(p, blk_shift ? (m >> 4) : m, n, h0, w0);
-        const uint32_t nn_off = blk_shift ? (uint32_t)((m & 15) * 16 * EB) : 0u;
-        pixb[j] = ((uint32_t)((n * p.H * p.W + h0 * p.W + w0 + p0) * C * EB) << blk_shift) + nn_off + chunk_off;
-        mask[j] = conv_tap_mask(p, h0, w0, rep);
-      }
+      const uint2 e = rows[Sh::lane_row() + j * 8 * Sh::NWAVES];
+      pixb[j] = e.x + chunk_off;
+      mask[j] = e.y;
     }
     const int k = kt0 * CPT;
     const int rs = (int)p.fd_c.div((uint32_t)k);
@@ -886,9 +896,11 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   static_assert(!CIN || (REQ && (SUMS & SUM_COLS) == 0), "precomputed column sums: whole requantize-only tiles");
   // (the im2col operand walks K in order, so the conv's B does too)
   constexpr bool CONV = KIND == KIND_F16_CONV || KIND == KIND_F16_CONV_C64 || KIND == KIND_U8I8_CONV;
-  // u8 activations through the uniform-tap loader (padding stored as zA by
-  // the loader itself)
+  // u8 activations through the uniform-tap loader (padded rows arrive as
+  // zeros and become zA - 128 in the fragment conversion)
   constexpr bool U8_UNIFORM_TAPS = KIND == KIND_U8I8_CONV && FAST;
+  // the uniform-tap loaders read their rows' im2col data from a table
+  constexpr bool ROW_TABLE = KIND == KIND_F16_CONV_C64 || U8_UNIFORM_TAPS;
   constexpr bool TAIL_FIRST = FAST && !CONV;
   typedef typename std::conditional<
       KIND == KIND_F16_CONV_C64 || U8_UNIFORM_TAPS, Im2colC64Loader<NT, BM, EB>,
@@ -965,8 +977,27 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   tile_coords<8>(p, t, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
+  // The uniform-tap conv loaders: each row's pixel offset and tap mask
+  // (integer divisions and a mask, some 50 instructions, a quarter of them
+  // quarter-rate multiplies) are formed once per tile, one row per thread,
+  // into a table in the last A stage, where every lane that loads or
+  // converts the row reads them (formed per lane, 7-14 rows each, they took
+  // 1.6-2.2 us per tile).  That stage's first loads are issued after the
+  // prologue's wait and barrier, so the table's reads are done by then.
+  const uint2* rows = nullptr;
+  if constexpr (ROW_TABLE) {
+    // (every thread writes an entry, rows m0 .. m0 + NT - 1: no branch)
+    static_assert(NT * (int)sizeof(uint2) <= SA_ALLOC && BM <= NT, "the row table fits one stage, one row per thread");
+    uint2* const tab = reinterpret_cast<uint2*>(sa_ring[RA - 1]);
+    if (!first_seg) __syncthreads();  // the previous segment's epilogue may still read LDS
+    tab[tid] = ALoader::row_entry(p, m0 + tid, conv_tap_rows(p));
+    __syncthreads();
+    rows = tab;
+  }
   ALoader la;
-  if constexpr (CONV) {
+  if constexpr (ROW_TABLE) {
+    la.init(p, rows, k0);
+  } else if constexpr (CONV) {
     la.init(p, m0, k0);
   } else {
     la.init(p.A, p.lda, m0, p.M, p.K);
@@ -1037,17 +1068,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   int xtap = 0, xleft = 1, xtpt = 1;  // tap of the K tile in use, its tiles left, tiles per tap
   if constexpr (U8_UNIFORM_TAPS) {
     xz = X80 ^ ((uint32_t)(uint8_t)(p.zAp + 128) * 0x01010101u);
-    const uint32_t rep = conv_tap_rows(p);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = m0 + wm * TM + i * MB + frow;
-      fmask[i] = 0;
-      if (m < p.M) {
-        int n, h0, w0;
-        conv_row(p, m, n, h0, w0);
-        fmask[i] = conv_tap_mask(p, h0, w0, rep);
-      }
-    }
+    for (int i = 0; i < FM; ++i) fmask[i] = rows[wm * TM + i * MB + frow].y;
     const int k = k0 * KT_BYTES;  // u8: one byte per channel
     xtap = (int)p.fd_c.div((uint32_t)k);
     xtpt = p.C / KT_BYTES;
