@@ -1541,6 +1541,16 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
         }
       };
       fetch(0);
+      // C = acc' - zA'*colsum(B) - zB*rowsum(A') + K*zA'*zB (wrapping; the
+      // true value fits in int32) as acc' + a row term + a column term: the
+      // row terms -zB*rowsum(A') once per fragment row, the column terms
+      // K*zA'*zB - zA'*colsum(B) once per group of 4 columns, so each value
+      // takes one three-operand add (formed per value, the terms and their
+      // row sums' LDS reads took a third of the epilogue's instructions).
+      uint32_t rterm[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        rterm[i] = ((SUMS & SUM_ROWS) != 0 && p.zB != 0) ? 0u - (uint32_t)p.zB * (uint32_t)sums[wm * TM + i * MB + arow] : 0u;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -1549,14 +1559,16 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           __builtin_amdgcn_sched_barrier(0);
           const int t = j * (NE / 4) + g4;
           const int lc = group_col(t);  // tile column of the first of the 4
-          uint32_t ccorr[4];
+          uint32_t cterm[4];
           float sc[4], bi[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
+            uint32_t ccorr;
             if constexpr (CIN)
-              ccorr[q] = (uint32_t)p.zAp * (uint32_t)ncs[q];
+              ccorr = (uint32_t)p.zAp * (uint32_t)ncs[q];
             else
-              ccorr[q] = ((SUMS & SUM_COLS) != 0 && p.zAp != 0) ? (uint32_t)p.zAp * (uint32_t)sums[BM + lc + q] : 0u;
+              ccorr = ((SUMS & SUM_COLS) != 0 && p.zAp != 0) ? (uint32_t)p.zAp * (uint32_t)sums[BM + lc + q] : 0u;
+            cterm[q] = kzz - ccorr;
             sc[q] = nsc[q];
             bi[q] = nbi[q];
           }
@@ -1565,14 +1577,11 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           for (int i = 0; i < FM; ++i) {
             const uint4 v = acc_quad(i, j, g4);
             const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-            const uint32_t rcorr =
-                ((SUMS & SUM_ROWS) != 0 && p.zB != 0) ? (uint32_t)p.zB * (uint32_t)sums[wm * TM + i * MB + arow] : 0u;
             int qi[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              // C = acc' - zA'*colsum(B) - zB*rowsum(A') + K*zA'*zB (wrapping;
-              // the true value fits in int32), then the requantize steps
-              const int32_t c = (int32_t)(vv[q] - ccorr[q] - rcorr + kzz);
+              // the corrected C, then the requantize steps
+              const int32_t c = (int32_t)(vv[q] + cterm[q] + rterm[i]);
               const float t = (float)c * sc[q];  // separately rounded: built with -ffp-contract=off
               const float y = t + bi[q];
               qi[q] = (int)requant_bits(y);      // half to even, saturated, in the low byte
