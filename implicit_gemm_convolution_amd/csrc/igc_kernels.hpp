@@ -1748,6 +1748,12 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   if constexpr (!SK) break;  // one whole tile per workgroup: no loop
   it += k1 - k0;
   first_seg = false;
+  // Every access of this segment is complete before the next one: the
+  // compiler then carries no load of the fix-up (mode 2) round this loop as
+  // outstanding (it did in some integer kernels, and waited for it inside
+  // the next segment's K loop, where the wait also drained the operand
+  // loads in flight every K tile).
+  wait_vmcnt_lgkm0<0>();
   }  // segments
 }
 

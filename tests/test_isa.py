@@ -219,3 +219,19 @@ def test_no_scc_read_across_asm(asm):
     compiled comparison is kept in SCC across one."""
     for name, (body, _) in asm.items():
         assert not scc_reads_after_asm(body), (name, scc_reads_after_asm(body)[:4])
+
+
+def test_no_compiler_vmcnt_wait_in_fast_main_loops(tiled):
+    """The K loop's memory waits are the kernel's own (vmcnt with lgkmcnt(0),
+    counting the direct-to-LDS loads in flight).  A wait the compiler inserts
+    there (for a load it still counts as outstanding, e.g. one carried round
+    the stream-K segment loop) would drain the operand loads every K tile."""
+    for name, (body, _) in tiled.items():
+        kind, bm, bn, fast = _params(name)
+        if not fast:
+            continue
+        lines = [l.split(";")[0].strip() for l in body.splitlines()]
+        lines = [l for l in lines if l and not l.startswith(".")]
+        mf = [i for i, l in enumerate(lines) if l.startswith("v_mfma")]
+        stray = [l for l in lines[mf[0]:mf[-1]] if l.startswith("s_waitcnt") and "vmcnt" in l and "lgkmcnt(0)" not in l]
+        assert not stray, (name, stray[:2])
