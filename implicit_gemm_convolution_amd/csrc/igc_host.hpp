@@ -214,22 +214,23 @@ int launch_variant(const igc::Params& p, const Plan& pl, hipStream_t stream) {
         if (pl.variant == V_256x256) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, pl, stream);
     }
     return fail(IGC_EUNSUPPORTED, "internal: variant %d has no whole-tile requantize-only kernel", pl.variant);
+  } else {
+    switch (pl.variant) {
+      case V_224x256:
+        if constexpr (FAST) return launch_one<KIND, 224, 256, 2, 2, FAST, SUMS>(p, pl, stream);
+        break;
+      case V_256x256:  // (not for the uniform-tap u8 convolution, see make_plan)
+        if constexpr (FAST && KIND != igc::KIND_U8I8_CONV) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, pl, stream);
+        break;
+      case V_256x128:
+        if constexpr (FAST) return launch_one<KIND, 256, 128, 2, 2, FAST, SUMS>(p, pl, stream);
+        break;
+      case V_128x128: return launch_one<KIND, 128, 128, 2, 2, FAST, SUMS>(p, pl, stream);
+      case V_64x64: return launch_one<KIND, 64, 64, 2, 2, FAST, SUMS>(p, pl, stream);
+      default: break;
+    }
+    return fail(IGC_EUNSUPPORTED, "internal: variant %d not compiled for this operand form", pl.variant);
   }
-  switch (pl.variant) {
-    case V_224x256:
-      if constexpr (FAST) return launch_one<KIND, 224, 256, 2, 2, FAST, SUMS>(p, pl, stream);
-      break;
-    case V_256x256:  // (not for the uniform-tap u8 convolution, see make_plan)
-      if constexpr (FAST && KIND != igc::KIND_U8I8_CONV) return launch_one<KIND, 256, 256, 2, 2, FAST, SUMS>(p, pl, stream);
-      break;
-    case V_256x128:
-      if constexpr (FAST) return launch_one<KIND, 256, 128, 2, 2, FAST, SUMS>(p, pl, stream);
-      break;
-    case V_128x128: return launch_one<KIND, 128, 128, 2, 2, FAST, SUMS>(p, pl, stream);
-    case V_64x64: return launch_one<KIND, 64, 64, 2, 2, FAST, SUMS>(p, pl, stream);
-    default: break;
-  }
-  return fail(IGC_EUNSUPPORTED, "internal: variant %d not compiled for this operand form", pl.variant);
 }
 
 inline int launch_bypass(const igc::Params& p, const Plan& pl, hipStream_t stream) {
