@@ -653,8 +653,8 @@ __device__ __forceinline__ uint32_t conv_tap_mask(const Params& p, int h0, int w
 // load's scalar offset.  In NHWC that position grows by 128 bytes per K tile
 // (tap (r, s+1) channel 0 follows tap (r, s) channel C-1 in memory), plus
 // (W - S)*C elements when the walk moves to the next filter row, so a K tile
-// costs a few scalar additions.  Each row keeps a bit mask of the taps that
-// fall inside the image (the zero padding); once per tap the per-lane offset
+// costs a few scalar additions.  Each row keeps a bit mask of its taps that
+// fall in the zero padding; once per tap the per-lane offset
 // becomes OOB where the tap is padding, so that lane's load reads zeros.
 // The buffer spans 2^31 bytes (OOB): valid offsets stay below it (the host
 // checks that x plus the padding's offset, and the largest scalar offset, fit
@@ -669,7 +669,7 @@ struct Im2colC64Loader {
   Rsrc rsrc;            // x moved back by the padding's offset, 2^31 bytes
   int C, S, RS;
   uint32_t pixb[Sh::NQ];  // (pixel of tap (0,0) + ph*W + pw) * C * EB + chunk * 16
-  uint32_t mask[Sh::NQ];  // bit r*S+s: tap (r, s) of this row is inside the image
+  uint32_t pad[Sh::NQ];   // bit r*S+s: tap (r, s) of this row is padding (all set past M)
   mutable uint32_t vo[Sh::NQ];  // pixb, or OOB where the current tap is padding
   mutable int vo_tap;           // the tap vo[] was formed for
   mutable int cur_tap, cur_s, cur_c;  // tap r*S + s, s and channel of the next K tile
@@ -715,7 +715,7 @@ struct Im2colC64Loader {
     for (int j = 0; j < Sh::NQ; ++j) {
       const uint2 e = rows[Sh::lane_row() + j * 8 * Sh::NWAVES];
       pixb[j] = e.x + chunk_off;
-      mask[j] = e.y;
+      pad[j] = ~e.y;
     }
     const int k = kt0 * CPT;
     const int rs = (int)p.fd_c.div((uint32_t)k);
@@ -745,7 +745,13 @@ struct Im2colC64Loader {
       // tiles past the last tap (prefetch beyond K) use bit 31, never set
       const int bit = tap < RS ? tap : 31;
 #pragma unroll
-      for (int j = 0; j < Sh::NQ; ++j) vo[j] = ((mask[j] >> bit) & 1u) ? pixb[j] : OOB;
+      for (int j = 0; j < Sh::NQ; ++j) {
+        // m = -1 where the tap is padding, 0 inside; then a bit-field insert.
+        // (The compare-and-select form serialized the rows on VCC, with the
+        // matrix pipe idle, once per tap.)
+        const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)pad[j], bit, 1);
+        vo[j] = (pixb[j] & ~m) | (OOB & m);
+      }
       vo_tap = tap;
     }
   }
@@ -1077,20 +1083,26 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // last k-step begins (its last chunk converts the next tile's first
   // fragment), the others at the end of the tile.
   constexpr uint32_t X80 = 0x80808080u;
-  uint32_t fmask[U8_UNIFORM_TAPS ? FM : 1];  // tap-inside bits of this lane's fragment rows
+  uint32_t fpad[U8_UNIFORM_TAPS ? FM : 1];  // padding-tap bits of this lane's fragment rows
   uint32_t xk[U8_UNIFORM_TAPS ? FM : 1];
   uint32_t xz = X80;
+  // fragment row i's constant for tap t: X80, xor zA in every byte where t is
+  // padding (a bit-field extract and two bit operations; no compare)
+  auto xk_for = [&](int i, int t) -> uint32_t {
+    const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)fpad[i], t, 1);
+    return X80 ^ ((xz ^ X80) & m);
+  };
   int xtap = 0, xleft = 1, xtpt = 1;  // tap of the K tile in use, its tiles left, tiles per tap
   if constexpr (U8_UNIFORM_TAPS) {
     xz = X80 ^ ((uint32_t)(uint8_t)(p.zAp + 128) * 0x01010101u);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) fmask[i] = rows[wm * TM + i * MB + frow].y;
+    for (int i = 0; i < FM; ++i) fpad[i] = ~rows[wm * TM + i * MB + frow].y;
     const int k = k0 * KT_BYTES;  // u8: one byte per channel
     xtap = (int)p.fd_c.div((uint32_t)k);
     xtpt = p.C / KT_BYTES;
     xleft = xtpt - (k - xtap * p.C) / KT_BYTES;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) xk[i] = ((fmask[i] >> xtap) & 1u) ? X80 : xz;
+    for (int i = 0; i < FM; ++i) xk[i] = xk_for(i, xtap);
   }
   // the conversion constant of fragment row i
   auto xconst = [&](int i) -> uint32_t {
@@ -1270,7 +1282,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     const uint8_t* As1 = stA(std::integral_constant<int, u + 1>());
     const uint8_t* Bs1 = stB(std::integral_constant<int, u + 1>());
     // row 0's conversion constant now serves the next tile's first fragment
-    if constexpr (U8_UNIFORM_TAPS) xk[0] = ((fmask[0] >> (xleft == 1 ? xtap + 1 : xtap)) & 1u) ? X80 : xz;
+    if constexpr (U8_UNIFORM_TAPS) xk[0] = xk_for(0, xleft == 1 ? xtap + 1 : xtap);
 #pragma unroll
     for (int c = 0; c < FM; ++c) {
       chunk(c, fa[buf], fb[buf], As1, Bs1, 0, fa[buf ^ 1], fb[buf ^ 1],
@@ -1286,7 +1298,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
         ++xtap;
         xleft = xtpt;
 #pragma unroll
-        for (int i = 1; i < FM; ++i) xk[i] = ((fmask[i] >> xtap) & 1u) ? X80 : xz;
+        for (int i = 1; i < FM; ++i) xk[i] = xk_for(i, xtap);
       }
     }
   };
