@@ -16,7 +16,9 @@ the same run the same way, before the headline, and reported under
 between two HIP events on the stream the kernel runs on, against the MI355X
 dense MFMA peak of its dtype.  After that timed region, untimed for `value`:
 each launch alone between two events (median, min, max), for c1 and c2 also
-with the caches flushed before every launch (cold), and the shader clock read
+with the caches flushed before every launch (cold) and as replays of 100
+launches captured into one HIP graph (no host launch path per kernel; a replay
+must reproduce the eager call's outputs bit for bit), and the shader clock read
 from the driver while the launches run.  `traffic` (HBM bytes per launch)
 comes from the committed rocprofv3 counter summary in profiles/ when that
 summary was taken on the current kernel sources, else null.
@@ -90,12 +92,14 @@ class Runner:
         d = wl.dims
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
         self.keep = []
+        self.outs = []  # output tensors (the GEMMs: checked after graph replays)
         if wl.kind == "gemm_f16":
             A, B = t(wl.arrays["A"]), t(wl.arrays["Bt"])
             C = torch.empty((d["M"], d["N"]), dtype=torch.float32, device=dev)
             M, N, K = d["M"], d["N"], d["K"]
             ws, nws = self._workspace(igc.gemm_f16f32_workspace_size(M, N, K), torch, dev)
             self.keep = [A, B, C, ws]
+            self.outs = [C]
             self.call = self._direct("gemm_f16f32", M, N, K, A.data_ptr(), K, B.data_ptr(), K,
                                      C.data_ptr(), N, ws.data_ptr() if nws else None, nws, self.stream)
             self.dtype, self.peak, self.unit = "f16", PEAK_F16_TFLOPS, "TFLOPS"
@@ -117,6 +121,7 @@ class Runner:
                 kw.update(Q_i8=Q, ldq=N, scale_n=S, bias_n=Bi)
             ws, nws = self._workspace(igc.gemm_u8i8_zp_workspace_size(M, N, K), torch, dev)
             self.keep = [A, B, ws] + [v for v in kw.values() if hasattr(v, "data_ptr")]
+            self.outs = [kw[k] for k in ("C_i32", "D_f32", "Q_i8") if k in kw]
             zA, zB = pr["zA"], pr["zB"]
             a = lambda k: kw[k].data_ptr() if k in kw else None  # noqa: E731
             self.ep = igc.Epilogue(a("C_i32"), kw.get("ldc", 0), a("D_f32"), kw.get("ldd", 0),
@@ -317,6 +322,43 @@ def host_info() -> dict:
     return {"cpu_model": model, "cpus_available": avail}
 
 
+def graph_launch_us(wl, igc, torch, launches: int = 100, replays: int = 10) -> dict:
+    """The workload's launches captured into one HIP graph and replayed: per
+    launch = elapsed / (launches x replays).  At the small sizes (c1, c2) the
+    host's per-call launch path (a ctypes call and a kernel launch), not the
+    kernel, bounds the back-to-back figure; a caller with a launch-bound loop
+    would capture it.  Reported only if a replay reproduces the eager call's
+    outputs bit for bit."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        r = Runner(wl, igc, torch)  # its launches go to the capture stream
+        r.call()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in r.outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side, capture_error_mode="thread_local"):
+        for _ in range(launches):
+            r.call()
+    for o in r.outs:
+        o.fill_(7)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    if not r.outs or not all(torch.equal(o, e) for o, e in zip(r.outs, ref)):
+        return {"graph_launch_us": None, "graph_note": "a replay did not reproduce the eager call"}
+    for _ in range(3):
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (launches * replays)
+    return {"graph_launch_us": us, "graph_launches": launches, "graph_replays": replays}
+
+
 def cpu_baseline(wl, budget_s: float) -> dict:
     """Time the oracle on whole output rows (pixels) of the workload for about budget_s."""
     import oracle
@@ -458,6 +500,8 @@ def main(argv=None) -> int:
         wl = synth.workload(name)
         r = Runner(wl, igc, torch)
         res = r.measure(torch, args.steps, args.warmup, cold=name in ("c1", "c2"), extras=not args.no_extras)
+        if name in ("c1", "c2") and not args.no_extras:
+            res.update(graph_launch_us(wl, igc, torch))
         res["roofline_traffic_bytes"] = traffic_for(name)
         res["config"] = synth.DESCRIPTIONS[name]
         results[name] = res
@@ -469,6 +513,7 @@ def main(argv=None) -> int:
               f"{res['launch_us_mean']:.1f} us/launch back to back"
               + (f", {res['launch_us_median']:.1f} us median alone" if "launch_us_median" in res else "")
               + (f", {res['cold_launch_us_median']:.1f} us cold" if "cold_launch_us_median" in res else "")
+              + (f", {res['graph_launch_us']:.1f} us/launch as graph replays" if res.get("graph_launch_us") else "")
               + (f", sclk {res['sclk_mhz']['median']:.0f} MHz" if res.get("sclk_mhz") else ""),
               file=sys.stderr, flush=True)
 
