@@ -825,6 +825,29 @@ __device__ __forceinline__ uint32_t requant_bits(float y) {
   return __builtin_bit_cast(uint32_t, v + 12582912.0f);
 }
 
+// requant_bits with the int8 code written straight into byte Q of `packed`:
+// the rounding add as an SDWA instruction whose destination select takes the
+// sum's low byte (byte 0 zeroes the other bytes, bytes 1-3 keep them), so
+// four codes are packed by their own rounding adds, without byte permutes.
+template <int Q>
+__device__ __forceinline__ void requant_byte(uint32_t& packed, float y) {
+  static_assert(Q >= 0 && Q < 4, "byte");
+  const float v = fminf(fmaxf(y, -128.f), 127.f);
+  const float magic = 12582912.0f;
+  if constexpr (Q == 0)
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_0 dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:DWORD"
+        : "=v"(packed) : "v"(magic), "v"(v));
+  else if constexpr (Q == 1)
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(packed) : "v"(magic), "v"(v));
+  else if constexpr (Q == 2)
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_2 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(packed) : "v"(magic), "v"(v));
+  else
+    asm("v_add_f32_sdwa %0, %1, %2 dst_sel:BYTE_3 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(packed) : "v"(magic), "v"(v));
+}
+
 __device__ __forceinline__ int sum_bytes(uint4 v, int acc) {
   acc = __builtin_amdgcn_sdot4((int)v.x, 0x01010101, acc, false);
   acc = __builtin_amdgcn_sdot4((int)v.y, 0x01010101, acc, false);
@@ -1604,18 +1627,20 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           for (int i = 0; i < FM; ++i) {
             const uint4 v = acc_quad(i, j, g4);
             const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-            int qi[4];
+            float y[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               // the corrected C, then the requantize steps
               const int32_t c = (int32_t)(vv[q] + cterm[q] + rterm[i]);
               const float t = (float)c * sc[q];  // separately rounded: built with -ffp-contract=off
-              const float y = t + bi[q];
-              qi[q] = (int)requant_bits(y);      // half to even, saturated, in the low byte
+              y[q] = t + bi[q];
             }
-            const uint32_t lo = __builtin_amdgcn_perm((uint32_t)qi[1], (uint32_t)qi[0], 0x0c0c0400u);
-            const uint32_t hi = __builtin_amdgcn_perm((uint32_t)qi[3], (uint32_t)qi[2], 0x04000c0cu);
-            *reinterpret_cast<uint32_t*>(qs + qoff(wm * TM + i * MB + arow, lc)) = lo | hi;
+            uint32_t packed;  // half to even, saturated, byte q = column q
+            requant_byte<0>(packed, y[0]);
+            requant_byte<1>(packed, y[1]);
+            requant_byte<2>(packed, y[2]);
+            requant_byte<3>(packed, y[3]);
+            *reinterpret_cast<uint32_t*>(qs + qoff(wm * TM + i * MB + arow, lc)) = packed;
           }
         }
       __syncthreads();
