@@ -1590,17 +1590,24 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           if constexpr (CIN) ncs[q] = p.colsum[n0 + lc + q];
         }
       };
-      fetch(0);
+      // (kernels that keep both epilogue paths load each group's where it is
+      // used and form the row terms per row: the prefetched values and the
+      // row terms held across the groups made them spill more)
+      if constexpr (REQ) fetch(0);
       // C = acc' - zA'*colsum(B) - zB*rowsum(A') + K*zA'*zB (wrapping; the
       // true value fits in int32) as acc' + a row term + a column term: the
       // row terms -zB*rowsum(A') once per fragment row, the column terms
       // K*zA'*zB - zA'*colsum(B) once per group of 4 columns, so each value
       // takes one three-operand add (formed per value, the terms and their
       // row sums' LDS reads took a third of the epilogue's instructions).
-      uint32_t rterm[FM];
+      auto row_term = [&](int i) -> uint32_t {
+        return ((SUMS & SUM_ROWS) != 0 && p.zB != 0) ? 0u - (uint32_t)p.zB * (uint32_t)sums[wm * TM + i * MB + arow] : 0u;
+      };
+      uint32_t rterm[REQ ? FM : 1];
+      if constexpr (REQ) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        rterm[i] = ((SUMS & SUM_ROWS) != 0 && p.zB != 0) ? 0u - (uint32_t)p.zB * (uint32_t)sums[wm * TM + i * MB + arow] : 0u;
+        for (int i = 0; i < FM; ++i) rterm[i] = row_term(i);
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -1609,6 +1616,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
           __builtin_amdgcn_sched_barrier(0);
           const int t = j * (NE / 4) + g4;
           const int lc = group_col(t);  // tile column of the first of the 4
+          if constexpr (!REQ) fetch(t);
           uint32_t cterm[4];
           float sc[4], bi[4];
 #pragma unroll
@@ -1622,7 +1630,8 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
             sc[q] = nsc[q];
             bi[q] = nbi[q];
           }
-          if (t + 1 < NG) fetch(t + 1);
+          if constexpr (REQ)
+            if (t + 1 < NG) fetch(t + 1);
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
             const uint4 v = acc_quad(i, j, g4);
@@ -1631,7 +1640,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               // the corrected C, then the requantize steps
-              const int32_t c = (int32_t)(vv[q] + cterm[q] + rterm[i]);
+              const int32_t c = (int32_t)(vv[q] + cterm[q] + (REQ ? rterm[i] : row_term(i)));
               const float t = (float)c * sc[q];  // separately rounded: built with -ffp-contract=off
               y[q] = t + bi[q];
             }
