@@ -167,6 +167,8 @@ int plan_and_launch(igc::Params& p, bool fast, void* ws, size_t ws_bytes, hipStr
       return launch<KIND, SUMS | igc::REQ_TILES>(p, pl, fast, stream);
     }
   }
+  if constexpr (KIND == igc::KIND_F16_GEMM || KIND == igc::KIND_F16_CONV || KIND == igc::KIND_F16_CONV_C64)
+    if (pl.sk_wgs == 0) return launch<KIND, SUMS | igc::NO_SPLIT>(p, pl, fast, stream);
   return launch<KIND, SUMS>(p, pl, fast, stream);
 }
 
@@ -412,6 +414,7 @@ int gemm_f16f32_noalloc(int M, int N, int K, const void* A, int lda, const void*
     if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   }
   apply_plan(p, pl, ws);
+  if (pl.sk_wgs == 0) return launch<igc::KIND_F16_GEMM, igc::NO_SPLIT>(p, pl, fast, st);
   return launch<igc::KIND_F16_GEMM, 0>(p, pl, fast, st);
 }
 
@@ -569,8 +572,12 @@ int conv2d_implicit_gemm_nhwcnc(int Nb, int H, int W, int C, int Kout, int R, in
   if (e != hipSuccess) return fail(IGC_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   p.B = wk;
   apply_plan(p, pl, workspace);
-  if (kind == igc::KIND_F16_CONV_C64) return launch<igc::KIND_F16_CONV_C64, igc::BLK_OUT>(p, pl, true, st);
-  return launch<igc::KIND_F16_CONV, igc::BLK_OUT>(p, pl, fast, st);
+  constexpr int WHOLE = igc::BLK_OUT | igc::NO_SPLIT;
+  if (kind == igc::KIND_F16_CONV_C64)
+    return pl.sk_wgs == 0 ? launch<igc::KIND_F16_CONV_C64, WHOLE>(p, pl, true, st)
+                          : launch<igc::KIND_F16_CONV_C64, igc::BLK_OUT>(p, pl, true, st);
+  return pl.sk_wgs == 0 ? launch<igc::KIND_F16_CONV, WHOLE>(p, pl, fast, st)
+                        : launch<igc::KIND_F16_CONV, igc::BLK_OUT>(p, pl, fast, st);
 }
 
 }  // extern "C"

@@ -268,7 +268,8 @@ inline bool req_tiles(const igc::Params& p, const Plan& pl, bool fast) {
 // The (kind, variant) pairs the C ABI launches: the fp16 kinds without
 // sums (the convolutions also with BLK_OUT), the u8 x i8 kinds with each
 // subset of SUM_ROWS | SUM_COLS, alone and with REQ_TILES, and REQ_TILES
-// with the caller's column sums (COLS_IN, with or without SUM_ROWS).
+// with the caller's column sums (COLS_IN, with or without SUM_ROWS); the fp16
+// kinds also as NO_SPLIT, for launches whose tiles are all whole.
 #define IGC_LAUNCH_KINDS(X)         \
   X(0, igc::KIND_F16_GEMM, 0)       \
   X(1, igc::KIND_F16_CONV, 0)       \
@@ -294,7 +295,12 @@ inline bool req_tiles(const igc::Params& p, const Plan& pl, bool fast) {
   X(21, igc::KIND_U8I8_GEMM, 20)    \
   X(22, igc::KIND_U8I8_GEMM, 21)    \
   X(23, igc::KIND_U8I8_CONV, 20)    \
-  X(24, igc::KIND_U8I8_CONV, 21)
+  X(24, igc::KIND_U8I8_CONV, 21)    \
+  X(25, igc::KIND_F16_GEMM, 32)     \
+  X(26, igc::KIND_F16_CONV, 32)     \
+  X(27, igc::KIND_F16_CONV_C64, 32) \
+  X(28, igc::KIND_F16_CONV, 40)     \
+  X(29, igc::KIND_F16_CONV_C64, 40)
 
 #define IGC_EXTERN_LAUNCH(n, K, S) \
   extern template int launch<K, S>(const igc::Params&, const Plan&, bool, hipStream_t);

@@ -81,5 +81,20 @@ template int launch<igc::KIND_U8I8_CONV, 20>(const igc::Params&, const Plan&, bo
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 24
 template int launch<igc::KIND_U8I8_CONV, 21>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 25
+template int launch<igc::KIND_F16_GEMM, 32>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 26
+template int launch<igc::KIND_F16_CONV, 32>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 27
+template int launch<igc::KIND_F16_CONV_C64, 32>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 28
+template int launch<igc::KIND_F16_CONV, 40>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 29
+template int launch<igc::KIND_F16_CONV_C64, 40>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
 
 }  // namespace igc_host
