@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libigc.so")
 ABI_SOURCE = os.path.join(CSRC, "igc.hip")
 LAUNCH_SOURCE = os.path.join(CSRC, "igc_launch.hip")
-LAUNCH_UNITS = 30  # the (kind, variant) pairs of IGC_LAUNCH_KINDS in igc_host.hpp
+LAUNCH_UNITS = 38  # the (kind, variant) pairs of IGC_LAUNCH_KINDS in igc_host.hpp
 SOURCES = [ABI_SOURCE, LAUNCH_SOURCE]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

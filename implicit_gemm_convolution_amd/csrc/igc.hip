@@ -166,6 +166,8 @@ int plan_and_launch(igc::Params& p, bool fast, void* ws, size_t ws_bytes, hipStr
           return launch<KIND, (SUMS & igc::SUM_ROWS) | igc::REQ_TILES | igc::COLS_IN>(p, pl, fast, stream);
       return launch<KIND, SUMS | igc::REQ_TILES>(p, pl, fast, stream);
     }
+    if (pl.sk_wgs == 0 && fast && (pl.variant == V_64x64 || pl.variant == V_128x128))
+      return launch<KIND, SUMS | igc::NO_SPLIT>(p, pl, fast, stream);
   }
   if constexpr (KIND == igc::KIND_F16_GEMM || KIND == igc::KIND_F16_CONV || KIND == igc::KIND_F16_CONV_C64)
     if (pl.sk_wgs == 0) return launch<KIND, SUMS | igc::NO_SPLIT>(p, pl, fast, stream);

@@ -206,7 +206,16 @@ int launch_one(const igc::Params& p, const Plan& pl, hipStream_t stream) {
 
 template <int KIND, bool FAST, int SUMS>
 int launch_variant(const igc::Params& p, const Plan& pl, hipStream_t stream) {
-  if constexpr ((SUMS & igc::REQ_TILES) != 0) {
+  constexpr bool INT8 = KIND == igc::KIND_U8I8_GEMM || KIND == igc::KIND_U8I8_CONV;
+  if constexpr (INT8 && (SUMS & igc::NO_SPLIT) != 0) {
+    // whole tiles of the integer kinds without the split code: the aligned
+    // tiles that have it (the wider ones never split)
+    if constexpr (FAST) {
+      if (pl.variant == V_128x128) return launch_one<KIND, 128, 128, 2, 2, FAST, SUMS>(p, pl, stream);
+      if (pl.variant == V_64x64) return launch_one<KIND, 64, 64, 2, 2, FAST, SUMS>(p, pl, stream);
+    }
+    return fail(IGC_EUNSUPPORTED, "internal: variant %d has no whole-tile integer kernel", pl.variant);
+  } else if constexpr ((SUMS & igc::REQ_TILES) != 0) {
     // whole requantize-only tiles: compiled for the 256-column integer tiles
     if constexpr (FAST) {
       if (pl.variant == V_224x256) return launch_one<KIND, 224, 256, 2, 2, FAST, SUMS>(p, pl, stream);
@@ -250,7 +259,8 @@ int launch(const igc::Params& p, const Plan& pl, bool fast, hipStream_t stream) 
   if constexpr (KIND == igc::KIND_F16_GEMM) {
     if (pl.variant == V_BYPASS || pl.variant == V_BYPASS16) return launch_bypass(p, pl, stream);
   }
-  if constexpr (KIND == igc::KIND_F16_CONV_C64 || (SUMS & igc::REQ_TILES) != 0) {
+  constexpr bool INT8 = KIND == igc::KIND_U8I8_GEMM || KIND == igc::KIND_U8I8_CONV;
+  if constexpr (KIND == igc::KIND_F16_CONV_C64 || (SUMS & igc::REQ_TILES) != 0 || (INT8 && (SUMS & igc::NO_SPLIT) != 0)) {
     return launch_variant<KIND, true, SUMS>(p, pl, stream);  // dispatched only with aligned operands
   } else {
     return fast ? launch_variant<KIND, true, SUMS>(p, pl, stream)
@@ -268,8 +278,9 @@ inline bool req_tiles(const igc::Params& p, const Plan& pl, bool fast) {
 // The (kind, variant) pairs the C ABI launches: the fp16 kinds without
 // sums (the convolutions also with BLK_OUT), the u8 x i8 kinds with each
 // subset of SUM_ROWS | SUM_COLS, alone and with REQ_TILES, and REQ_TILES
-// with the caller's column sums (COLS_IN, with or without SUM_ROWS); the fp16
-// kinds also as NO_SPLIT, for launches whose tiles are all whole.
+// with the caller's column sums (COLS_IN, with or without SUM_ROWS); every
+// kind also as NO_SPLIT, for launches whose tiles are all whole (the integer
+// kinds only at the aligned 64x64 and 128x128 tiles, the ones that can split).
 #define IGC_LAUNCH_KINDS(X)         \
   X(0, igc::KIND_F16_GEMM, 0)       \
   X(1, igc::KIND_F16_CONV, 0)       \
@@ -300,7 +311,15 @@ inline bool req_tiles(const igc::Params& p, const Plan& pl, bool fast) {
   X(26, igc::KIND_F16_CONV, 32)     \
   X(27, igc::KIND_F16_CONV_C64, 32) \
   X(28, igc::KIND_F16_CONV, 40)     \
-  X(29, igc::KIND_F16_CONV_C64, 40)
+  X(29, igc::KIND_F16_CONV_C64, 40) \
+  X(30, igc::KIND_U8I8_GEMM, 32)    \
+  X(31, igc::KIND_U8I8_GEMM, 33)    \
+  X(32, igc::KIND_U8I8_GEMM, 34)    \
+  X(33, igc::KIND_U8I8_GEMM, 35)    \
+  X(34, igc::KIND_U8I8_CONV, 32)    \
+  X(35, igc::KIND_U8I8_CONV, 33)    \
+  X(36, igc::KIND_U8I8_CONV, 34)    \
+  X(37, igc::KIND_U8I8_CONV, 35)
 
 #define IGC_EXTERN_LAUNCH(n, K, S) \
   extern template int launch<K, S>(const igc::Params&, const Plan&, bool, hipStream_t);

@@ -903,10 +903,11 @@ __device__ __forceinline__ void touch_params(const Params& p) {
 //  BLK_OUT writes the output in the blocked NHWCnc layout (the launch's
 //  p.blk), so the row-major kernels carry no blocked code.  u8 x i8:
 //  COLS_IN (with REQ_TILES) takes colsum(B) from p.colsum instead of forming
-//  it in the K loop (SUM_COLS then not set).  fp16: NO_SPLIT compiles the
-//  kernel without the stream-K code, for launches whose tiles are all whole
-//  (the split code, never run there, cost the whole-tile launches 1-3.5%:
-//  the 4096^3 GEMM 104.9 -> 103.6 us, the 256x14x14 conv 109.5 -> 105.6 us).
+//  it in the K loop (SUM_COLS then not set).  NO_SPLIT compiles the kernel
+//  without the stream-K code, for launches whose tiles are all whole (the
+//  split code, never run there, cost them 1-12%: the 4096^3 fp16 GEMM
+//  104.9 -> 103.6 us, the 256x14x14 conv 109.5 -> 105.6 us, the 1024^3
+//  u8 x i8 GEMM 6.44 -> 5.67 us).
 //  DEPTH: K tiles in flight ahead of the one being multiplied.  A has
 //  DEPTH + 1 LDS stages; B has 2 at DEPTH 2 (the 160 KiB of LDS at 256 x 256)
 //  and DEPTH + 1 otherwise.  Every launch uses DEPTH 2: deeper rings for the
@@ -937,8 +938,7 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
   // stream-K (shared tiles): compiled for the fp16 kinds and for the integer
   // kinds' aligned tiles of at most 128 rows (the wider integer tiles use
   // every register); the host splits only where it is compiled
-  constexpr bool SK = INT8 ? (BM <= 128 && FAST && !REQ) : (SUMS == 0 && (VAR & NO_SPLIT) == 0);
-  static_assert((VAR & NO_SPLIT) == 0 || !INT8, "whole-tile fp16 kernels (the integer ones split only below 129 rows)");
+  constexpr bool SK = (VAR & NO_SPLIT) == 0 && (INT8 ? (BM <= 128 && FAST && !REQ) : (SUMS == 0));
   static_assert(!REQ || (INT8 && FAST), "whole requantize-only tiles: the aligned integer kernels");
   static_assert(!BLKO || !INT8, "blocked output: the fp16 convolution");
   static_assert(!CIN || (REQ && (SUMS & SUM_COLS) == 0), "precomputed column sums: whole requantize-only tiles");

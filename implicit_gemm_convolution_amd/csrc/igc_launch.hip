@@ -96,5 +96,29 @@ template int launch<igc::KIND_F16_CONV, 40>(const igc::Params&, const Plan&, boo
 #if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 29
 template int launch<igc::KIND_F16_CONV_C64, 40>(const igc::Params&, const Plan&, bool, hipStream_t);
 #endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 30
+template int launch<igc::KIND_U8I8_GEMM, 32>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 31
+template int launch<igc::KIND_U8I8_GEMM, 33>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 32
+template int launch<igc::KIND_U8I8_GEMM, 34>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 33
+template int launch<igc::KIND_U8I8_GEMM, 35>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 34
+template int launch<igc::KIND_U8I8_CONV, 32>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 35
+template int launch<igc::KIND_U8I8_CONV, 33>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 36
+template int launch<igc::KIND_U8I8_CONV, 34>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
+#if !defined(IGC_LAUNCH_UNIT) || IGC_LAUNCH_UNIT == 37
+template int launch<igc::KIND_U8I8_CONV, 35>(const igc::Params&, const Plan&, bool, hipStream_t);
+#endif
 
 }  // namespace igc_host
