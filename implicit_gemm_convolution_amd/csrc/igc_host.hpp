@@ -116,18 +116,16 @@ inline Plan make_plan(int kind, int M, int N, int K, bool fast, int cus, bool ws
   int v;
   if (kind == igc::KIND_F16_GEMM && fast &&
       (fv == V_BYPASS || fv == V_BYPASS16 ||
-       (fv == V_AUTO && ceil_div(M, 32) * ceil_div(N, 32) <= cus && K <= 512))) {
-    // The LDS-bypass kernel wins only where the whole problem is one short
-    // round: measured on MI355X, 256^3 3.6 us against 4.1 (64x64 tiles),
-    // 512^3 4.8 against 4.9, but 1024^3 16.4 against 6.6 and 256x256x4096
-    // 23.5 against 14.2 (a single wave then walks a long K loop alone).
-    // Its 16x16 tiles, where they still fit one wave per compute unit, spread
-    // the problem over four times the compute units: 256^3 2.87 us against
-    // 3.73 (kernel time, rocprofv3).
-    if (fv == V_AUTO)
-      v = ceil_div(M, 16) * ceil_div(N, 16) <= cus ? V_BYPASS16 : V_BYPASS;
-    else
-      v = fv;
+       (fv == V_AUTO && ceil_div(M, 16) * ceil_div(N, 16) <= cus && K <= 512))) {
+    // The LDS-bypass kernel wins only where its 16x16 tiles, one wave each,
+    // fit one round of compute units and K is short: measured on MI355X
+    // (graph replays, per launch) 256x256x512 2.82 us against 3.69 us on
+    // 64x64 LDS tiles.  Where they do not fit, the 64x64 whole-tile kernel
+    // matches or beats both bypass forms: 512^3 3.77 us against 4.52 (32x32
+    // bypass) and 5.25 (16x16, two rounds), 384^3 3.46 against 4.15 and 4.00,
+    // 512x256x512 3.72 against 4.43 and 3.63.  The 32x32 form is taken only
+    // when forced.
+    v = fv == V_AUTO ? V_BYPASS16 : fv;
   } else {
     v = fv == V_AUTO ? choose_variant(M, N, cus) : fv;
     if (v == V_BYPASS || v == V_BYPASS16) v = V_64x64;  // (forced, for a kind or shape without the bypass kernel)

@@ -1675,7 +1675,10 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
         }
       }
     }
-  #pragma unroll
+    // (one wave-row of the tile per step; not unrolled in the 256x256 u8 x i8
+    // kernels with in-loop column sums, where the optimizer cannot)
+    constexpr int UNR_H = (INT8 && BM == 256 && BN == 256 && (SUMS & SUM_COLS) != 0) ? 1 : WM;
+  #pragma unroll UNR_H
     for (int h = 0; h < WM; ++h) {
       if (wm == h) {
   #pragma unroll
