@@ -1,0 +1,112 @@
+"""Randomized parity (GPU): seeded random shapes, zero points, outputs, tile
+variants and split modes for the four entry points, every output compared
+with the oracle bit for bit (integer-valued fp16 operands, whose sums are
+exact in fp32; u8 x i8 int32 and requantized int8 outputs).  The fixed-case
+tests pin chosen corners; these cover their combinations."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+from test_gpu_parity import run_conv, run_f16, run_qconv, run_u8i8
+
+pytestmark = pytest.mark.gpu
+
+KINDS = ("gemm_u8i8", "conv_u8i8", "gemm_f16", "conv_f16")
+
+
+@pytest.fixture(scope="module")
+def igc():
+    import torch
+
+    assert torch.cuda.is_available()
+    import implicit_gemm_convolution_amd as m
+
+    assert m.device_check() == m.IGC_OK, m.last_error()
+    m.set_tuning(-1, 1)
+    yield m
+    m.set_tuning(-1, 1)
+
+
+def _conv_shape(rng, channels):
+    while True:
+        Nb, H, W = int(rng.integers(1, 4)), int(rng.integers(1, 17)), int(rng.integers(1, 17))
+        C = int(rng.choice(channels))
+        Kout = int(rng.integers(1, 300))
+        R, S = int(rng.choice([1, 3, 3, 5])), int(rng.choice([1, 3, 3, 5]))
+        st = (int(rng.choice([1, 1, 2])), int(rng.choice([1, 1, 2])))
+        pd = (int(rng.integers(0, 3)), int(rng.integers(0, 3)))
+        if H + 2 * pd[0] >= R and W + 2 * pd[1] >= S:
+            return Nb, H, W, C, Kout, R, S, st, pd
+
+
+def _gemm_shape(rng, m_max, n_max, big):
+    if rng.random() < 0.4:
+        return int(rng.choice(big[0])), int(rng.choice(big[1])), int(rng.choice(big[2]))
+    return int(rng.integers(1, m_max)), int(rng.integers(1, n_max)), int(rng.integers(1, 1300))
+
+
+def _one_case(igc, oracle, rng):
+    import torch
+
+    kind = KINDS[int(rng.integers(0, len(KINDS)))]
+    v = int(rng.choice([-1, -1, -1, 0, 1, 2, 3, 4]))  # by shape, or a forced tile
+    sk = int(rng.choice([1, 1, 0, 2]))  # split where it pays, never, always
+    igc.set_tuning(v, sk)
+    try:
+        if kind == "gemm_f16":
+            M, N, K = _gemm_shape(rng, 700, 600, ([256, 512, 1024], [256, 512], [64, 512, 1024]))
+            A, Bt = synth.f16_small_ints(rng, (M, K)), synth.f16_small_ints(rng, (N, K))
+            desc = f"{kind} M={M} N={N} K={K} variant={v} split={sk}"
+            print(desc, flush=True)
+            assert np.array_equal(run_f16(igc, A, Bt).astype(np.float64), oracle.gemm_f16(A, Bt)), desc
+            return kind
+        if kind == "conv_f16":
+            Nb, H, W, C, Kout, R, S, st, pd = _conv_shape(rng, [64, 128, 256, int(rng.integers(1, 100))])
+            x, w = synth.f16_small_ints(rng, (Nb, H, W, C)), synth.f16_small_ints(rng, (Kout, R, S, C))
+            desc = f"{kind} {Nb}x{H}x{W}x{C} * {Kout}x{R}x{S} stride={st} pad={pd} variant={v} split={sk}"
+            print(desc, flush=True)
+            assert np.array_equal(run_conv(igc, x, w, st, pd).astype(np.float64),
+                                  oracle.conv2d_direct(x, w, st, pd)), desc
+            return kind
+        outs = [("Q",), ("C",), ("C", "Q"), ("Q",)][int(rng.integers(0, 4))]
+        zA = int(rng.choice([0, 128, int(rng.integers(0, 256))]))
+        zB = int(rng.choice([0, int(rng.integers(-128, 128))]))
+        use_cs = "C" not in outs and rng.random() < 0.5
+        if kind == "gemm_u8i8":
+            M, N, K = _gemm_shape(rng, 600, 520, ([224, 256, 448, 512], [256, 512], [128, 256, 384, 1024]))
+            A, Bt = synth.u8_uniform(rng, (M, K)), synth.i8_uniform(rng, (N, K))
+            scale = rng.uniform(0.001, 0.05, size=N).astype(np.float32)
+            bias = (rng.standard_normal(N) * 4).astype(np.float32)
+            cs = torch.from_numpy(oracle.i8_colsum(Bt).astype(np.int32)).cuda() if use_cs else None
+            desc = f"{kind} M={M} N={N} K={K} zA={zA} zB={zB} outputs={outs} colsum={use_cs} variant={v} split={sk}"
+            print(desc, flush=True)
+            got = run_u8i8(igc, A, zA, Bt, zB, outputs=outs, scale=scale, bias=bias, colsum_B=cs)
+            C32 = oracle.gemm_u8i8_naive(A, zA, Bt, zB)
+        else:
+            Nb, H, W, C, Kout, R, S, st, pd = _conv_shape(rng, [128, 256, 128, int(rng.integers(1, 200))])
+            x, w = synth.u8_uniform(rng, (Nb, H, W, C)), synth.i8_uniform(rng, (Kout, R, S, C))
+            scale = rng.uniform(0.0001, 0.01, size=Kout).astype(np.float32)
+            bias = (rng.standard_normal(Kout) * 4).astype(np.float32)
+            cs = (torch.from_numpy(oracle.i8_colsum(w.reshape(Kout, -1)).astype(np.int32)).cuda()
+                  if use_cs else None)
+            desc = (f"{kind} {Nb}x{H}x{W}x{C} * {Kout}x{R}x{S} stride={st} pad={pd} zA={zA} zB={zB} "
+                    f"outputs={outs} colsum={use_cs} variant={v} split={sk}")
+            print(desc, flush=True)
+            got = run_qconv(igc, x, zA, w, zB, st, pd, outputs=outs, scale=scale, bias=bias, colsum_B=cs)
+            C32 = oracle.conv2d_u8i8_direct(x, zA, w, zB, st, pd).reshape(-1, Kout)
+        if "C" in got:
+            assert np.array_equal(got["C"].astype(np.int64), C32), desc
+        if "Q" in got:
+            assert np.array_equal(got["Q"], oracle.requant(C32, scale, bias)), desc
+        return kind
+    finally:
+        igc.set_tuning(-1, 1)
+
+
+@pytest.mark.parametrize("seed", [101, 102, 103])
+def test_random_cases_match_the_oracle(igc, oracle, seed):
+    rng = np.random.default_rng(seed)
+    seen = [_one_case(igc, oracle, rng) for _ in range(50)]
+    assert set(seen) == set(KINDS)
