@@ -233,7 +233,7 @@ class Runner:
         )
         if not extras:
             return res
-        res.update(self._per_launch(torch, steps, "launch_us"))
+        res.update(self._per_launch(torch, steps, "alone_us"))
         if cold:
             # a 512 MiB write between launches evicts the operands from the
             # 256 MiB last-level cache (MALL) and the L2s
@@ -511,7 +511,7 @@ def main(argv=None) -> int:
         torch.cuda.empty_cache()
         print(f"# {name}: {res['value']:.1f} {res['unit']} ({100 * res['frac_of_peak']:.1f}% of peak), "
               f"{res['launch_us_mean']:.1f} us/launch back to back"
-              + (f", {res['launch_us_median']:.1f} us median alone" if "launch_us_median" in res else "")
+              + (f", {res['alone_us_median']:.1f} us median alone" if "alone_us_median" in res else "")
               + (f", {res['cold_launch_us_median']:.1f} us cold" if "cold_launch_us_median" in res else "")
               + (f", {res['graph_launch_us']:.1f} us/launch as graph replays" if res.get("graph_launch_us") else "")
               + (f", sclk {res['sclk_mhz']['median']:.0f} MHz" if res.get("sclk_mhz") else ""),
@@ -549,9 +549,10 @@ def main(argv=None) -> int:
             "frac": round(head["frac_of_peak"], 4),
             "traffic": traffic_for(args.workload),
             "launch_us_mean": round(head["launch_us_mean"], 2),
-            "launch_us_median": round(head["launch_us_median"], 2) if "launch_us_median" in head else None,
-            "launch_us_min": round(head["launch_us_min"], 2) if "launch_us_min" in head else None,
-            "launch_us_max": round(head["launch_us_max"], 2) if "launch_us_max" in head else None,
+            # each launch alone between two events (after the timed region)
+            "alone_us_median": round(head["alone_us_median"], 2) if "alone_us_median" in head else None,
+            "alone_us_min": round(head["alone_us_min"], 2) if "alone_us_min" in head else None,
+            "alone_us_max": round(head["alone_us_max"], 2) if "alone_us_max" in head else None,
             "sclk_mhz": head.get("sclk_mhz"),
             "kernel_source_hash": kernel_source_hash(),
         },
