@@ -1,0 +1,112 @@
+"""Convolutions at the input-size limits of the loaders (GPU).
+
+The uniform-tap and 16-byte im2col loaders address x with 32-bit byte
+offsets from one buffer base, so the host takes them only while those
+offsets stay below 2^31 bytes: the uniform-tap loader needs x plus the
+padding's offset ((pad_h * W + pad_w) * C elements) below 2^31 bytes, the
+16-byte loader x itself below 2^31 bytes; beyond that the element-wise
+loader (64-bit element index) runs.  Each case sits just past one of these
+switch points.  Operands are small integers in fp16, so every output is exact
+in fp32 and compared bit for bit with the oracle at sampled pixels: the
+first and last rows of the image, its corners and random pixels (the last
+rows read the highest offsets of x)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import empty_dev, to_dev, workspace_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def igc():
+    import torch
+
+    assert torch.cuda.is_available()
+    import implicit_gemm_convolution_amd as m
+
+    assert m.device_check() == m.IGC_OK, m.last_error()
+    m.set_tuning(-1, 1)
+    yield m
+
+
+CASES = [
+    # H = W, C, Kout, R = S, pad; x bytes = H*W*C*2
+    # 4095^2 x 64 fp16 plus the padding's offset (4095 + 1)*64*2 is
+    # 2,146,959,488 bytes < 2^31: the uniform-tap loader at its largest input
+    pytest.param(4095, 64, 16, 3, 1, id="uniform_taps_largest_input"),
+    # 4100^2 x 64 fp16 = 2,151,680,000 bytes >= 2^31: element-wise loader
+    pytest.param(4100, 64, 16, 3, 1, id="x_past_2GiB_elementwise"),
+    # 4095^2 x 64 fp16 = 2,146,435,200 bytes < 2^31, but with the padding's
+    # offset (2*4095 + 2)*64*2 = 1,048,576 bytes it passes 2^31: the 16-byte
+    # loader instead of the uniform-tap one
+    pytest.param(4095, 64, 16, 5, 2, id="x_plus_padding_past_2GiB_16byte"),
+]
+
+
+@pytest.mark.parametrize("HW, C, Kout, RS, pad", CASES)
+def test_conv_f16_at_loader_limits(igc, oracle, HW, C, Kout, RS, pad):
+    import torch
+
+    rng = np.random.default_rng(HW)
+    print(f"conv f16 1x{HW}x{HW}x{C} * {Kout}x{RS}x{RS}x{C} pad {pad}", flush=True)
+    x = synth.i8_uniform(rng, (1, HW, HW, C), -8, 8).astype(np.float16)
+    w = synth.i8_uniform(rng, (Kout, RS, RS, C), -8, 8).astype(np.float16)
+    P = Q = HW + 2 * pad - RS + 1
+    M = P * Q
+    dims = (1, HW, HW, C, Kout, RS, RS, 1, 1, pad, pad)
+    dx, dw = to_dev(x), to_dev(w)
+    dy = empty_dev((M, Kout), torch.float32)
+    igc.conv2d_implicit_gemm(*dims, dx, dw, dy,
+                             workspace=workspace_for(igc.conv2d_implicit_gemm_workspace_size(*dims)))
+    torch.cuda.synchronize()
+    pix = {0, Q - 1, (P - 1) * Q, M - 1, M // 2}
+    pix |= set(range(0, 40)) | set(range(M - 40, M))
+    pix |= set(rng.integers(0, M, 200).tolist())
+    pix = np.array(sorted(pix), dtype=np.int64)
+    got = dy[torch.from_numpy(pix).cuda()].cpu().numpy().astype(np.float64)
+    del dx, dy
+    ref = oracle.conv2d_direct_at(x, w, pix, (1, 1), (pad, pad))
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:10]
+
+
+QCASES = [
+    # H = W, C, Kout, R = S, pad; x bytes = H*W*C
+    # 4095^2 x 128 u8 plus (4095 + 1)*128 is 2,146,959,488 bytes < 2^31: the
+    # uniform-tap loader at its largest input
+    pytest.param(4095, 128, 16, 3, 1, id="uniform_taps_largest_input"),
+    # with (2*4095 + 2)*128 it is 2,147,483,776 >= 2^31: the element-wise loader
+    pytest.param(4095, 128, 16, 5, 2, id="x_plus_padding_past_2GiB_elementwise"),
+]
+
+
+@pytest.mark.parametrize("HW, C, Kout, RS, pad", QCASES)
+def test_conv_u8i8_at_loader_limits(igc, oracle, HW, C, Kout, RS, pad):
+    """The quantized convolution at the same limits, int32 output, with zero
+    points on both sides (the padding holds zA)."""
+    import torch
+
+    rng = np.random.default_rng(HW + RS)
+    zA, zB = 100, -3
+    print(f"conv u8i8 1x{HW}x{HW}x{C} * {Kout}x{RS}x{RS}x{C} pad {pad}", flush=True)
+    x = synth.u8_uniform(rng, (1, HW, HW, C))
+    w = synth.i8_uniform(rng, (Kout, RS, RS, C))
+    P = Q = HW + 2 * pad - RS + 1
+    M = P * Q
+    dims = (1, HW, HW, C, Kout, RS, RS, 1, 1, pad, pad)
+    dx, dw = to_dev(x), to_dev(w)
+    dC = empty_dev((M, Kout), torch.int32)
+    igc.conv2d_u8i8_zp(*dims, dx, zA, dw, zB, C_i32=dC, ldc=Kout,
+                       workspace=workspace_for(igc.conv2d_u8i8_zp_workspace_size(*dims)))
+    torch.cuda.synchronize()
+    pix = {0, Q - 1, (P - 1) * Q, M - 1, M // 2}
+    pix |= set(range(0, 40)) | set(range(M - 40, M))
+    pix |= set(rng.integers(0, M, 200).tolist())
+    pix = np.array(sorted(pix), dtype=np.int64)
+    got = dC[torch.from_numpy(pix).cuda()].cpu().numpy().astype(np.int64)
+    del dx, dC
+    ref = oracle.conv2d_u8i8_direct_at(x, zA, w, zB, pix, (1, 1), (pad, pad))
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:10]
