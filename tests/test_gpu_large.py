@@ -1,4 +1,4 @@
-"""Convolutions at the input-size limits of the loaders (GPU).
+"""Operands at the input-size limits of the loaders (GPU).
 
 The uniform-tap and 16-byte im2col loaders address x with 32-bit byte
 offsets from one buffer base, so the host takes them only while those
@@ -9,7 +9,8 @@ loader (64-bit element index) runs.  Each case sits just past one of these
 switch points.  Operands are small integers in fp16, so every output is exact
 in fp32 and compared bit for bit with the oracle at sampled pixels: the
 first and last rows of the image, its corners and random pixels (the last
-rows read the highest offsets of x)."""
+rows read the highest offsets of x).  The GEMMs take an A of 2.25 GB,
+compared on its first, last and random rows."""
 from __future__ import annotations
 
 import numpy as np
@@ -110,3 +111,58 @@ def test_conv_u8i8_at_loader_limits(igc, oracle, HW, C, Kout, RS, pad):
     del dx, dC
     ref = oracle.conv2d_u8i8_direct_at(x, zA, w, zB, pix, (1, 1), (pad, pad))
     assert np.array_equal(got, ref), np.argwhere(got != ref)[:10]
+
+
+def _rows_sample(rng, M):
+    rows = set(range(0, 40)) | set(range(M - 40, M)) | {M // 2}
+    rows |= set(rng.integers(0, M, 100).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def test_gemm_f16_operand_past_2GiB(igc, oracle):
+    """fp16 GEMM whose A (1,100,000 x 1024) spans 2.25 GB: each tile's loads
+    are addressed from its own first row (64-bit base), so the whole-matrix
+    size never enters a 32-bit offset.  Integer-valued operands: exact."""
+    import torch
+
+    M, N, K = 1_100_000, 64, 1024
+    rng = np.random.default_rng(7)
+    print(f"gemm f16 M={M} N={N} K={K}", flush=True)
+    A = synth.i8_uniform(rng, (M, K), -8, 8).astype(np.float16)
+    Bt = synth.i8_uniform(rng, (N, K), -8, 8).astype(np.float16)
+    dA, dB = to_dev(A), to_dev(Bt)
+    dC = empty_dev((M, N), torch.float32)
+    igc.gemm_f16f32(M, N, K, dA, K, dB, K, dC, N, workspace=workspace_for(igc.gemm_f16f32_workspace_size(M, N, K)))
+    torch.cuda.synchronize()
+    rows = _rows_sample(rng, M)
+    got = dC[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, oracle.gemm_f16(A[rows], Bt))
+
+
+def test_gemm_u8i8_operand_past_2GiB(igc, oracle):
+    """u8 x i8 GEMM whose A (2,200,000 x 1024) spans 2.25 GB, int32 and
+    requantized int8 outputs, zero points on both sides."""
+    import torch
+
+    M, N, K = 2_200_000, 64, 1024
+    zA, zB = 77, 5
+    rng = np.random.default_rng(8)
+    print(f"gemm u8i8 M={M} N={N} K={K}", flush=True)
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = synth.i8_uniform(rng, (N, K))
+    scale = rng.uniform(0.0005, 0.002, size=N).astype(np.float32)
+    bias = (rng.standard_normal(N) * 4).astype(np.float32)
+    dA, dB = to_dev(A), to_dev(Bt)
+    dS, dBi = to_dev(scale), to_dev(bias)
+    dC = empty_dev((M, N), torch.int32)
+    dQ = empty_dev((M, N), torch.int8)
+    igc.gemm_u8i8_zp(M, N, K, dA, K, zA, dB, K, zB, C_i32=dC, ldc=N, Q_i8=dQ, ldq=N, scale_n=dS, bias_n=dBi,
+                     workspace=workspace_for(igc.gemm_u8i8_zp_workspace_size(M, N, K)))
+    torch.cuda.synchronize()
+    rows = _rows_sample(rng, M)
+    idx = torch.from_numpy(rows).cuda()
+    C = dC[idx].cpu().numpy().astype(np.int64)
+    Q = dQ[idx].cpu().numpy()
+    ref = oracle.gemm_u8i8_naive(A[rows], zA, Bt, zB)
+    assert np.array_equal(C, ref)
+    assert np.array_equal(Q, oracle.requant(ref, scale, bias))
