@@ -10,7 +10,8 @@ switch points.  Operands are small integers in fp16, so every output is exact
 in fp32 and compared bit for bit with the oracle at sampled pixels: the
 first and last rows of the image, its corners and random pixels (the last
 rows read the highest offsets of x).  The GEMMs take an A of 2.25 GB,
-compared on its first, last and random rows."""
+compared on its first, last and random rows, and two outputs have more
+than 2^31 elements."""
 from __future__ import annotations
 
 import numpy as np
@@ -166,3 +167,48 @@ def test_gemm_u8i8_operand_past_2GiB(igc, oracle):
     ref = oracle.gemm_u8i8_naive(A[rows], zA, Bt, zB)
     assert np.array_equal(C, ref)
     assert np.array_equal(Q, oracle.requant(ref, scale, bias))
+
+
+def test_gemm_f16_output_past_2G_elements(igc, oracle):
+    """fp32 C of 65,536 x 32,800 = 2,149,580,800 elements (8.6 GB), ragged in
+    N: every output address is a 64-bit row offset.  Compared on sampled rows
+    (the last ones hold the highest addresses)."""
+    import torch
+
+    M, N, K = 65_536, 32_800, 64
+    rng = np.random.default_rng(9)
+    print(f"gemm f16 M={M} N={N} K={K}", flush=True)
+    A = synth.i8_uniform(rng, (M, K), -8, 8).astype(np.float16)
+    Bt = synth.i8_uniform(rng, (N, K), -8, 8).astype(np.float16)
+    dA, dB = to_dev(A), to_dev(Bt)
+    dC = empty_dev((M, N), torch.float32)
+    igc.gemm_f16f32(M, N, K, dA, K, dB, K, dC, N, workspace=workspace_for(igc.gemm_f16f32_workspace_size(M, N, K)))
+    torch.cuda.synchronize()
+    rows = _rows_sample(rng, M)
+    got = dC[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    del dC
+    assert np.array_equal(got, oracle.gemm_f16(A[rows], Bt))
+
+
+def test_gemm_u8i8_requant_output_past_2G_elements(igc, oracle):
+    """Requantized int8 Q of 65,536 x 32,800 elements (2.15 GB), ragged in N."""
+    import torch
+
+    M, N, K = 65_536, 32_800, 256
+    zA, zB = 128, 0
+    rng = np.random.default_rng(10)
+    print(f"gemm u8i8 requant M={M} N={N} K={K}", flush=True)
+    A = synth.u8_uniform(rng, (M, K))
+    Bt = synth.i8_uniform(rng, (N, K))
+    scale = rng.uniform(0.001, 0.01, size=N).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    dA, dB = to_dev(A), to_dev(Bt)
+    dS, dBi = to_dev(scale), to_dev(bias)
+    dQ = empty_dev((M, N), torch.int8)
+    igc.gemm_u8i8_zp(M, N, K, dA, K, zA, dB, K, zB, Q_i8=dQ, ldq=N, scale_n=dS, bias_n=dBi,
+                     workspace=workspace_for(igc.gemm_u8i8_zp_workspace_size(M, N, K)))
+    torch.cuda.synchronize()
+    rows = _rows_sample(rng, M)
+    Q = dQ[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del dQ
+    assert np.array_equal(Q, oracle.requant(oracle.gemm_u8i8_naive(A[rows], zA, Bt, zB), scale, bias))
