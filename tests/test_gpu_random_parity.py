@@ -1,5 +1,5 @@
 """Randomized parity (GPU): seeded random shapes, zero points, outputs, tile
-variants and split modes for the four entry points, every output compared
+variants and split modes for the five entry points, every output compared
 with the oracle bit for bit (integer-valued fp16 operands, whose sums are
 exact in fp32; u8 x i8 int32 and requantized int8 outputs).  The fixed-case
 tests pin chosen corners; these cover their combinations."""
@@ -9,11 +9,11 @@ import numpy as np
 import pytest
 
 import synth
-from test_gpu_parity import run_conv, run_f16, run_qconv, run_u8i8
+from test_gpu_parity import run_conv, run_conv_nhwcnc, run_f16, run_qconv, run_u8i8
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ("gemm_u8i8", "conv_u8i8", "gemm_f16", "conv_f16")
+KINDS = ("gemm_u8i8", "conv_u8i8", "gemm_f16", "conv_f16", "conv_nhwcnc")
 
 
 @pytest.fixture(scope="module")
@@ -69,6 +69,19 @@ def _one_case(igc, oracle, rng):
             print(desc, flush=True)
             assert np.array_equal(run_conv(igc, x, w, st, pd).astype(np.float64),
                                   oracle.conv2d_direct(x, w, st, pd)), desc
+            return kind
+        if kind == "conv_nhwcnc":
+            # blocked layout: 16 images x 16 channels innermost (the shape's
+            # batch, channels and output channels are block counts)
+            _, H, W, _, _, R, S, st, pd = _conv_shape(rng, [16])
+            NB, CB, OB = int(rng.integers(1, 3)), int(rng.choice([1, 2, 3, 4, 8])), int(rng.integers(1, 9))
+            xb = synth.f16_small_ints(rng, (NB, H, W, CB, 16, 16), -4, 4)
+            wb = synth.f16_small_ints(rng, (R, S, CB, OB, 16, 16), -4, 4)
+            desc = (f"{kind} {16 * NB}x{H}x{W}x{16 * CB} * {16 * OB}x{R}x{S} stride={st} pad={pd} "
+                    f"variant={v} split={sk}")
+            print(desc, flush=True)
+            assert np.array_equal(run_conv_nhwcnc(igc, xb, wb, st, pd).astype(np.float64),
+                                  oracle.conv2d_nhwcnc_direct(xb, wb, st, pd)), desc
             return kind
         outs = [("Q",), ("C",), ("C", "Q"), ("Q",)][int(rng.integers(0, 4))]
         zA = int(rng.choice([0, 128, int(rng.integers(0, 256))]))
