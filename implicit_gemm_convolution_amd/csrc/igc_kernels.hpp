@@ -231,10 +231,11 @@ __device__ __forceinline__ void store4_nt(void* dst, uint32_t v) {
 // Buffer descriptors and direct-to-LDS loads.
 // ---------------------------------------------------------------------------
 constexpr uint32_t OOB = 0x80000000u;  // descriptors are limited to < 2^31 bytes
-// Cache policy of a buffer access coherent across the XCDs of the device
-// (each XCD has its own L2): device ("agent") scope, sc1.  Stream-K partial
-// tiles are written and read this way, so they need no cache-wide
-// write-back or invalidation.
+// Cache policy of a buffer access at device ("agent") scope: sc1.  The
+// stream-K partial tiles are written and read with it; it does not by itself
+// make them visible across XCDs (each has its own L2): the arrival count is
+// an acquire-release atomic at device scope, which writes the L2 back before
+// it and invalidates after it.
 constexpr int CPOL_DEV = 16;
 
 // A buffer descriptor, both as the compiler's resource type (for the
@@ -1737,8 +1738,13 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
               }
               v = make_uint4(vv[0], vv[1], vv[2], vv[3]);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), wsr, voff,
-                                                   (2 * g + (first_seg ? 0 : 1)) * SLOT, CPOL_DEV);
+            // (the slot in the vector offset, scalar offset 0: with a
+            // register there the compiler keeps no wait states between this
+            // 16-byte store and a following write of its data registers, and
+            // on this GPU that write reached the store: the first of the four
+            // values became the next store's offset)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), wsr,
+                                                   voff + (2 * g + (first_seg ? 0 : 1)) * SLOT, 0, CPOL_DEV);
             continue;
           }
         }
@@ -1757,7 +1763,17 @@ __global__ void __launch_bounds__(64 * WM * WN, 1) gemm_kernel(const Params p) {
     // value so the segment loop stays scalar)
     volatile int* const s_last = reinterpret_cast<volatile int*>(sb1);
     if (tid == 0) {
-      const int before = atomicAdd(p.cnt + j_sk, 1);
+      // Release and acquire at device scope: the sc1 policy alone does not
+      // carry the partials past an XCD's L2 (a last contributor on another
+      // XCD then read a zero-filled slot: one contributor's sums missing).
+      // The count follows a write-back of this XCD's L2 (every wave has
+      // waited for its stores above) that has completed (the explicit wait:
+      // the compiler dropped its own between the write-back and the atomic),
+      // and a last contributor invalidates before its loads below.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      wait_vmcnt_lgkm0<0>();
+      const int before = __hip_atomic_fetch_add(p.cnt + j_sk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       const int last = before == g_hi - g_lo;
       if (last) __hip_atomic_store(p.cnt + j_sk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
       *s_last = last;

@@ -741,6 +741,26 @@ def test_conv_nhwcnc_misaligned_input(igc, oracle, case):
     assert np.array_equal(y.astype(np.float64), oracle.conv2d_nhwcnc_direct(xb, wb, stride, pad))
 
 
+def test_conv_nhwcnc_split_tiles_across_xcds(igc, oracle):
+    """Regression: 64x64 tiles with the partial round split (320 tiles over
+    256 compute units, each split tile shared by two workgroups on different
+    XCDs).  While the arrival count was a relaxed atomic, the last contributor
+    could read the other's partial slot still zero-filled: hundreds of wrong
+    outputs per call, a different set each call.  Several calls, bit-exact."""
+    NB, H, W, CB, OB, R, S, stride, pad = 2, 16, 16, 8, 8, 3, 1, (1, 1), (1, 2)
+    rng = np.random.default_rng(334)
+    xb = synth.f16_small_ints(rng, (NB, H, W, CB, 16, 16), -4, 4)
+    wb = synth.f16_small_ints(rng, (R, S, CB, OB, 16, 16), -4, 4)
+    ref = oracle.conv2d_nhwcnc_direct(xb, wb, stride, pad)
+    igc.set_tuning(2, 2)  # 64x64 tiles, split wherever tiles leave compute units idle
+    try:
+        for rep in range(4):
+            y = run_conv_nhwcnc(igc, xb, wb, stride, pad).astype(np.float64)
+            assert np.array_equal(y, ref), (rep, int(np.sum(y != ref)))
+    finally:
+        igc.set_tuning(-1, 1)
+
+
 def test_conv_nhwcnc_matches_the_nhwc_path(igc):
     """The same logical convolution through both entry points gives the same
     fp32 values (same tiles, same K order)."""

@@ -235,3 +235,71 @@ def test_no_compiler_vmcnt_wait_in_fast_main_loops(tiled):
         mf = [i for i, l in enumerate(lines) if l.startswith("v_mfma")]
         stray = [l for l in lines[mf[0]:mf[-1]] if l.startswith("s_waitcnt") and "vmcnt" in l and "lgkmcnt(0)" not in l]
         assert not stray, (name, stray[:2])
+
+
+def test_stream_k_count_is_released_and_acquired_at_device_scope(tiled):
+    """A split tile's partial sums cross XCDs, each with its own L2: before a
+    workgroup counts itself in, its L2 is written back and the write-back has
+    completed; after the count, the caches are invalidated before a last
+    contributor reads the others' partials."""
+    n = 0
+    for name, (body, _) in tiled.items():
+        lines = [l.split(";")[0].strip() for l in body.splitlines()]
+        lines = [l for l in lines if l and not l.startswith(".")]
+        at = [i for i, l in enumerate(lines) if l.startswith("global_atomic_add")]
+        if not at:
+            continue
+        n += 1
+        i = at[0]
+        wb = [k for k in range(max(0, i - 40), i) if lines[k].startswith("buffer_wbl2") and "sc1" in lines[k]]
+        assert wb, (name, "no L2 write-back before the count")
+        assert any(l.startswith("s_waitcnt") and "vmcnt(0)" in l for l in lines[wb[-1] + 1:i]), \
+            (name, "the count does not wait for the write-back")
+        inv = [k for k in range(i + 1, min(len(lines), i + 20)) if lines[k].startswith("buffer_inv") and "sc1" in lines[k]]
+        assert inv, (name, "no invalidation after the count")
+        assert any(l.startswith("s_waitcnt") and "vmcnt(0)" in l for l in lines[i + 1:inv[0]]), name
+    assert n > 0  # the stream-K kernels are compiled
+
+
+def _vregs(tok):
+    m = re.fullmatch(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.fullmatch(r"v(\d+)", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _wide_store_data(ins):
+    op, _, rest = ins.partition(" ")
+    ops = [o.strip() for o in rest.split(",")]
+    if re.match(r"(buffer|scratch)_store_(dwordx[34]|b96|b128)", op):
+        return _vregs(ops[0])
+    if re.match(r"(global|flat)_store_(dwordx[34]|b96|b128)", op):
+        return _vregs(ops[1])
+    return set()
+
+
+def test_no_vector_write_of_a_wide_store_s_data_right_after_it(asm):
+    """A store of more than 8 bytes reads its data registers after it issues:
+    a vector write to them within the next two wait states can reach the
+    store.  (The compiler pads buffer stores only when their scalar offset is
+    not a register; the stream-K partial tiles, stored with the slot in the
+    scalar offset, had their first value replaced by the next store's offset.)"""
+    for name, (body, _) in asm.items():
+        lines = [l.split(";")[0].strip() for l in body.splitlines()]
+        lines = [l for l in lines if l and not l.startswith(".")]
+        for i, ins in enumerate(lines):
+            data = _wide_store_data(ins)
+            if not data:
+                continue
+            waits = 0
+            for nxt in lines[i + 1:i + 3]:
+                if waits >= 2:
+                    break
+                m = re.match(r"s_nop (\d+)", nxt)
+                if m:
+                    waits += int(m.group(1)) + 1
+                    continue
+                if nxt.startswith("v_") and " " in nxt:
+                    assert not (_vregs(nxt.split(" ", 1)[1].split(",")[0].strip()) & data), (name, ins, nxt)
+                waits += 1
