@@ -1,7 +1,8 @@
 """Randomized parity (GPU): seeded random shapes, zero points, outputs, tile
-variants and split modes for the five entry points, every output compared
-with the oracle bit for bit (integer-valued fp16 operands, whose sums are
-exact in fp32; u8 x i8 int32 and requantized int8 outputs).  The fixed-case
+variants, split modes and leading dimensions for the five entry points,
+every output compared with the oracle bit for bit (integer-valued fp16
+operands, whose sums are exact in fp32; u8 x i8 int32, dequantized fp32 and
+requantized int8 outputs).  The fixed-case
 tests pin chosen corners; these cover their combinations."""
 from __future__ import annotations
 
@@ -14,6 +15,7 @@ from test_gpu_parity import run_conv, run_conv_nhwcnc, run_f16, run_qconv, run_u
 pytestmark = pytest.mark.gpu
 
 KINDS = ("gemm_u8i8", "conv_u8i8", "gemm_f16", "conv_f16", "conv_nhwcnc")
+LD_PAD = (0, 0, 0, 8, 16, 3, 64)  # leading dimension = extent + one of these
 
 
 @pytest.fixture(scope="module")
@@ -58,9 +60,11 @@ def _one_case(igc, oracle, rng):
         if kind == "gemm_f16":
             M, N, K = _gemm_shape(rng, 700, 600, ([256, 512, 1024], [256, 512], [64, 512, 1024]))
             A, Bt = synth.f16_small_ints(rng, (M, K)), synth.f16_small_ints(rng, (N, K))
-            desc = f"{kind} M={M} N={N} K={K} variant={v} split={sk}"
+            lda, ldb, ldc = (int(x + rng.choice(LD_PAD)) for x in (K, K, N))
+            desc = f"{kind} M={M} N={N} K={K} lda={lda} ldb={ldb} ldc={ldc} variant={v} split={sk}"
             print(desc, flush=True)
-            assert np.array_equal(run_f16(igc, A, Bt).astype(np.float64), oracle.gemm_f16(A, Bt)), desc
+            got = run_f16(igc, A, Bt, lda=lda, ldb=ldb, ldc=ldc)
+            assert np.array_equal(got.astype(np.float64), oracle.gemm_f16(A, Bt)), desc
             return kind
         if kind == "conv_f16":
             Nb, H, W, C, Kout, R, S, st, pd = _conv_shape(rng, [64, 128, 256, int(rng.integers(1, 100))])
@@ -83,9 +87,10 @@ def _one_case(igc, oracle, rng):
             assert np.array_equal(run_conv_nhwcnc(igc, xb, wb, st, pd).astype(np.float64),
                                   oracle.conv2d_nhwcnc_direct(xb, wb, st, pd)), desc
             return kind
-        outs = [("Q",), ("C",), ("C", "Q"), ("Q",)][int(rng.integers(0, 4))]
+        outs = [("Q",), ("C",), ("C", "Q"), ("Q",), ("D",), ("C", "D", "Q")][int(rng.integers(0, 6))]
         zA = int(rng.choice([0, 128, int(rng.integers(0, 256))]))
         zB = int(rng.choice([0, int(rng.integers(-128, 128))]))
+        sA, sB = float(rng.uniform(0.001, 0.1)), float(rng.uniform(0.001, 0.1))
         use_cs = "C" not in outs and rng.random() < 0.5
         if kind == "gemm_u8i8":
             M, N, K = _gemm_shape(rng, 600, 520, ([224, 256, 448, 512], [256, 512], [128, 256, 384, 1024]))
@@ -93,9 +98,12 @@ def _one_case(igc, oracle, rng):
             scale = rng.uniform(0.001, 0.05, size=N).astype(np.float32)
             bias = (rng.standard_normal(N) * 4).astype(np.float32)
             cs = torch.from_numpy(oracle.i8_colsum(Bt).astype(np.int32)).cuda() if use_cs else None
-            desc = f"{kind} M={M} N={N} K={K} zA={zA} zB={zB} outputs={outs} colsum={use_cs} variant={v} split={sk}"
+            lda, ldb = (int(K + rng.choice(LD_PAD)) for _ in range(2))
+            desc = (f"{kind} M={M} N={N} K={K} lda={lda} ldb={ldb} zA={zA} zB={zB} outputs={outs} "
+                    f"colsum={use_cs} variant={v} split={sk}")
             print(desc, flush=True)
-            got = run_u8i8(igc, A, zA, Bt, zB, outputs=outs, scale=scale, bias=bias, colsum_B=cs)
+            got = run_u8i8(igc, A, zA, Bt, zB, outputs=outs, scale=scale, bias=bias, colsum_B=cs,
+                           dq=float(oracle.dequant_scale(sA, sB)), lda=lda, ldb=ldb)
             C32 = oracle.gemm_u8i8_naive(A, zA, Bt, zB)
         else:
             Nb, H, W, C, Kout, R, S, st, pd = _conv_shape(rng, [128, 256, 128, int(rng.integers(1, 200))])
@@ -107,10 +115,13 @@ def _one_case(igc, oracle, rng):
             desc = (f"{kind} {Nb}x{H}x{W}x{C} * {Kout}x{R}x{S} stride={st} pad={pd} zA={zA} zB={zB} "
                     f"outputs={outs} colsum={use_cs} variant={v} split={sk}")
             print(desc, flush=True)
-            got = run_qconv(igc, x, zA, w, zB, st, pd, outputs=outs, scale=scale, bias=bias, colsum_B=cs)
+            got = run_qconv(igc, x, zA, w, zB, st, pd, outputs=outs, scale=scale, bias=bias, colsum_B=cs,
+                            dq=float(oracle.dequant_scale(sA, sB)))
             C32 = oracle.conv2d_u8i8_direct(x, zA, w, zB, st, pd).reshape(-1, Kout)
         if "C" in got:
             assert np.array_equal(got["C"].astype(np.int64), C32), desc
+        if "D" in got:
+            assert np.array_equal(got["D"], oracle.dequant(C32, sA, sB)), desc
         if "Q" in got:
             assert np.array_equal(got["Q"], oracle.requant(C32, scale, bias)), desc
         return kind
