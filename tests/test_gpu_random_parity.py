@@ -134,3 +134,72 @@ def test_random_cases_match_the_oracle(igc, oracle, seed):
     rng = np.random.default_rng(seed)
     seen = [_one_case(igc, oracle, rng) for _ in range(50)]
     assert set(seen) == set(KINDS)
+
+
+def _medium_case(igc, oracle, rng, kind):
+    """GEMMs of about 600-2500 x 256-1500 and convolutions of up to 16 x 28 x 28
+    x 256 -> 512: the shapes where the default plan picks the large tiles and,
+    in the partial last round, the split; bit-exact like the small cases."""
+    sk = int(rng.choice([1, 1, 2]))
+    igc.set_tuning(-1, sk)
+    try:
+        if kind == "gemm_f16":
+            M, N, K = int(rng.integers(600, 2500)), int(rng.integers(256, 1500)), int(rng.choice([64, 256, 512, 1000, 1024]))
+            A, Bt = synth.f16_small_ints(rng, (M, K), -4, 4), synth.f16_small_ints(rng, (N, K), -4, 4)
+            desc = f"{kind} M={M} N={N} K={K} split={sk}"
+            print(desc, flush=True)
+            assert np.array_equal(run_f16(igc, A, Bt).astype(np.float64), oracle.gemm_f16(A, Bt)), desc
+        elif kind == "gemm_u8i8":
+            M, N, K = int(rng.integers(600, 2500)), int(rng.integers(256, 1500)), int(rng.choice([128, 256, 512, 1024]))
+            zA, zB = int(rng.choice([128, 0, 77])), int(rng.choice([0, -9]))
+            A, Bt = synth.u8_uniform(rng, (M, K)), synth.i8_uniform(rng, (N, K))
+            scale = rng.uniform(0.0005, 0.005, N).astype(np.float32)
+            bias = rng.standard_normal(N).astype(np.float32)
+            outs = [("Q",), ("C",), ("C", "D", "Q")][int(rng.integers(0, 3))]
+            desc = f"{kind} M={M} N={N} K={K} zA={zA} zB={zB} outputs={outs} split={sk}"
+            print(desc, flush=True)
+            got = run_u8i8(igc, A, zA, Bt, zB, outputs=outs, scale=scale, bias=bias,
+                           dq=float(oracle.dequant_scale(0.02, 0.01)))
+            C = oracle.gemm_u8i8_naive(A, zA, Bt, zB)
+            if "C" in got:
+                assert np.array_equal(got["C"].astype(np.int64), C), desc
+            if "D" in got:
+                assert np.array_equal(got["D"], oracle.dequant(C, 0.02, 0.01)), desc
+            if "Q" in got:
+                assert np.array_equal(got["Q"], oracle.requant(C, scale, bias)), desc
+        else:
+            Nb, HW = int(rng.choice([4, 8, 16])), int(rng.choice([7, 14, 28]))
+            C = int(rng.choice([128, 256])) if kind == "conv_u8i8" else int(rng.choice([64, 128, 256]))
+            Kout, RS = int(rng.choice([64, 128, 256, 512])), int(rng.choice([1, 3]))
+            st = int(rng.choice([1, 1, 2]))
+            pd = int(rng.choice([0, 1])) if RS == 3 else 0
+            desc = f"{kind} {Nb}x{HW}x{HW}x{C} * {Kout}x{RS}x{RS} stride={st} pad={pd} split={sk}"
+            print(desc, flush=True)
+            if kind == "conv_f16":
+                x = synth.f16_small_ints(rng, (Nb, HW, HW, C), -4, 4)
+                w = synth.f16_small_ints(rng, (Kout, RS, RS, C), -4, 4)
+                assert np.array_equal(run_conv(igc, x, w, (st, st), (pd, pd)).astype(np.float64),
+                                      oracle.conv2d_direct(x, w, (st, st), (pd, pd))), desc
+            elif kind == "conv_nhwcnc":
+                xb = synth.f16_small_ints(rng, (max(1, Nb // 8), HW, HW, C // 16, 16, 16), -4, 4)
+                wb = synth.f16_small_ints(rng, (RS, RS, C // 16, Kout // 16, 16, 16), -4, 4)
+                assert np.array_equal(run_conv_nhwcnc(igc, xb, wb, (st, st), (pd, pd)).astype(np.float64),
+                                      oracle.conv2d_nhwcnc_direct(xb, wb, (st, st), (pd, pd))), desc
+            else:
+                x, w = synth.u8_uniform(rng, (Nb, HW, HW, C)), synth.i8_uniform(rng, (Kout, RS, RS, C))
+                zA = int(rng.choice([100, 128, 0]))
+                scale = rng.uniform(0.0001, 0.002, Kout).astype(np.float32)
+                bias = rng.standard_normal(Kout).astype(np.float32)
+                got = run_qconv(igc, x, zA, w, 0, (st, st), (pd, pd), outputs=("C", "Q"), scale=scale, bias=bias)
+                Cr = oracle.conv2d_u8i8_direct(x, zA, w, 0, (st, st), (pd, pd)).reshape(-1, Kout)
+                assert np.array_equal(got["C"].astype(np.int64), Cr), desc
+                assert np.array_equal(got["Q"], oracle.requant(Cr, scale, bias)), desc
+    finally:
+        igc.set_tuning(-1, 1)
+
+
+@pytest.mark.parametrize("seed", [201, 202])
+def test_medium_random_cases_match_the_oracle(igc, oracle, seed):
+    rng = np.random.default_rng(seed)
+    for i in range(30):
+        _medium_case(igc, oracle, rng, KINDS[i % len(KINDS)])
