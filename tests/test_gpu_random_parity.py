@@ -203,3 +203,35 @@ def test_medium_random_cases_match_the_oracle(igc, oracle, seed):
     rng = np.random.default_rng(seed)
     for i in range(30):
         _medium_case(igc, oracle, rng, KINDS[i % len(KINDS)])
+
+
+def test_long_k_random_cases_match_the_oracle(igc, oracle):
+    """Small outputs over a long K (fp16 up to 16384, u8 x i8 up to the 33025
+    limit): few tiles, so the split shares each tile's K range between many
+    workgroups (the u8 x i8 split arithmetic is 32-bit)."""
+    rng = np.random.default_rng(301)
+    for i in range(10):
+        v, sk = int(rng.choice([-1, -1, 1, 2])), int(rng.choice([1, 2]))
+        igc.set_tuning(v, sk)
+        try:
+            if i % 2 == 0:
+                M, N, K = int(rng.integers(64, 1024)), int(rng.integers(64, 1024)), int(rng.integers(2048, 16385))
+                A, Bt = synth.f16_small_ints(rng, (M, K), -2, 2), synth.f16_small_ints(rng, (N, K), -2, 2)
+                desc = f"gemm_f16 M={M} N={N} K={K} variant={v} split={sk}"
+                print(desc, flush=True)
+                assert np.array_equal(run_f16(igc, A, Bt).astype(np.float64), oracle.gemm_f16(A, Bt)), desc
+            else:
+                M, N = int(rng.integers(64, 768)), int(rng.integers(64, 768))
+                K = [33025, 33024, int(rng.integers(2048, 33026))][i // 2 % 3]
+                zA, zB = int(rng.choice([128, 0, 255])), int(rng.choice([0, 127, -128]))
+                A, Bt = synth.u8_uniform(rng, (M, K)), synth.i8_uniform(rng, (N, K), -128, 127)
+                scale = rng.uniform(1e-6, 1e-4, N).astype(np.float32)
+                bias = rng.standard_normal(N).astype(np.float32)
+                desc = f"gemm_u8i8 M={M} N={N} K={K} zA={zA} zB={zB} variant={v} split={sk}"
+                print(desc, flush=True)
+                got = run_u8i8(igc, A, zA, Bt, zB, outputs=("C", "Q"), scale=scale, bias=bias)
+                C = oracle.gemm_u8i8_naive(A, zA, Bt, zB)
+                assert np.array_equal(got["C"].astype(np.int64), C), desc
+                assert np.array_equal(got["Q"], oracle.requant(C, scale, bias)), desc
+        finally:
+            igc.set_tuning(-1, 1)
