@@ -195,9 +195,9 @@ class Runner:
         HIP events: the average launch duration is the elapsed time / steps
         (no event commands between the launches, as a caller would run them).
         Then, untimed for the headline value: each launch alone between two
-        events (median, min, max), the same with the caches flushed before
-        every launch when `cold`, and the shader clock read while the launches
-        run."""
+        events (median, min, max), and the same with the caches flushed before
+        every launch when `cold`.  (The shader clock is read in a pass of its
+        own after every workload's timed regions: see `sclk_while_running`.)"""
         if warmup is None:
             # until 0.25 s of work has run (at least 10 launches)
             warmup, t0 = 0, time.perf_counter()
@@ -241,7 +241,6 @@ class Runner:
             res.update(self._per_launch(torch, steps, "cold_launch_us", before=lambda: flush.fill_(1.0)))
             res["cold_alg_gbps"] = algorithmic_bytes(self.wl) / (res["cold_launch_us_median"] * 1e-6) / 1e9
             del flush
-        res["sclk_mhz"] = self._sclk_while_running(torch)
         return res
 
     def _per_launch(self, torch, steps, key, before=None) -> dict:
@@ -257,15 +256,30 @@ class Runner:
         return {f"{key}_median": us[len(us) // 2], f"{key}_min": us[0], f"{key}_max": us[-1],
                 f"{key}_mean": sum(us) / len(us)}
 
-    def _sclk_while_running(self, torch, seconds=0.3):
-        """Shader clock (MHz) read while back-to-back launches run, or None."""
+    def sustain(self, torch, seconds):
+        """Back-to-back launches for `seconds` (untimed)."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                self.call()
+            torch.cuda.synchronize()
+
+    def sclk_while_running(self, torch, path, seconds=0.3):
+        """Shader clock (MHz) read from `path` while back-to-back launches run,
+        or None.  Each read of the driver's DPM table queries the GPU's power
+        management, and the launches timed shortly after such reads ran
+        slower (8192^3 int8 with --warmup 5: 447-459 us per launch against
+        368 us without them), so bench takes these readings only after every
+        workload's timed regions."""
         import threading
 
+        if path is None:
+            return None
         samples, stop = [], threading.Event()
 
         def poll():
             while not stop.is_set():
-                v = read_sclk_mhz()
+                v = read_sclk_mhz(path)
                 if v is None:
                     return
                 samples.append(v)
@@ -273,11 +287,7 @@ class Runner:
 
         th = threading.Thread(target=poll, daemon=True)
         th.start()
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < seconds:
-            for _ in range(20):
-                self.call()
-            torch.cuda.synchronize()
+        self.sustain(torch, seconds)
         stop.set()
         th.join()
         if not samples:
@@ -287,21 +297,37 @@ class Runner:
                 "samples": len(samples)}
 
 
-def read_sclk_mhz():
-    """Current shader clock of GPU 0 from the driver's DPM table (the level
-    marked '*'), or None where the file is not readable."""
+def sclk_path(torch):
+    """The driver's DPM table (pp_dpm_sclk) of the GPU this process uses,
+    matched by PCI address among /sys/class/drm/card*, or None (another
+    card's table would give another GPU's clock)."""
     import glob
 
+    try:
+        pr = torch.cuda.get_device_properties(torch.cuda.current_device())
+        want = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}."
+    except (AttributeError, RuntimeError):
+        return None
     for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-        try:
-            with open(path) as f:
-                for line in f:
-                    if line.rstrip().endswith("*"):
-                        tok = [t for t in line.split() if t.lower().endswith("mhz")]
-                        if tok:
-                            return float(tok[0][:-3])
-        except OSError:
-            continue
+        if os.path.basename(os.path.realpath(os.path.dirname(path))).lower().startswith(want):
+            return path
+    return None
+
+
+def read_sclk_mhz(path=None):
+    """Current shader clock (MHz) in a pp_dpm_sclk table (the level marked
+    '*'), or None where there is none or it is not readable."""
+    if path is None:
+        return None
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    tok = [t for t in line.split() if t.lower().endswith("mhz")]
+                    if tok:
+                        return float(tok[0][:-3])
+    except OSError:
+        pass
     return None
 
 
@@ -512,8 +538,8 @@ def main(argv=None) -> int:
     head_wl = None
     for name in names:
         wl = wls[name]
-        r = runners.pop(name)
-        res = r.measure(torch, args.steps, args.warmup, cold=name in ("c1", "c2"), extras=not args.no_extras)
+        res = runners[name].measure(torch, args.steps, args.warmup, cold=name in ("c1", "c2"),
+                                    extras=not args.no_extras)
         if name in ("c1", "c2") and not args.no_extras:
             res.update(graph_launch_us(wl, igc, torch))
         res["roofline_traffic_bytes"] = traffic_for(name)
@@ -521,7 +547,19 @@ def main(argv=None) -> int:
         results[name] = res
         if name == args.workload:
             head_wl = wl
-        del r
+        elif not args.no_extras:
+            # 0.3 s of this workload's own load, untimed: the next workload's
+            # warm-up and timed launches follow sustained load, not a host gap
+            runners[name].sustain(torch, 0.3)
+    # the shader clock of each workload, read only now that every timed
+    # region is over (see Runner.sclk_while_running)
+    if not args.no_extras:
+        path = sclk_path(torch)
+        for name in names:
+            results[name]["sclk_mhz"] = runners[name].sclk_while_running(torch, path)
+    del runners
+    for name in names:
+        res = results[name]
         print(f"# {name}: {res['value']:.1f} {res['unit']} ({100 * res['frac_of_peak']:.1f}% of peak), "
               f"{res['launch_us_mean']:.1f} us/launch back to back"
               + (f", {res['alone_us_median']:.1f} us median alone" if "alone_us_median" in res else "")
