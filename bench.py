@@ -7,9 +7,11 @@ One step is one call of the workload's entry point over its synthetic inputs,
 which are resident in HBM before the timed region starts.  W untimed steps,
 then exactly K steps between two synchronizations; rank 0 prints one JSON
 line.  The headline workload is the 4096^3 fp16 GEMM (TFLOPS); the other
-workloads (c1, c2, c4, c5 and the quantized convolution q4) are measured in
-the same run the same way, before the headline, and reported under
-"workloads" (the u8 x i8 ones in TOPS).
+workloads (c1, c2, c4, c5, the quantized convolution q4 and the
+blocked-layout convolution b4) are measured in
+the same run the same way, before the headline, each followed by 0.3 s of
+its own untimed load, and reported under "workloads" (the u8 x i8 ones in
+TOPS).
 
 `value` and `roofline.achieved` are algorithmic operations per launch
 (2*M*N*K) divided by the mean launch duration of K back-to-back launches
@@ -18,8 +20,9 @@ dense MFMA peak of its dtype.  After that timed region, untimed for `value`:
 each launch alone between two events (median, min, max), for c1 and c2 also
 with the caches flushed before every launch (cold) and as replays of 100
 launches captured into one HIP graph (no host launch path per kernel; a replay
-must reproduce the eager call's outputs bit for bit), and the shader clock read
-from the driver while the launches run.  `traffic` (HBM bytes per launch)
+must reproduce the eager call's outputs bit for bit).  Once every timed region
+is over, the shader clock of this GPU is read from the driver while each
+workload runs (its reads perturbed the launches timed right after them).  `traffic` (HBM bytes per launch)
 comes from the committed rocprofv3 counter summary in profiles/ when that
 summary was taken on the current kernel sources, else null.
 
