@@ -523,7 +523,13 @@ def main(argv=None) -> int:
     # steady clock it holds under sustained load (it needs ~20 ms of load to
     # leave its idle clock), whatever --warmup says, provided nothing leaves
     # it idle in between (below).
-    names = ([] if args.only else [w for w in synth.WORKLOADS if w != args.workload]) + [args.workload]
+    # The others run in an order where each follows one of similar power
+    # draw: the fp16 convolutions, then the int8 ones (q4 after c5 read
+    # 61-62 us per launch with --warmup 5, 58.5 after the fp16 convolutions;
+    # c5 right after c2 read 405-411 us, 377-382 after q4).
+    order = ("c1", "c2", "c4", "b4", "q4", "c5", "c3")
+    assert sorted(order) == sorted(synth.WORKLOADS)
+    names = ([] if args.only else [w for w in order if w != args.workload]) + [args.workload]
     # Every workload's inputs are made resident before the first measurement,
     # so the measurements follow one another with no host-to-device copies
     # between them and the headline's timed region starts from the sustained
