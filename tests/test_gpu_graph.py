@@ -125,3 +125,23 @@ def test_graph_conv_u8i8_requant(igc):
     Q = torch.empty((M, Kout), dtype=torch.int8, device="cuda")
     _check_replays(lambda: igc.conv2d_u8i8_zp(Nb, H, W, Cin, Kout, R, S, 1, 1, 1, 1, x, zA, w, zB,
                                               Q_i8=Q, ldq=Kout, scale_n=scale, bias_n=bias), [Q])
+
+
+def test_graph_gemm_u8i8_streamk(igc):
+    import torch
+
+    rng = np.random.default_rng(15)
+    M, N, K = 384, 320, 4096
+    A = torch.from_numpy(rng.integers(0, 256, size=(M, K), dtype=np.uint8)).cuda()
+    B = torch.from_numpy(rng.integers(-128, 128, size=(N, K), dtype=np.int8)).cuda()
+    C = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    igc.set_tuning(-1, 2)  # split wherever the tiles leave compute units idle
+    try:
+        nws = igc.gemm_u8i8_zp_workspace_size(M, N, K)
+        assert nws > 0
+        ws = torch.zeros(nws, dtype=torch.uint8, device="cuda")
+        _check_replays(lambda: igc.gemm_u8i8_zp(M, N, K, A, K, 90, B, K, 5, C_i32=C, ldc=N,
+                                                workspace=ws, ws_bytes=nws), [C])
+        assert int(ws[:256].view(torch.int32).abs().sum().item()) == 0  # arrival counters back at zero
+    finally:
+        igc.set_tuning(-1, 1)
